@@ -1,0 +1,141 @@
+"""Brute-force reference for the block-based fixed-length BF16 stream.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Pure Python, bit by bit, for
+tiny inputs only (a few thousand elements). It restates the stream definition
+a second, independent way -- as one long list of bits and by exhaustive search
+of the block width -- so that the C oracle can be checked against it byte for
+byte.
+
+Sources: "ENEC: A Lossless AI Model Compression Method Enabling Fast Inference
+on Ascend NPUs", Abstract (block-based fixed-length encoding, bit-width
+quantization, branch-free integer transformation, intra-segment prefix scan);
+"ZipServ: Fast and Memory-Efficient LLM Inference with Hardware-Aware Lossless
+Compression", Abstract (fixed-length format, parallel decoding).
+"""
+
+HEADER = 256
+SEG = 64
+
+
+def _align(v, a):
+    return -(-v // a) * a
+
+
+def split(x):
+    """BF16 bit pattern -> (exponent byte, sign+mantissa byte)."""
+    bits = [(x >> k) & 1 for k in range(16)]          # bit k of x
+    exp = sum(bits[7 + k] << k for k in range(8))      # bits 7..14
+    sm = sum(bits[k] << k for k in range(7)) + (bits[15] << 7)
+    return exp, sm
+
+
+def join(exp, sm):
+    bits = [0] * 16
+    for k in range(7):
+        bits[k] = (sm >> k) & 1
+    for k in range(8):
+        bits[7 + k] = (exp >> k) & 1
+    bits[15] = (sm >> 7) & 1
+    return sum(b << k for k, b in enumerate(bits))
+
+
+def width_by_search(codes):
+    """Smallest w in 0..8 with every code < 2**w."""
+    for w in range(9):
+        if all(c < (1 << w) for c in codes):
+            return w
+    raise ValueError("code above 255")
+
+
+def _le(v, nbytes):
+    return [(v >> (8 * i)) & 0xFF for i in range(nbytes)]
+
+
+def _header(flags, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
+            payload_bytes, raw_off, total):
+    h = list(b"ENCB") + _le(1, 2) + _le(1, 2) + _le(flags, 4) + _le(B, 4)
+    h += _le(SEG, 4) + _le(0, 4)
+    for v in (n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
+              payload_bytes, raw_off, total):
+        h += _le(v, 8)
+    return h + [0] * (HEADER - len(h))
+
+
+def encode(xs, B):
+    """Stream bytes for the BF16 patterns xs (list of ints) at block size B."""
+    n = len(xs)
+    raw = _header(1, B, n, 0, 0, 0, 0, 0, 0, 0, HEADER, HEADER + 2 * n)
+    for x in xs:
+        raw += _le(x, 2)
+    if n == 0:
+        return bytes(raw)
+    blocks = [xs[i:i + B] for i in range(0, n, B)]
+    nb = len(blocks)
+    nseg = -(-nb // SEG)
+    metas, payloads = [], []
+    for blk in blocks:
+        exps = [split(v)[0] for v in blk]
+        base = min(exps)
+        codes = [e - base for e in exps]
+        w = width_by_search(codes)
+        bitlist = []
+        for c in codes:                      # LSB first, consecutive fields
+            bitlist += [(c >> b) & 1 for b in range(w)]
+        while len(bitlist) % 8:
+            bitlist.append(0)
+        body = [sum(bitlist[8 * k + b] << b for b in range(8))
+                for k in range(len(bitlist) // 8)]
+        while len(body) % 16:
+            body.append(0)
+        metas.append((base, w))
+        payloads.append(body)
+    sm_off = HEADER
+    meta_off = sm_off + _align(n, 256)
+    segoff_off = meta_off + _align(2 * nb, 256)
+    payload_off = segoff_off + _align(8 * nseg, 256)
+    segoffs = [sum(len(p) for p in payloads[:SEG * s]) for s in range(nseg)]
+    payload_bytes = sum(len(p) for p in payloads)
+    total = payload_off + payload_bytes
+    if total >= HEADER + 2 * n:
+        return bytes(raw)
+    out = _header(0, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
+                  payload_bytes, 0, total)
+    out += [split(v)[1] for v in xs]
+    out += [0] * (meta_off - len(out))
+    for base, w in metas:
+        out += [base, w]
+    out += [0] * (segoff_off - len(out))
+    for so in segoffs:
+        out += _le(so, 8)
+    out += [0] * (payload_off - len(out))
+    for p in payloads:
+        out += p
+    assert len(out) == total
+    return bytes(out)
+
+
+def _get(s, off, nbytes):
+    return sum(s[off + i] << (8 * i) for i in range(nbytes))
+
+
+def decode(s):
+    """BF16 patterns decoded from stream bytes s (walks every block)."""
+    assert bytes(s[:4]) == b"ENCB"
+    flags, B = _get(s, 8, 4), _get(s, 12, 4)
+    n = _get(s, 24, 8)
+    if flags & 1:
+        return [_get(s, HEADER + 2 * j, 2) for j in range(n)]
+    nb = _get(s, 32, 8)
+    sm_off, meta_off = _get(s, 48, 8), _get(s, 56, 8)
+    payload_off = _get(s, 72, 8)
+    out = []
+    pos = payload_off
+    for i in range(nb):
+        L = min(B, n - i * B)
+        base, w = s[meta_off + 2 * i], s[meta_off + 2 * i + 1]
+        bitstream = [(s[pos + k // 8] >> (k % 8)) & 1 for k in range(L * w)]
+        for t in range(L):
+            d = sum(bitstream[t * w + b] << b for b in range(w))
+            out.append(join((base + d) & 0xFF, s[sm_off + i * B + t]))
+        pos += _align(-(-L * w // 8), 16)
+    return out

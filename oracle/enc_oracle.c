@@ -1,0 +1,473 @@
+/*
+ * enc_oracle.c -- CPU oracle for lossless block-based fixed-length coding of
+ * BF16 weights.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg load this library. It shares no
+ * code, header, table or constant with the GPU library: it redeclares the
+ * stream layout itself from the written format definition.
+ *
+ * Plain, scalar, single-threaded C. Every loop follows the definition of the
+ * stream step by step; nothing is blocked, fused or vectorised by hand. Bits
+ * are set and read one at a time.
+ *
+ * Sources (the pages are abstracts; where they are silent the plainest reading
+ * is taken and listed with the design notes):
+ *  - "ENEC: A Lossless AI Model Compression Method Enabling Fast Inference on
+ *    Ascend NPUs", Abstract: block-based fixed-length encoding; bit-width
+ *    quantization with bit-packing; branch-free integer transformation;
+ *    intra-segment scan for the prefix sums of block sizes.
+ *  - "ZipServ: Fast and Memory-Efficient LLM Inference with Hardware-Aware
+ *    Lossless Compression", Abstract: a fixed-length format decodable in
+ *    constant time and in parallel; a fused decompress-GEMM.
+ *
+ * Readings used here (the pages give no layout):
+ *  - a BF16 value x splits into an exponent byte E = (x >> 7) & 0xFF and a
+ *    sign+mantissa byte SM = (sign << 7) | mantissa;
+ *  - the branch-free transform is d = E - base, base = the block minimum;
+ *  - the block width is the number of bits of (max E - base), 0..8, with no
+ *    further rounding of the width;
+ *  - fields are packed LSB first, consecutively, within each block;
+ *  - stored offsets: one u64 per 64-block segment (exclusive prefix sum of
+ *    padded block payload sizes); offsets inside a segment are re-derived by
+ *    the decoder from the widths.
+ *
+ * Parity status of each function is given in its comment; all are pinned by
+ * the CPU tests (round trip, closed-form size, exhaustive width search,
+ * brute-force bit layout, hand-derived blocks, exact GEMM special cases).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ----- stream layout constants (the format definition, restated here) ----- */
+#define ORC_HEADER_BYTES 256u
+#define ORC_SEG_BLOCKS 64u
+#define ORC_SECTION_ALIGN 256u
+#define ORC_PAYLOAD_ALIGN 16u
+#define ORC_VERSION 1u
+#define ORC_DTYPE_BF16 1u
+#define ORC_FLAG_RAW 1u
+
+/* status codes returned by the oracle (negative = failure) */
+#define ORC_OK 0
+#define ORC_E_ARG (-1)
+#define ORC_E_CAPACITY (-3)
+#define ORC_E_STREAM (-4)
+#define ORC_E_NOMEM (-7)
+
+static uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+static void put_le(uint8_t *p, uint64_t v, int nbytes) {
+  for (int i = 0; i < nbytes; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+static uint64_t get_le(const uint8_t *p, int nbytes) {
+  uint64_t v = 0;
+  for (int i = 0; i < nbytes; i++) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+/* ---------------------------------------------------------------------------
+ * Field split (ENEC Abstract, "block-based fixed-length encoding" of the
+ * exponent; reading: exponent byte plus a raw sign+mantissa byte).
+ * ------------------------------------------------------------------------- */
+unsigned orc_exponent(uint16_t x) { return (x >> 7) & 0xFFu; }
+
+unsigned orc_signmant(uint16_t x) {
+  unsigned sign = (x >> 15) & 1u;
+  unsigned mant = x & 0x7Fu;
+  return (sign << 7) | mant;
+}
+
+uint16_t orc_join(unsigned sm, unsigned e) {
+  unsigned sign = (sm >> 7) & 1u;
+  unsigned mant = sm & 0x7Fu;
+  return (uint16_t)((sign << 15) | ((e & 0xFFu) << 7) | mant);
+}
+
+/* Number of bits needed to write r (0 for r == 0): the smallest w with
+ * r < 2^w ("bit-width quantization", ENEC Abstract, read as the minimal
+ * width). Counted by repeated halving. */
+unsigned orc_bit_width(unsigned r) {
+  unsigned w = 0;
+  while (r != 0) {
+    w++;
+    r >>= 1;
+  }
+  return w;
+}
+
+/* ---------------------------------------------------------------------------
+ * Layout of a non-RAW stream for n elements and block size B.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  uint64_t n, nb, nseg;
+  uint64_t sm_off, meta_off, segoff_off, payload_off;
+} orc_layout;
+
+static orc_layout layout_of(uint64_t n, uint32_t B) {
+  orc_layout L;
+  L.n = n;
+  L.nb = (n + B - 1) / B;
+  L.nseg = (L.nb + ORC_SEG_BLOCKS - 1) / ORC_SEG_BLOCKS;
+  L.sm_off = ORC_HEADER_BYTES;
+  L.meta_off = L.sm_off + round_up(n, ORC_SECTION_ALIGN);
+  L.segoff_off = L.meta_off + round_up(2 * L.nb, ORC_SECTION_ALIGN);
+  L.payload_off = L.segoff_off + round_up(8 * L.nseg, ORC_SECTION_ALIGN);
+  return L;
+}
+
+/* Length of block i (the last block may be shorter). */
+static uint64_t block_len(uint64_t n, uint32_t B, uint64_t i) {
+  uint64_t start = i * B;
+  uint64_t end = start + B;
+  if (end > n) end = n;
+  return end - start;
+}
+
+/* Padded payload bytes of a block of L codes of w bits. */
+uint64_t orc_block_payload_bytes(unsigned w, uint64_t L) {
+  uint64_t bits = (uint64_t)w * L;
+  uint64_t bytes = (bits + 7) / 8;
+  return round_up(bytes, ORC_PAYLOAD_ALIGN);
+}
+
+static int block_size_ok(uint32_t B) { return B >= 8 && B <= 4096 && B % 8 == 0; }
+
+/* ---------------------------------------------------------------------------
+ * Per-block base and width (ENEC Abstract: "branch-free integer
+ * transformation" read as subtraction of the block minimum exponent; "bit-width
+ * quantization" read as the minimal width of the transformed values).
+ * Writes base[nb], width[nb]. Returns nb, or a negative status.
+ * ------------------------------------------------------------------------- */
+int64_t orc_block_params(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *base,
+                         uint8_t *width) {
+  if (!block_size_ok(B)) return ORC_E_ARG;
+  uint64_t nb = (n + B - 1) / B;
+  for (uint64_t i = 0; i < nb; i++) {
+    uint64_t L = block_len(n, B, i);
+    unsigned lo = 255, hi = 0;
+    for (uint64_t t = 0; t < L; t++) {
+      unsigned e = orc_exponent(x[i * B + t]);
+      if (e < lo) lo = e;
+      if (e > hi) hi = e;
+    }
+    base[i] = (uint8_t)lo;
+    width[i] = (uint8_t)orc_bit_width(hi - lo);
+  }
+  return (int64_t)nb;
+}
+
+/* Size in bytes of the stream that orc_encode writes for x (RAW fallback
+ * included). Closed form of the layout: header + aligned sections + sum of
+ * padded block payloads; RAW when that is not smaller than header + 2n. */
+int64_t orc_stream_size(const uint16_t *x, uint64_t n, uint32_t B) {
+  if (!block_size_ok(B)) return ORC_E_ARG;
+  uint64_t raw_total = ORC_HEADER_BYTES + 2 * n;
+  if (n == 0) return (int64_t)raw_total;
+  orc_layout L = layout_of(n, B);
+  uint8_t *base = (uint8_t *)malloc(L.nb), *w = (uint8_t *)malloc(L.nb);
+  if (!base || !w) {
+    free(base);
+    free(w);
+    return ORC_E_NOMEM;
+  }
+  orc_block_params(x, n, B, base, w);
+  uint64_t payload = 0;
+  for (uint64_t i = 0; i < L.nb; i++) payload += orc_block_payload_bytes(w[i], block_len(n, B, i));
+  free(base);
+  free(w);
+  uint64_t total = L.payload_off + payload;
+  return (int64_t)(total >= raw_total ? raw_total : total);
+}
+
+static void write_header(uint8_t *h, uint32_t flags, uint32_t B, uint64_t n, uint64_t nb,
+                         uint64_t nseg, uint64_t sm_off, uint64_t meta_off, uint64_t segoff_off,
+                         uint64_t payload_off, uint64_t payload_bytes, uint64_t raw_off,
+                         uint64_t total) {
+  memset(h, 0, ORC_HEADER_BYTES);
+  h[0] = 'E';
+  h[1] = 'N';
+  h[2] = 'C';
+  h[3] = 'B';
+  put_le(h + 4, ORC_VERSION, 2);
+  put_le(h + 6, ORC_DTYPE_BF16, 2);
+  put_le(h + 8, flags, 4);
+  put_le(h + 12, B, 4);
+  put_le(h + 16, ORC_SEG_BLOCKS, 4);
+  put_le(h + 20, 0, 4);
+  put_le(h + 24, n, 8);
+  put_le(h + 32, nb, 8);
+  put_le(h + 40, nseg, 8);
+  put_le(h + 48, sm_off, 8);
+  put_le(h + 56, meta_off, 8);
+  put_le(h + 64, segoff_off, 8);
+  put_le(h + 72, payload_off, 8);
+  put_le(h + 80, payload_bytes, 8);
+  put_le(h + 88, raw_off, 8);
+  put_le(h + 96, total, 8);
+}
+
+/* Set bit k of the byte array q (bit k = bit (k mod 8) of byte k / 8). */
+static void set_bit(uint8_t *q, uint64_t k) { q[k >> 3] |= (uint8_t)(1u << (k & 7)); }
+
+static unsigned get_bit(const uint8_t *q, uint64_t k) { return (q[k >> 3] >> (k & 7)) & 1u; }
+
+/* ---------------------------------------------------------------------------
+ * Encoder. Writes the whole stream into out[0..cap). Returns the stream size
+ * or a negative status. Steps, in order:
+ *  1. split every value into exponent and sign+mantissa bytes;
+ *  2. per block: base = min exponent, width = bits of (max - base);
+ *  3. per block: transformed codes d = exponent - base;
+ *  4. per block: padded payload size; per segment of 64 blocks: exclusive
+ *     prefix sum of the payload sizes (ENEC Abstract, intra-segment scan);
+ *  5. pack each block's codes at its fixed width, LSB first;
+ *  6. fall back to a verbatim (RAW) stream when that is not larger.
+ * ------------------------------------------------------------------------- */
+int64_t orc_encode(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *out, uint64_t cap) {
+  if (!block_size_ok(B)) return ORC_E_ARG;
+  if (n > 0 && x == NULL) return ORC_E_ARG;
+  int64_t size = orc_stream_size(x, n, B);
+  if (size < 0) return size;
+  if ((uint64_t)size > cap) return ORC_E_CAPACITY;
+  uint64_t raw_total = ORC_HEADER_BYTES + 2 * n;
+
+  if ((uint64_t)size == raw_total) {
+    /* RAW: header, then the input bytes verbatim, little-endian u16. */
+    memset(out, 0, (size_t)size);
+    write_header(out, ORC_FLAG_RAW, B, n, 0, 0, 0, 0, 0, 0, 0, ORC_HEADER_BYTES, raw_total);
+    for (uint64_t j = 0; j < n; j++) put_le(out + ORC_HEADER_BYTES + 2 * j, x[j], 2);
+    return size;
+  }
+
+  orc_layout L = layout_of(n, B);
+  uint8_t *base = (uint8_t *)malloc(L.nb), *w = (uint8_t *)malloc(L.nb);
+  uint64_t *psize = (uint64_t *)malloc(L.nb * sizeof(uint64_t));
+  if (!base || !w || !psize) {
+    free(base);
+    free(w);
+    free(psize);
+    return ORC_E_NOMEM;
+  }
+  orc_block_params(x, n, B, base, w);
+  for (uint64_t i = 0; i < L.nb; i++) psize[i] = orc_block_payload_bytes(w[i], block_len(n, B, i));
+
+  memset(out, 0, (size_t)size);
+
+  /* sign+mantissa plane */
+  for (uint64_t j = 0; j < n; j++) out[L.sm_off + j] = (uint8_t)orc_signmant(x[j]);
+
+  /* meta: {base, width} per block */
+  for (uint64_t i = 0; i < L.nb; i++) {
+    out[L.meta_off + 2 * i] = base[i];
+    out[L.meta_off + 2 * i + 1] = w[i];
+  }
+
+  /* segment offsets: exclusive prefix sum of payload sizes, one per segment */
+  uint64_t running = 0;
+  for (uint64_t i = 0; i < L.nb; i++) {
+    if (i % ORC_SEG_BLOCKS == 0) put_le(out + L.segoff_off + 8 * (i / ORC_SEG_BLOCKS), running, 8);
+    running += psize[i];
+  }
+  uint64_t payload_bytes = running;
+
+  /* payloads, concatenated in block order */
+  uint64_t pos = L.payload_off;
+  for (uint64_t i = 0; i < L.nb; i++) {
+    uint64_t len = block_len(n, B, i);
+    uint8_t *q = out + pos;
+    for (uint64_t t = 0; t < len; t++) {
+      unsigned d = orc_exponent(x[i * B + t]) - base[i];
+      for (unsigned b = 0; b < w[i]; b++)
+        if ((d >> b) & 1u) set_bit(q, (uint64_t)t * w[i] + b);
+    }
+    pos += psize[i];
+  }
+
+  write_header(out, 0, B, n, L.nb, L.nseg, L.sm_off, L.meta_off, L.segoff_off, L.payload_off,
+               payload_bytes, 0, L.payload_off + payload_bytes);
+  free(base);
+  free(w);
+  free(psize);
+  return size;
+}
+
+/* ---------------------------------------------------------------------------
+ * Header parsing and full validation. Fills the fields the decoder needs.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  uint32_t flags, B;
+  uint64_t n, nb, nseg, sm_off, meta_off, segoff_off, payload_off, payload_bytes, raw_off, total;
+} orc_header;
+
+static int parse_header(const uint8_t *s, uint64_t bytes, orc_header *h) {
+  if (s == NULL || bytes < ORC_HEADER_BYTES) return ORC_E_STREAM;
+  if (s[0] != 'E' || s[1] != 'N' || s[2] != 'C' || s[3] != 'B') return ORC_E_STREAM;
+  if (get_le(s + 4, 2) != ORC_VERSION || get_le(s + 6, 2) != ORC_DTYPE_BF16) return ORC_E_STREAM;
+  h->flags = (uint32_t)get_le(s + 8, 4);
+  h->B = (uint32_t)get_le(s + 12, 4);
+  if (get_le(s + 16, 4) != ORC_SEG_BLOCKS || get_le(s + 20, 4) != 0) return ORC_E_STREAM;
+  h->n = get_le(s + 24, 8);
+  h->nb = get_le(s + 32, 8);
+  h->nseg = get_le(s + 40, 8);
+  h->sm_off = get_le(s + 48, 8);
+  h->meta_off = get_le(s + 56, 8);
+  h->segoff_off = get_le(s + 64, 8);
+  h->payload_off = get_le(s + 72, 8);
+  h->payload_bytes = get_le(s + 80, 8);
+  h->raw_off = get_le(s + 88, 8);
+  h->total = get_le(s + 96, 8);
+  for (int k = 104; k < 256; k++)
+    if (s[k] != 0) return ORC_E_STREAM;
+  if (!block_size_ok(h->B)) return ORC_E_STREAM;
+  if (h->total > bytes) return ORC_E_STREAM;
+  if (h->flags == ORC_FLAG_RAW) {
+    if (h->nb || h->nseg || h->sm_off || h->meta_off || h->segoff_off || h->payload_off ||
+        h->payload_bytes || h->raw_off != ORC_HEADER_BYTES ||
+        h->total != ORC_HEADER_BYTES + 2 * h->n)
+      return ORC_E_STREAM;
+    return ORC_OK;
+  }
+  if (h->flags != 0 || h->n == 0) return ORC_E_STREAM;
+  orc_layout L = layout_of(h->n, h->B);
+  if (h->nb != L.nb || h->nseg != L.nseg || h->sm_off != L.sm_off || h->meta_off != L.meta_off ||
+      h->segoff_off != L.segoff_off || h->payload_off != L.payload_off || h->raw_off != 0 ||
+      h->total != h->payload_off + h->payload_bytes)
+    return ORC_E_STREAM;
+  /* widths and offsets must agree with the meta section */
+  uint64_t running = 0;
+  for (uint64_t i = 0; i < h->nb; i++) {
+    unsigned w = s[h->meta_off + 2 * i + 1];
+    if (w > 8) return ORC_E_STREAM;
+    if (i % ORC_SEG_BLOCKS == 0 && get_le(s + h->segoff_off + 8 * (i / ORC_SEG_BLOCKS), 8) != running)
+      return ORC_E_STREAM;
+    running += orc_block_payload_bytes(w, block_len(h->n, h->B, i));
+  }
+  if (running != h->payload_bytes) return ORC_E_STREAM;
+  return ORC_OK;
+}
+
+/* Validates a stream; returns its element count or a negative status. */
+int64_t orc_stream_elements(const uint8_t *s, uint64_t bytes) {
+  orc_header h;
+  int st = parse_header(s, bytes, &h);
+  if (st != ORC_OK) return st;
+  return (int64_t)h.n;
+}
+
+/* Payload start of block i, found the way a parallel decoder finds it: the
+ * stored offset of its segment plus the sizes of the earlier blocks of the
+ * same segment (ZipServ Abstract: constant-time, parallel decoding; ENEC
+ * Abstract: intra-segment scan). */
+static uint64_t block_payload_start(const uint8_t *s, const orc_header *h, uint64_t i) {
+  uint64_t seg = i / ORC_SEG_BLOCKS;
+  uint64_t off = get_le(s + h->segoff_off + 8 * seg, 8);
+  for (uint64_t k = seg * ORC_SEG_BLOCKS; k < i; k++)
+    off += orc_block_payload_bytes(s[h->meta_off + 2 * k + 1], block_len(h->n, h->B, k));
+  return h->payload_off + off;
+}
+
+/* Decoder for one element j of a validated non-RAW stream (the per-element
+ * definition: locate block, read the w-bit field, add the base, rejoin). */
+static uint16_t decode_one(const uint8_t *s, const orc_header *h, uint64_t j, uint64_t qstart) {
+  uint64_t i = j / h->B, t = j - i * h->B;
+  unsigned base = s[h->meta_off + 2 * i];
+  unsigned w = s[h->meta_off + 2 * i + 1];
+  unsigned d = 0;
+  for (unsigned b = 0; b < w; b++) d |= get_bit(s + qstart, (uint64_t)t * w + b) << b;
+  unsigned e = (base + d) & 0xFFu;
+  return orc_join(s[h->sm_off + j], e);
+}
+
+/* Full decoder. out must hold n elements (n = the stream's element count).
+ * Returns ORC_OK or a negative status. */
+int orc_decode(const uint8_t *s, uint64_t bytes, uint16_t *out, uint64_t n) {
+  orc_header h;
+  int st = parse_header(s, bytes, &h);
+  if (st != ORC_OK) return st;
+  if (n != h.n) return ORC_E_ARG;
+  if (h.flags == ORC_FLAG_RAW) {
+    for (uint64_t j = 0; j < n; j++) out[j] = (uint16_t)get_le(s + h.raw_off + 2 * j, 2);
+    return ORC_OK;
+  }
+  for (uint64_t i = 0; i < h.nb; i++) {
+    uint64_t q = block_payload_start(s, &h, i);
+    uint64_t len = block_len(h.n, h.B, i);
+    for (uint64_t t = 0; t < len; t++) out[i * h.B + t] = decode_one(s, &h, i * h.B + t, q);
+  }
+  return ORC_OK;
+}
+
+/* Decoder for elements [first, first + count) only (for sampled checks of
+ * large tensors). Same definition as orc_decode. */
+int orc_decode_range(const uint8_t *s, uint64_t bytes, uint64_t first, uint64_t count,
+                     uint16_t *out) {
+  orc_header h;
+  int st = parse_header(s, bytes, &h);
+  if (st != ORC_OK) return st;
+  if (first > h.n || count > h.n - first) return ORC_E_ARG;
+  for (uint64_t j = first; j < first + count; j++) {
+    if (h.flags == ORC_FLAG_RAW) {
+      out[j - first] = (uint16_t)get_le(s + h.raw_off + 2 * j, 2);
+    } else {
+      uint64_t i = j / h.B;
+      out[j - first] = decode_one(s, &h, j, block_payload_start(s, &h, i));
+    }
+  }
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * GEMM oracle (ZipServ Abstract: the fused decompress-GEMM computes the same
+ * product as decompression followed by a GEMM). Y[m][n] = sum_k X[m][k] *
+ * W[k][n] in double precision, k ascending for every output; absb[m][n] =
+ * sum_k |X[m][k] * W[k][n]|. X is [M,K], W is [K,N], both BF16 row-major.
+ * Products of two BF16 values are exact in double.
+ * ------------------------------------------------------------------------- */
+double orc_bf16_to_double(uint16_t v) {
+  uint32_t u = (uint32_t)v << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+void orc_gemm_f64(const uint16_t *X, uint32_t M, uint32_t K, const uint16_t *W, uint32_t N,
+                  double *Y, double *absb) {
+  for (uint64_t i = 0; i < (uint64_t)M * N; i++) {
+    Y[i] = 0.0;
+    if (absb) absb[i] = 0.0;
+  }
+  for (uint32_t m = 0; m < M; m++) {
+    for (uint32_t k = 0; k < K; k++) {
+      double xv = orc_bf16_to_double(X[(uint64_t)m * K + k]);
+      const uint16_t *wrow = W + (uint64_t)k * N;
+      double *yrow = Y + (uint64_t)m * N;
+      double *arow = absb ? absb + (uint64_t)m * N : NULL;
+      for (uint32_t n = 0; n < N; n++) {
+        double p = xv * orc_bf16_to_double(wrow[n]);
+        yrow[n] += p;
+        if (arow) arow[n] += p < 0 ? -p : p;
+      }
+    }
+  }
+}
+
+/* Same product for a chosen set of columns only: Y[m][c], absb[m][c] for
+ * c in [0, ncols), column index cols[c]. */
+void orc_gemm_f64_cols(const uint16_t *X, uint32_t M, uint32_t K, const uint16_t *W, uint32_t N,
+                       const uint32_t *cols, uint32_t ncols, double *Y, double *absb) {
+  for (uint32_t m = 0; m < M; m++) {
+    for (uint32_t c = 0; c < ncols; c++) {
+      double acc = 0.0, aacc = 0.0;
+      for (uint32_t k = 0; k < K; k++) {
+        double p = orc_bf16_to_double(X[(uint64_t)m * K + k]) *
+                   orc_bf16_to_double(W[(uint64_t)k * N + cols[c]]);
+        acc += p;
+        aacc += p < 0 ? -p : p;
+      }
+      Y[(uint64_t)m * ncols + c] = acc;
+      if (absb) absb[(uint64_t)m * ncols + c] = aacc;
+    }
+  }
+}

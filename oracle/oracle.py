@@ -1,0 +1,192 @@
+"""ctypes loader for the C oracle (``enc_oracle.c``).
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only the test suite, the smoke
+check and the benchmark's CPU-baseline leg import this module. It builds the
+oracle with the host C compiler when the shared library is missing and never
+touches the GPU library.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "enc_oracle.c")
+_LIB = os.path.join(_HERE, "liborc.so")
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force=False):
+    """Compile the oracle with gcc (plain -O2, no vector intrinsics)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
+                               "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        L.orc_exponent.argtypes = [ctypes.c_uint16]
+        L.orc_exponent.restype = ctypes.c_uint
+        L.orc_signmant.argtypes = [ctypes.c_uint16]
+        L.orc_signmant.restype = ctypes.c_uint
+        L.orc_join.argtypes = [ctypes.c_uint, ctypes.c_uint]
+        L.orc_join.restype = ctypes.c_uint16
+        L.orc_bit_width.argtypes = [ctypes.c_uint]
+        L.orc_bit_width.restype = ctypes.c_uint
+        L.orc_block_payload_bytes.argtypes = [ctypes.c_uint, ctypes.c_uint64]
+        L.orc_block_payload_bytes.restype = ctypes.c_uint64
+        L.orc_block_params.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32, _u8p, _u8p]
+        L.orc_block_params.restype = ctypes.c_int64
+        L.orc_stream_size.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32]
+        L.orc_stream_size.restype = ctypes.c_int64
+        L.orc_encode.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32, _u8p, ctypes.c_uint64]
+        L.orc_encode.restype = ctypes.c_int64
+        L.orc_stream_elements.argtypes = [_u8p, ctypes.c_uint64]
+        L.orc_stream_elements.restype = ctypes.c_int64
+        L.orc_decode.argtypes = [_u8p, ctypes.c_uint64, _u16p, ctypes.c_uint64]
+        L.orc_decode.restype = ctypes.c_int
+        L.orc_decode_range.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                       _u16p]
+        L.orc_decode_range.restype = ctypes.c_int
+        L.orc_gemm_f64.argtypes = [_u16p, ctypes.c_uint32, ctypes.c_uint32, _u16p,
+                                   ctypes.c_uint32, _f64p, _f64p]
+        L.orc_gemm_f64.restype = None
+        L.orc_gemm_f64_cols.argtypes = [_u16p, ctypes.c_uint32, ctypes.c_uint32, _u16p,
+                                        ctypes.c_uint32, _u32p, ctypes.c_uint32, _f64p, _f64p]
+        L.orc_gemm_f64_cols.restype = None
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _u16(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("expected uint16 BF16 bit patterns")
+    return x.reshape(-1)
+
+
+def exponent(v):
+    return lib().orc_exponent(int(v))
+
+
+def signmant(v):
+    return lib().orc_signmant(int(v))
+
+
+def join(sm, e):
+    return lib().orc_join(int(sm), int(e))
+
+
+def bit_width(r):
+    return lib().orc_bit_width(int(r))
+
+
+def block_payload_bytes(w, L):
+    return lib().orc_block_payload_bytes(int(w), int(L))
+
+
+def block_params(x, B):
+    """(base[nb], width[nb]) as uint8 arrays."""
+    x = _u16(x)
+    nb = -(-x.size // B)
+    base = np.zeros(max(nb, 1), np.uint8)
+    w = np.zeros(max(nb, 1), np.uint8)
+    r = lib().orc_block_params(_ptr(x, _u16p), x.size, B, _ptr(base, _u8p), _ptr(w, _u8p))
+    if r < 0:
+        raise OracleError("block_params failed: %d" % r)
+    return base[:nb], w[:nb]
+
+
+def stream_size(x, B):
+    x = _u16(x)
+    r = lib().orc_stream_size(_ptr(x, _u16p), x.size, B)
+    if r < 0:
+        raise OracleError("stream_size failed: %d" % r)
+    return int(r)
+
+
+def encode(x, B):
+    """Stream bytes (np.uint8 array) for the BF16 patterns x at block size B."""
+    x = _u16(x)
+    size = stream_size(x, B)
+    out = np.empty(size, np.uint8)
+    r = lib().orc_encode(_ptr(x, _u16p), x.size, B, _ptr(out, _u8p), out.size)
+    if r < 0:
+        raise OracleError("encode failed: %d" % r)
+    assert r == size
+    return out
+
+
+def stream_elements(s):
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    return int(lib().orc_stream_elements(_ptr(s, _u8p), s.size))
+
+
+def decode(s):
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    n = stream_elements(s)
+    if n < 0:
+        raise OracleError("bad stream: %d" % n)
+    out = np.empty(max(n, 1), np.uint16)
+    r = lib().orc_decode(_ptr(s, _u8p), s.size, _ptr(out, _u16p), n)
+    if r != 0:
+        raise OracleError("decode failed: %d" % r)
+    return out[:n]
+
+
+def decode_range(s, first, count):
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    out = np.empty(max(count, 1), np.uint16)
+    r = lib().orc_decode_range(_ptr(s, _u8p), s.size, first, count, _ptr(out, _u16p))
+    if r != 0:
+        raise OracleError("decode_range failed: %d" % r)
+    return out[:count]
+
+
+def gemm_f64(X, W):
+    """(Y, absbound) in float64 for X [M,K] and W [K,N] given as uint16 BF16 bits."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    M, K = X.shape
+    K2, N = W.shape
+    assert K == K2
+    Y = np.empty((M, N), np.float64)
+    A = np.empty((M, N), np.float64)
+    lib().orc_gemm_f64(_ptr(X, _u16p), M, K, _ptr(W, _u16p), N, _ptr(Y, _f64p), _ptr(A, _f64p))
+    return Y, A
+
+
+def gemm_f64_cols(X, W, cols):
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    cols = np.ascontiguousarray(cols, dtype=np.uint32)
+    M, K = X.shape
+    K2, N = W.shape
+    assert K == K2 and (cols < N).all()
+    Y = np.empty((M, cols.size), np.float64)
+    A = np.empty((M, cols.size), np.float64)
+    lib().orc_gemm_f64_cols(_ptr(X, _u16p), M, K, _ptr(W, _u16p), N, _ptr(cols, _u32p), cols.size,
+                            _ptr(Y, _f64p), _ptr(A, _f64p))
+    return Y, A
