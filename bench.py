@@ -1,0 +1,324 @@
+"""Decompression throughput of the 8B-shaped BF16 weight set on one MI355X.
+
+One step = one batched decode (a single kernel launch) of all 226 compressed
+tensors of the set (32 Llama-3-8B-shaped layers + embedding + LM head,
+8,029,995,008 values, 16.06 GB of BF16 out), with the compressed streams
+already resident in HBM: every weight is streamed once per step, as in
+single-stream inference. The streams are made once, before timing, by the
+GPU encoder (encode throughput is reported too), and the decoded outputs are
+checked bit-exactly against the inputs after the timed region.
+
+Printed as ONE JSON line: metric/value (BF16-out GB/s), roofline of the
+decode kernel (algorithmic HBM bytes per launch / launch time vs 8 TB/s),
+compression ratio, the measured device copy ceiling, the fused
+decompress-GEMM against the same GEMM on uncompressed weights, and the CPU
+oracle timed on a bounded sample on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+METRIC = "decompress GB/s (BF16 out) + % of HBM roofline; compression ratio"
+DECODE_SRC = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc", "decode.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_batch_set8b_pmc.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--block-size", type=int, default=512)
+    p.add_argument("--layers", type=int, default=32,
+                   help="decoder layers in the set (32 = the full 8B shape)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--cpu-sample-tensors", type=int, default=7,
+                   help="tensors of layer 0 the CPU oracle decodes (bounded sample)")
+    return p.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(n_launch_bytes):
+    """HBM bytes per decode launch from the committed rocprofv3 PMC summary,
+    if it was taken on the current decode kernel source; else None."""
+    try:
+        d = json.load(open(PMC_SUMMARY))
+    except (OSError, ValueError):
+        return None
+    if d.get("decode_source_sha256_16") != source_hash(DECODE_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode shards by tensor or by segment with no communication)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from lossless_weight_compression_amd import enc, synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    B = args.block_size
+
+    shapes = synth.set8b_shapes()
+    if args.layers != 32:
+        keep = ["L%d." % l for l in range(args.layers)]
+        idx = [i for i, (nm, _, _) in enumerate(shapes)
+               if any(nm.startswith(k) for k in keep) or nm in ("embed", "lm_head")]
+    else:
+        idx = list(range(len(shapes)))
+
+    # ---- compress once (GPU encoder), timing each call ----------------------
+    streams, enc_ms, n_total, comp_total = [], 0.0, 0, 0
+    algo_read = 0
+    ws_cache = {}
+    for i in idx:
+        x = synth.set8b_tensor_gpu(i, device=dev)
+        n = x.numel()
+        out = torch.empty(enc.enc_compress_bound(n), dtype=torch.uint8, device=dev)
+        wsb = enc.enc_compress_workspace_bytes(n, B)
+        ws = ws_cache.get(wsb)
+        if ws is None:
+            ws = ws_cache[wsb] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        comp, info = enc.enc_compress(x, B, out=out, ws=ws)   # synchronises once inside
+        torch.cuda.synchronize()
+        enc_ms += (time.perf_counter() - t0) * 1e3
+        streams.append((comp.clone(), info))
+        n_total += n
+        comp_total += info.total_bytes
+        if info.flags == 1:
+            algo_read += 2 * n
+        else:
+            algo_read += n + 2 * info.n_blocks + 8 * info.n_segments + info.payload_bytes
+        del x, out, comp
+    ws_cache.clear()
+    torch.cuda.empty_cache()
+    ratio = 2 * n_total / comp_total
+    log("compressed %d tensors, %d values, ratio %.4f, encode %.1f ms"
+        % (len(idx), n_total, ratio, enc_ms))
+
+    # ---- batched decode: one launch per step ---------------------------------
+    outs = [torch.empty(streams[k][1].n_elems, dtype=torch.int16, device=dev)
+            for k in range(len(idx))]
+    table = enc.enc_batch_prepare([(c, inf, o) for (c, inf), o in zip(streams, outs)])
+    count = len(idx)
+    for _ in range(args.warmup):
+        enc.enc_decompress_batch(table, count)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        enc.enc_decompress_batch(table, count)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = float(np.mean(launch_ms))
+    step_ms = max(wall_ms, avg_launch_ms)
+    out_bytes = 2 * n_total
+    launch_bytes = algo_read + out_bytes
+    value = out_bytes / (step_ms * 1e-3) / 1e9
+    achieved = launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    log("decode: %.3f ms/step (launch avg %.3f, min %.3f), %.1f GB/s out, %.1f GB/s HBM"
+        % (step_ms, avg_launch_ms, min(launch_ms), value, achieved))
+
+    # ---- correctness of what was timed (outside the timed region) ------------
+    for k, i in enumerate(idx):
+        x = synth.set8b_tensor_gpu(i, device=dev).reshape(-1)
+        if not torch.equal(outs[k], x):
+            log("MISMATCH in tensor", shapes[i][0])
+            sys.exit(1)
+        del x
+    log("all decoded tensors bit-exact")
+    del outs
+    torch.cuda.empty_cache()
+
+    # ---- device copy ceiling (same sizes as one step, 2 x 4 GiB) -------------
+    a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * a.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": ("set8b: %d x Llama-3-8B layer (q,o 4096x4096; k,v 4096x1024; gate,up "
+                         "4096x14336; down 14336x4096) + 128256x4096 embedding + LM head; BF16 "
+                         "N(0, sigma ~ U(0.01,0.05)) with 0.1%% of entries x20; decode all per step"
+                         % args.layers),
+            "tensors": len(idx),
+            "elements": n_total,
+            "block_size": B,
+        },
+        "compression_ratio": round(ratio, 5),
+        "hbm_gbs": round(achieved, 1),
+        "hbm_frac_of_8tbs": round(achieved / HBM_PEAK_GBS, 4),
+        "copy_ceiling_gbs": round(copy_gbs, 1),
+        "hbm_frac_of_copy": round(achieved / copy_gbs, 4),
+        "encode_gbs": round((2 * n_total + comp_total) / (enc_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_decode_batch",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(launch_bytes),
+            "algorithmic_bytes_per_launch": launch_bytes,
+            "avg_launch_ms": round(avg_launch_ms, 4),
+        },
+    }
+
+    if not args.no_gemm:
+        result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(synth, np, torch, dev, args.cpu_sample_tensors, B)
+
+    print(json.dumps(result), flush=True)
+
+
+def _time(fn, stream, torch, reps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return sorted(s.elapsed_time(e) for s, e in ev)
+
+
+def bench_gemm(enc, synth, torch, np, dev, stream):
+    """Y = X W with W 4096x14336 compressed (B=512) vs the same GEMM on the
+    uncompressed W, M in {1, 16, 128}; 4 rotating weight copies so the
+    working set exceeds the 256 MB last-level cache."""
+    K, N = 4096, 14336
+    W = torch.from_numpy(synth.gemm_weight(K, N).view(np.int16)).to(dev)
+    copies = 4
+    Ws = [W.clone() for _ in range(copies)]
+    comps = [enc.enc_compress(w, 512) for w in Ws]
+    out = {"shape": "X[M,4096] x W[4096,14336], W compressed at B=512",
+           "w_bytes_compressed": comps[0][1].total_bytes, "w_bytes_dense": 2 * K * N}
+    for M in (1, 16, 128):
+        X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = enc.gemm_workspace(M, K, N, 512, dev)
+        try:
+            k = [0]
+
+            def fused():
+                c, inf = comps[k[0] % copies]
+                enc.enc_decompress_gemm(X, c, inf, N, y=Y, ws=ws)
+                k[0] += 1
+
+            def dense():
+                enc.enc_gemm_dense(X, Ws[k[0] % copies], y=Y, ws=ws)
+                k[0] += 1
+
+            for _ in range(3):
+                fused()
+                dense()
+            torch.cuda.synchronize()
+            tf = _time(fused, stream, torch, 20)
+            td = _time(dense, stream, torch, 20)
+            Xb = X.view(torch.bfloat16)
+            tb = _time(lambda: torch.matmul(Xb, Ws[k[0] % copies].view(torch.bfloat16)), stream,
+                       torch, 20)
+            med = lambda t: t[len(t) // 2]
+            flops = 2.0 * M * K * N
+            bytes_f = comps[0][1].total_bytes + 2 * M * K + 4 * M * N
+            out["M%d" % M] = {
+                "fused_us": round(med(tf) * 1e3, 2),
+                "dense_same_kernel_us": round(med(td) * 1e3, 2),
+                "torch_matmul_bf16_us": round(med(tb) * 1e3, 2),
+                "fused_hbm_gbs": round(bytes_f / (med(tf) * 1e-3) / 1e9, 1),
+                "fused_tflops": round(flops / (med(tf) * 1e-3) / 1e12, 2),
+                "mfma_util_vs_2.5pf": round(flops / (med(tf) * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+                "speedup_vs_dense": round(med(td) / med(tf), 3),
+            }
+        except Exception as e:  # the GEMM kernels report through EncError
+            out["M%d" % M] = {"error": str(e)}
+    return out
+
+
+def cpu_baseline(synth, np, torch, dev, ntensors, B):
+    """The CPU oracle, as it is (plain C, one thread), decoding the oracle's
+    own streams of the first `ntensors` tensors of layer 0 of the set."""
+    from oracle import oracle as orc
+    orc.build()
+    n_total = 0
+    enc_s = dec_s = 0.0
+    for i in range(ntensors):
+        x = synth.set8b_tensor_gpu(i, device=dev).cpu().numpy().view(np.uint16).reshape(-1)
+        t0 = time.perf_counter()
+        s = orc.encode(x, B)
+        enc_s += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        y = orc.decode(s)
+        dec_s += time.perf_counter() - t0
+        assert np.array_equal(y, x)
+        n_total += x.size
+    names = [synth.set8b_shapes()[i][0] for i in range(ntensors)]
+    return {
+        "value": round(2 * n_total / dec_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "oracle decode of its own streams of %s (%d values, %.2f GB BF16 out), B=%d; "
+                  "oracle encode %.2f GB/s" % ("+".join(names), n_total, 2 * n_total / 1e9, B,
+                                               2 * n_total / enc_s / 1e9),
+        "decode_s": round(dec_s, 3),
+        "encode_s": round(enc_s, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

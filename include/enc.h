@@ -1,0 +1,170 @@
+/*
+ * enc.h -- C ABI of libenc.so: lossless block-based fixed-length coding of
+ * BF16 weights on MI355X (gfx950), with a fused decompress-GEMM.
+ *
+ * What the operations are (the pages give abstracts, no interface):
+ *  - "ENEC: A Lossless AI Model Compression Method Enabling Fast Inference on
+ *    Ascend NPUs", Abstract: weights are compressed losslessly with a
+ *    block-based fixed-length code (per-block bit width, bit-packing, a
+ *    branch-free integer transform, an intra-segment prefix scan of block
+ *    sizes) so that less weight data has to be moved at inference time.
+ *  - "ZipServ: Fast and Memory-Efficient LLM Inference with Hardware-Aware
+ *    Lossless Compression", Abstract: a fixed-length format decodes in
+ *    constant time and in parallel, and a fused decompress-GEMM consumes the
+ *    compressed weights directly, with no intermediate decompressed buffer.
+ *  - "MINE: Entropy-coded Memory-efficient Inference for Large Language
+ *    Models", Abstract: single-stream decoding is memory-bound because every
+ *    weight is streamed once per generated token.
+ *
+ * Stream format (little-endian; all pad bytes zero):
+ *   [0, 256)            header: "ENCB", u16 version=1, u16 dtype=1 (BF16),
+ *                       u32 flags (bit 0 = RAW), u32 block_size, u32 64,
+ *                       u32 0, then u64 n_elems, n_blocks, n_segments, sm_off,
+ *                       meta_off, segoff_off, payload_off, payload_bytes,
+ *                       raw_off, total_bytes; bytes 104..255 zero.
+ *   sm_off = 256        u8[n]: sign (bit 7) and mantissa (bits 6..0) of each
+ *                       value, section padded to a multiple of 256.
+ *   meta_off            u8[2 * n_blocks]: {base, width} per block, padded.
+ *   segoff_off          u64[n_segments]: exclusive prefix sum of padded block
+ *                       payload sizes at each 64-block segment start, padded.
+ *   payload_off         per block, ceil(width * len / 8) bytes rounded up to
+ *                       16: the codes exponent - base, width bits each, packed
+ *                       LSB first in element order.
+ *   RAW streams (flags bit 0): header, then the n input values verbatim at
+ *   raw_off = 256; chosen when the coded stream would not be smaller.
+ *   A stream is valid only if every decoded exponent base + code is <= 255
+ *   (always true for streams this library or the reference encoder wrote).
+ *
+ * Conventions for every entry point:
+ *  - d_ pointers are device (HBM) pointers, h_ pointers are host pointers.
+ *    The caller owns every buffer; the library never allocates or frees
+ *    device memory, and keeps no state between calls.
+ *  - Device buffers holding streams, BF16 arrays and float arrays must be
+ *    16-byte aligned; inputs and outputs must not overlap.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous on that stream unless stated otherwise; a fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - Every entry point checks its arguments on the host before launching
+ *    anything; failures return a negative enc_status and set a thread-local
+ *    message readable with enc_last_error(). Nothing is launched on failure.
+ */
+#ifndef ENC_H
+#define ENC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum enc_status {
+  ENC_OK = 0,
+  ENC_ERR_INVALID_ARG = -1, /* null pointer, misalignment, bad size or block size */
+  ENC_ERR_UNSUPPORTED = -2, /* valid request outside what the kernels implement */
+  ENC_ERR_CAPACITY = -3,    /* output or workspace buffer too small */
+  ENC_ERR_BAD_STREAM = -4,  /* header or layout of a stream is inconsistent */
+  ENC_ERR_SHAPE = -5,       /* GEMM shapes do not match the stream */
+  ENC_ERR_HIP = -6          /* a HIP runtime call or a launch failed */
+} enc_status;
+
+/* Parsed header of a stream (field meanings as in the format above). */
+typedef struct enc_info {
+  uint32_t version, dtype, flags, block_size;
+  uint64_t n_elems, n_blocks, n_segments;
+  uint64_t sm_off, meta_off, segoff_off, payload_off, payload_bytes, raw_off, total_bytes;
+} enc_info;
+
+/* Largest stream any n-element input can produce: 256 + 2 n (the RAW size). */
+uint64_t enc_compress_bound(uint64_t n_elems);
+
+/* Device workspace bytes enc_compress needs for n elements at block size B
+ * (per-block {base, width}, per-segment sums and offsets, a size slot).
+ * Returns 0 for an unsupported block size. */
+uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size);
+
+/* Compress n BF16 values (bit patterns) d_in into d_out (ENEC Abstract).
+ * Block size: 128, 256, 512, 1024, 2048 or 4096. Launches the width/segment
+ * kernel, the scan of segment sizes and the pack kernel on `stream`; then
+ * synchronises `stream` once to read back the stream size (the only blocking
+ * point of the library), and fills *h_info. The bytes written are exactly
+ * those of the reference encoder for the same input. out_capacity must be
+ * at least the final stream size (enc_compress_bound(n) always suffices). */
+enc_status enc_compress(const uint16_t *d_in, uint64_t n_elems, uint32_t block_size, void *d_out,
+                        uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream,
+                        enc_info *h_info);
+
+/* Parse and check a stream header held in host memory (header_bytes >= 256)
+ * for a stream of comp_bytes bytes. Checks magic, version, dtype, flags,
+ * block size, section offsets against n, and total <= comp_bytes. Host only;
+ * launches nothing. */
+enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_t comp_bytes,
+                            enc_info *h_info);
+
+/* Copy the 256-byte header of a device stream to the host (synchronous on
+ * `stream`) and parse it with enc_parse_header. */
+enc_status enc_read_info(const void *d_comp, uint64_t comp_bytes, void *stream, enc_info *h_info);
+
+/* Decompress a whole stream into out_elems BF16 values (ZipServ Abstract:
+ * constant-time, parallel decoding). One kernel launch; asynchronous;
+ * allocates nothing. h_info must describe d_comp (enc_read_info or the
+ * enc_info enc_compress returned); out_elems must equal its n_elems. */
+enc_status enc_decompress(const void *d_comp, const enc_info *h_info, uint16_t *d_out,
+                          uint64_t out_elems, void *stream);
+
+/* Batched decompression: many streams, one launch (a model's whole weight
+ * set decoded per step, as single-stream inference streams every weight
+ * once per token -- MINE Abstract). */
+typedef struct enc_item {
+  const void *d_comp; /* device stream */
+  uint16_t *d_out;    /* device output, info.n_elems values */
+  enc_info info;      /* parsed header of d_comp */
+} enc_item;
+
+/* Device bytes of the batch table for `count` items. */
+uint64_t enc_batch_table_bytes(int count);
+
+/* Validate the items and write the batch table into d_table (device, at least
+ * enc_batch_table_bytes(count) bytes). Synchronous: returns after the table
+ * has been copied. The table stays valid while the streams and outputs do. */
+enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table,
+                             uint64_t table_bytes, void *stream);
+
+/* Decode every item of a prepared table with one kernel launch; asynchronous. */
+enc_status enc_decompress_batch(const void *d_table, int count, void *stream);
+
+/* Device workspace bytes for enc_decompress_gemm (split-K partial sums,
+ * arrival counters, per-block offset index). */
+uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size);
+
+/* Fused decompress-GEMM (ZipServ Abstract: decompress on the fly into the
+ * matrix units, no intermediate decompressed weights in HBM):
+ *   Y[M,N] (fp32, overwritten) = X[M,K] (BF16 row-major) * W[K,N]
+ * where W is the row-major BF16 matrix compressed in d_wcomp (n_elems = K*N).
+ * Requirements: K*N == n_elems, N % 512 == 0 and N % block_size == 0,
+ * 1 <= M <= 4096, else ENC_ERR_SHAPE / ENC_ERR_UNSUPPORTED. A RAW stream is
+ * multiplied directly from its verbatim values. The workspace must be at
+ * least enc_gemm_workspace_bytes(M, K, N, block_size) bytes and must be
+ * zero-filled before its first use; calls leave it zero-filled again, so it
+ * can be reused by later calls on the same stream (not by concurrent calls).
+ * Accumulation is fp32; the result is deterministic. */
+enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
+                               const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
+                               uint64_t ws_bytes, void *stream);
+
+/* The same GEMM on an uncompressed BF16 W[K,N] (same kernels with the decode
+ * stage replaced by plain loads): the baseline the fused path is compared
+ * with. Same workspace rules, with block_size 512. */
+enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
+                          uint32_t N, float *d_y, void *d_ws, uint64_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *enc_status_string(enc_status s);
+
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char *enc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENC_H */

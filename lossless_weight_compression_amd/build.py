@@ -1,0 +1,71 @@
+"""Build libenc.so (gfx950 HIP kernels + C-ABI host code) in-tree with hipcc.
+
+    python -m lossless_weight_compression_amd.build
+
+Objects go to ``_build/`` at the repository root; the shared library is
+written next to this file so the binding finds it without installation.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(PKG, "libenc.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+SOURCES = ["decode.hip", "encode.hip", "gemm.hip", "enc_api.cpp"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+    # no packed-fp32 instructions in any kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build failed: %s\n%s" % (" ".join(cmd), out))
+    if out.strip():
+        print(out)
+
+
+def build(verbose=True):
+    """Compile every source for gfx950 and link libenc.so (always rebuilds)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        lang = ["-x", "hip"]
+        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+        objs.append(obj)
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        out = "\n".join(l for l in out.splitlines()
+                        if "packed-fp32-ops' is not a recognized feature" not in l)
+        if p.returncode != 0:
+            raise RuntimeError("build failed: %s\n%s" % (" ".join(cmd), out))
+        if out.strip() and verbose:
+            print(out)
+    tmp = OUT + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
+    os.replace(tmp, OUT)
+    if verbose:
+        print("built", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

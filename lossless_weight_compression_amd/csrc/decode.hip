@@ -1,0 +1,209 @@
+// decode.hip -- gfx950 decoder for the block-based fixed-length BF16 stream.
+//
+// "ENEC: A Lossless AI Model Compression Method Enabling Fast Inference on
+// Ascend NPUs", Abstract: block-based fixed-length code with per-block bit
+// width and an intra-segment prefix scan of block sizes. "ZipServ: Fast and
+// Memory-Efficient LLM Inference with Hardware-Aware Lossless Compression",
+// Abstract: a fixed-length format decodes in constant time and in parallel.
+//
+// Mapping onto CDNA4 (wave64, 256 CUs in 8 XCDs):
+//  * a workgroup (4 waves) decodes one tile of 1024 groups = 8192 values;
+//    lane t owns groups t, t+256, t+512, t+768 of the tile, so every wave
+//    instruction touches 64 consecutive groups: 512 contiguous bytes of the
+//    sign+mantissa plane, one contiguous run of packed codes, and 1 KiB of
+//    contiguous output (one 16-byte store per lane);
+//  * each wave re-derives the payload offsets of the tile's 64-block segment
+//    itself: lane j reads block j's {base, width}, computes the padded payload
+//    size and a wave64 inclusive scan gives every block's start -- no
+//    workgroup barrier and no LDS;
+//  * a group's 8 codes of w bits are exactly w bytes starting on a byte
+//    boundary; the lane loads the (up to three) dwords that cover them,
+//    funnel-shifts them into place (v_alignbit) and cuts the fields with
+//    v_bfe; exponent bytes get the block base with one packed add (a valid
+//    stream never carries out of a byte), and v_bfi/v_perm interleave them
+//    with the sign+mantissa bytes into four BF16 pairs;
+//  * every load of a tile's groups is issued before any of them is decoded,
+//    so each lane keeps 4 groups of reads in flight;
+//  * the grid is persistent (a few workgroups per CU, striding over tiles),
+//    which also serves the batched decode of a whole weight set in one launch.
+#include "enc_common.h"
+#include "group_math.h"
+
+namespace enc {
+namespace {
+
+constexpr uint32_t GPT = kGroupsPerThread;
+
+// Tail group: store only the elements below n (no dynamically indexed array,
+// so nothing is placed in scratch or LDS).
+__device__ __forceinline__ void store_partial(uint16_t *out, uint64_t e0, uint64_t n, uint4 o) {
+#pragma unroll
+  for (uint32_t k = 0; k < 8; ++k) {
+    const uint32_t word = k < 2 ? o.x : k < 4 ? o.y : k < 6 ? o.z : o.w;
+    if (e0 + k < n) out[e0 + k] = (uint16_t)(word >> (16 * (k & 1)));
+  }
+}
+
+__device__ __forceinline__ void copy_group_raw(const uint16_t *__restrict__ src,
+                                               uint16_t *__restrict__ out, uint64_t e0, uint64_t n,
+                                               uint4 v) {
+  if (e0 + 8 <= n) {
+    *reinterpret_cast<uint4 *>(out + e0) = v;
+  } else {
+    for (uint64_t e = e0; e < n; ++e) out[e] = src[e];
+  }
+}
+
+// RAW stream: the values sit verbatim after the header; copy the tile with
+// all four 16-byte loads of a lane issued before the stores.
+__device__ __forceinline__ void copy_tile_raw(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
+  const uint16_t *__restrict__ src = reinterpret_cast<const uint16_t *>(d.stream + kHeaderBytes);
+  uint16_t *__restrict__ out = d.out;
+  const uint64_t e_a = tile * kTileElems + (uint64_t)tid * 8;
+  const uint64_t e_b = e_a + 8 * kThreads, e_c = e_b + 8 * kThreads, e_d = e_c + 8 * kThreads;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const uint4 va = e_a + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_a) : z;
+  const uint4 vb = e_b + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_b) : z;
+  const uint4 vc = e_c + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_c) : z;
+  const uint4 vd = e_d + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_d) : z;
+  if (e_a < d.n) copy_group_raw(src, out, e_a, d.n, va);
+  if (e_b < d.n) copy_group_raw(src, out, e_b, d.n, vb);
+  if (e_c < d.n) copy_group_raw(src, out, e_c, d.n, vc);
+  if (e_d < d.n) copy_group_raw(src, out, e_d, d.n, vd);
+}
+static_assert(kGroupsPerThread == 4, "copy_tile_raw is written for 4 groups per lane");
+
+__device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
+  if (d.raw) {
+    copy_tile_raw(d, tile, tid);
+    return;
+  }
+  const uint8_t *__restrict__ s = d.stream;
+  uint16_t *__restrict__ out = d.out;
+  const uint64_t n = d.n;
+  const uint32_t lane = tid & 63;
+  const uint32_t log2gpb = d.log2b - 3;       // groups per block
+  const uint32_t log2gps = log2gpb + 6;       // groups per segment
+  const uint64_t g0 = tile * kTileGroups;
+  const uint64_t seg = g0 >> log2gps;
+  const uint32_t gs0 = (uint32_t)(g0 & ((1ull << log2gps) - 1));
+
+  // Per-wave scan of the segment's padded block payload sizes.
+  const uint64_t blk = (seg << 6) + lane;
+  uint32_t P = 0, pk = 0;
+  if (blk < d.nb) {
+    const uint32_t m = *reinterpret_cast<const uint16_t *>(s + d.meta_off + 2 * blk);
+    const uint32_t w = m >> 8;
+    const uint32_t L = (blk + 1 == d.nb) ? (uint32_t)(n - ((d.nb - 1) << d.log2b)) : (1u << d.log2b);
+    P = (((w * L + 7) >> 3) + 15) & ~15u;
+    pk = ((m & 0xFFu) << 24) | (w << 20);
+  }
+  const uint32_t incl = wave_incl_scan(P, lane);
+  pk |= incl - P;   // exclusive offset < 2^18
+  uint64_t seg_payload =
+      d.payload_off + *reinterpret_cast<const uint64_t *>(s + d.segoff_off + 8 * seg);
+  // Guard against corrupted streams (checked once per wave, not per group):
+  // a width above 8 or a segment whose payload runs past the stream end
+  // decodes as width 0, so no lane ever reads outside [0, total).
+  const uint32_t seg_bytes = __shfl(incl, 63, 64);
+  if (__any((pk >> 20 & 15u) > 8) || seg_payload + seg_bytes > d.total) {
+    pk = 0;
+    seg_payload = d.payload_off;
+  }
+
+  // Phase 1: issue every load of this lane's groups.
+  uint32_t sml[GPT], smh[GPT], q0[GPT], q1[GPT], q2[GPT], info[GPT];
+#pragma unroll
+  for (uint32_t it = 0; it < GPT; ++it) {
+    const uint32_t q = it * kThreads + tid;
+    const uint64_t e0 = (g0 + q) * 8;
+    const uint32_t gs = gs0 + q;
+    const uint32_t p = __shfl(pk, (int)(gs >> log2gpb), 64);
+    const uint32_t u = gs & ((1u << log2gpb) - 1);
+    const uint32_t w = (p >> 20) & 15u;
+    const uint64_t rem = e0 < n ? n - e0 : 0;
+    const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
+    const uint32_t nbytes = (valid * w + 7) >> 3;
+    const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
+    const uint64_t a = pb & ~3ull;
+    const uint32_t lead = (uint32_t)(pb & 3);
+    // Branch-free, in-bounds addressing: a dword is read only if it holds a
+    // needed byte; otherwise the lane re-reads a dword it does need (or,
+    // with no payload bytes at all, its own sign+mantissa dword).
+    const uint64_t sm_addr = kHeaderBytes + (valid ? e0 : 0);
+    const uint64_t a0 = nbytes ? a : sm_addr;
+    const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
+    const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
+    if (valid) {
+      const uint2 smv = *reinterpret_cast<const uint2 *>(s + kHeaderBytes + e0);
+      sml[it] = smv.x;
+      smh[it] = smv.y;
+      q0[it] = ld32(s + a0);
+      q1[it] = ld32(s + a1);
+      q2[it] = ld32(s + a2);
+    }
+    info[it] = (p & 0xFFF00000u) | (lead << 3) | (valid << 8);
+  }
+
+  // Phase 2: decode and store.
+#pragma unroll
+  for (uint32_t it = 0; it < GPT; ++it) {
+    const uint32_t valid = (info[it] >> 8) & 15u;
+    if (!valid) continue;
+    const uint32_t q = it * kThreads + tid;
+    const uint64_t e0 = (g0 + q) * 8;
+    const uint32_t w = (info[it] >> 20) & 15u;
+    const uint32_t sh = info[it] & 31u;
+    const uint32_t base4 = (info[it] >> 24) * 0x01010101u;
+    const uint32_t lo = __builtin_amdgcn_alignbit(q1[it], q0[it], sh);
+    const uint32_t hi = __builtin_amdgcn_alignbit(q2[it], q1[it], sh);
+    const uint4 o = join_group(lo, hi, w, base4, sml[it], smh[it]);
+    if (valid == 8)
+      *reinterpret_cast<uint4 *>(out + e0) = o;
+    else
+      store_partial(out, e0, n, o);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_decode(DecodeDesc d, uint64_t ntiles) {
+  for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) decode_tile(d, t, threadIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void k_decode_batch(const uint8_t *__restrict__ table) {
+  const BatchHeader *h = reinterpret_cast<const BatchHeader *>(table);
+  const DecodeDesc *items = reinterpret_cast<const DecodeDesc *>(table + sizeof(BatchHeader));
+  const uint64_t *tile_begin =
+      reinterpret_cast<const uint64_t *>(table + sizeof(BatchHeader) + h->count * sizeof(DecodeDesc));
+  const uint64_t total = h->total_tiles;
+  const uint32_t count = h->count;
+  uint32_t cur = 0;
+  for (uint64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    // tiles only move forward for this workgroup: advance the item cursor
+    while (cur + 1 < count && tile_begin[cur + 1] <= t) ++cur;
+    const DecodeDesc d = items[cur];
+    decode_tile(d, t - tile_begin[cur], threadIdx.x);
+  }
+}
+
+uint32_t persistent_grid(uint64_t ntiles) {
+  // 256 CUs x 8 workgroups of 4 waves = 32 waves per CU.
+  const uint64_t cap = 256 * 8;
+  return (uint32_t)(ntiles < cap ? ntiles : cap);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeDesc &d, hipStream_t s) {
+  const uint64_t ntiles = tiles_for(d.n);
+  if (ntiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_decode, dim3(persistent_grid(ntiles)), dim3(kThreads), 0, s, d, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_batch(const void *table, hipStream_t s) {
+  hipLaunchKernelGGL(k_decode_batch, dim3(256 * 8), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint8_t *>(table));
+  return hipGetLastError();
+}
+
+}  // namespace enc

@@ -1,0 +1,470 @@
+// enc_api.cpp -- host side of the C ABI declared in include/enc.h.
+//
+// Validates every argument on the host before anything is launched, sizes
+// workspaces, builds stream headers and launches the gfx950 kernels. No
+// exception crosses the ABI; failures return a negative enc_status and leave
+// a message in a thread-local buffer (enc_last_error).
+#include "enc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "enc_common.h"
+
+using namespace enc;
+
+namespace {
+
+thread_local char g_err[512];
+
+enc_status fail(enc_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+enc_status hip_fail(hipError_t e, const char *what) {
+  return fail(ENC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void clear_err() { g_err[0] = 0; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_block(uint32_t B) {
+  for (uint32_t l = kMinLog2B; l <= kMaxLog2B; ++l)
+    if (B == (1u << l)) return (int)l;
+  return -1;
+}
+
+constexpr uint64_t kMaxElems = 1ull << 40;
+
+struct Layout {
+  uint64_t n, nb, nseg, sm_off, meta_off, segoff_off, payload_off;
+};
+
+Layout layout_of(uint64_t n, uint32_t B) {
+  Layout L;
+  L.n = n;
+  L.nb = (n + B - 1) / B;
+  L.nseg = (L.nb + kSegBlocks - 1) / kSegBlocks;
+  L.sm_off = kHeaderBytes;
+  L.meta_off = L.sm_off + align_up(n, kSectionAlign);
+  L.segoff_off = L.meta_off + align_up(2 * L.nb, kSectionAlign);
+  L.payload_off = L.segoff_off + align_up(8 * L.nseg, kSectionAlign);
+  return L;
+}
+
+void put_le(uint8_t *p, uint64_t v, int nbytes) {
+  for (int i = 0; i < nbytes; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+uint64_t get_le(const uint8_t *p, int nbytes) {
+  uint64_t v = 0;
+  for (int i = 0; i < nbytes; ++i) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+HeaderImage header_of(const enc_info &i) {
+  HeaderImage h;
+  memset(h.bytes, 0, sizeof h.bytes);
+  memcpy(h.bytes, "ENCB", 4);
+  put_le(h.bytes + 4, i.version, 2);
+  put_le(h.bytes + 6, i.dtype, 2);
+  put_le(h.bytes + 8, i.flags, 4);
+  put_le(h.bytes + 12, i.block_size, 4);
+  put_le(h.bytes + 16, kSegBlocks, 4);
+  const uint64_t f[] = {i.n_elems,    i.n_blocks,    i.n_segments,    i.sm_off,
+                        i.meta_off,   i.segoff_off,  i.payload_off,   i.payload_bytes,
+                        i.raw_off,    i.total_bytes};
+  for (int k = 0; k < 10; ++k) put_le(h.bytes + 24 + 8 * k, f[k], 8);
+  return h;
+}
+
+enc_info raw_info(uint64_t n, uint32_t B) {
+  enc_info i;
+  memset(&i, 0, sizeof i);
+  i.version = 1;
+  i.dtype = 1;
+  i.flags = 1;
+  i.block_size = B;
+  i.n_elems = n;
+  i.raw_off = kHeaderBytes;
+  i.total_bytes = kHeaderBytes + 2 * n;
+  return i;
+}
+
+// Consistency of a parsed header with the format (no device data read).
+enc_status check_info(const enc_info *i) {
+  if (!i) return fail(ENC_ERR_INVALID_ARG, "info is NULL");
+  if (i->version != 1 || i->dtype != 1)
+    return fail(ENC_ERR_BAD_STREAM, "version %u / dtype %u not supported", i->version, i->dtype);
+  if (i->n_elems > kMaxElems) return fail(ENC_ERR_UNSUPPORTED, "n_elems above 2^40");
+  if (i->flags == 1) {
+    if (i->n_blocks || i->n_segments || i->sm_off || i->meta_off || i->segoff_off ||
+        i->payload_off || i->payload_bytes || i->raw_off != kHeaderBytes ||
+        i->total_bytes != kHeaderBytes + 2 * i->n_elems)
+      return fail(ENC_ERR_BAD_STREAM, "inconsistent RAW header");
+    return ENC_OK;
+  }
+  if (i->flags != 0) return fail(ENC_ERR_BAD_STREAM, "unknown flags 0x%x", i->flags);
+  if (log2_block(i->block_size) < 0)
+    return fail(ENC_ERR_UNSUPPORTED, "block size %u (library supports 128..4096, powers of two)",
+                i->block_size);
+  if (i->n_elems == 0) return fail(ENC_ERR_BAD_STREAM, "coded stream with zero elements");
+  const Layout L = layout_of(i->n_elems, i->block_size);
+  if (i->n_blocks != L.nb || i->n_segments != L.nseg || i->sm_off != L.sm_off ||
+      i->meta_off != L.meta_off || i->segoff_off != L.segoff_off ||
+      i->payload_off != L.payload_off || i->raw_off != 0 ||
+      i->total_bytes != i->payload_off + i->payload_bytes ||
+      i->payload_bytes > L.nb * (uint64_t)i->block_size + 16 * L.nb || (i->total_bytes & 15))
+    return fail(ENC_ERR_BAD_STREAM, "section offsets do not match n=%llu, B=%u",
+                (unsigned long long)i->n_elems, i->block_size);
+  return ENC_OK;
+}
+
+DecodeDesc desc_of(const void *d_comp, const enc_info &i, uint16_t *d_out) {
+  DecodeDesc d;
+  memset(&d, 0, sizeof d);
+  d.stream = static_cast<const uint8_t *>(d_comp);
+  d.out = d_out;
+  d.n = i.n_elems;
+  d.total = i.total_bytes;
+  if (i.flags == 1) {
+    d.raw = 1;
+    d.log2b = kMinLog2B;
+  } else {
+    d.nb = i.n_blocks;
+    d.meta_off = i.meta_off;
+    d.segoff_off = i.segoff_off;
+    d.payload_off = i.payload_off;
+    d.log2b = (uint32_t)log2_block(i.block_size);
+  }
+  return d;
+}
+
+uint64_t batch_bytes(int count) {
+  return align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
+                      8 * ((uint64_t)count + 1),
+                  256);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t enc_compress_bound(uint64_t n_elems) { return kHeaderBytes + 2 * n_elems; }
+
+uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size) {
+  if (log2_block(block_size) < 0) return 0;
+  const Layout L = layout_of(n_elems, block_size);
+  return align_up(2 * L.nb, kSectionAlign) + align_up(8 * L.nseg, kSectionAlign) + kSectionAlign;
+}
+
+enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, void *d_out,
+                        uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream,
+                        enc_info *h_info) {
+  clear_err();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!h_info) return fail(ENC_ERR_INVALID_ARG, "h_info is NULL");
+  if (!d_out) return fail(ENC_ERR_INVALID_ARG, "d_out is NULL");
+  if (n > 0 && !d_in) return fail(ENC_ERR_INVALID_ARG, "d_in is NULL");
+  const int lb = log2_block(block_size);
+  if (lb < 0)
+    return fail(ENC_ERR_UNSUPPORTED, "block size %u (supported: 128..4096, powers of two)",
+                block_size);
+  if (n > kMaxElems) return fail(ENC_ERR_UNSUPPORTED, "n above 2^40");
+  if (!aligned16(d_in) || !aligned16(d_out) || !aligned16(d_ws))
+    return fail(ENC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const uint64_t raw_total = kHeaderBytes + 2 * n;
+  if (n == 0) {
+    if (out_capacity < raw_total) return fail(ENC_ERR_CAPACITY, "output capacity below 256");
+    const enc_info i = raw_info(0, block_size);
+    hipError_t e = launch_encode_raw(d_in, static_cast<uint8_t *>(d_out), 0, header_of(i), s);
+    if (e != hipSuccess) return hip_fail(e, "raw header launch");
+    *h_info = i;
+    return ENC_OK;
+  }
+  const uint64_t need_ws = enc_compress_workspace_bytes(n, block_size);
+  if (!d_ws || ws_bytes < need_ws)
+    return fail(ENC_ERR_CAPACITY, "workspace of %llu bytes needed", (unsigned long long)need_ws);
+
+  const Layout L = layout_of(n, block_size);
+  EncodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.in = d_in;
+  a.out = static_cast<uint8_t *>(d_out);
+  a.ws_meta = static_cast<uint8_t *>(d_ws);
+  a.ws_segsum = reinterpret_cast<uint64_t *>(a.ws_meta + align_up(2 * L.nb, kSectionAlign));
+  a.ws_total = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(a.ws_segsum) +
+                                            align_up(8 * L.nseg, kSectionAlign));
+  a.n = n;
+  a.nb = L.nb;
+  a.nseg = L.nseg;
+  a.meta_off = L.meta_off;
+  a.segoff_off = L.segoff_off;
+  a.payload_off = L.payload_off;
+  a.log2b = (uint32_t)lb;
+
+  hipError_t e = launch_encode_params(a, s);
+  if (e != hipSuccess) return hip_fail(e, "width kernel launch");
+  e = launch_encode_scan(a, s);
+  if (e != hipSuccess) return hip_fail(e, "scan kernel launch");
+  uint64_t payload = 0;
+  e = hipMemcpyAsync(&payload, a.ws_total, sizeof payload, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "size read-back");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+
+  const uint64_t coded_total = L.payload_off + payload;
+  enc_info i;
+  if (coded_total >= raw_total) {
+    if (out_capacity < raw_total)
+      return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
+                  (unsigned long long)out_capacity, (unsigned long long)raw_total);
+    i = raw_info(n, block_size);
+    e = launch_encode_raw(d_in, a.out, n, header_of(i), s);
+    if (e != hipSuccess) return hip_fail(e, "raw copy launch");
+  } else {
+    if (out_capacity < coded_total)
+      return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
+                  (unsigned long long)out_capacity, (unsigned long long)coded_total);
+    memset(&i, 0, sizeof i);
+    i.version = 1;
+    i.dtype = 1;
+    i.flags = 0;
+    i.block_size = block_size;
+    i.n_elems = n;
+    i.n_blocks = L.nb;
+    i.n_segments = L.nseg;
+    i.sm_off = L.sm_off;
+    i.meta_off = L.meta_off;
+    i.segoff_off = L.segoff_off;
+    i.payload_off = L.payload_off;
+    i.payload_bytes = payload;
+    i.raw_off = 0;
+    i.total_bytes = coded_total;
+    e = launch_encode_pack(a, s);
+    if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
+    e = launch_encode_finish(a, header_of(i), s);
+    if (e != hipSuccess) return hip_fail(e, "finish kernel launch");
+  }
+  *h_info = i;
+  return ENC_OK;
+}
+
+enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_t comp_bytes,
+                            enc_info *h_info) {
+  clear_err();
+  if (!h_header || !h_info) return fail(ENC_ERR_INVALID_ARG, "NULL argument");
+  if (header_bytes < kHeaderBytes) return fail(ENC_ERR_INVALID_ARG, "header needs 256 bytes");
+  const uint8_t *h = static_cast<const uint8_t *>(h_header);
+  if (memcmp(h, "ENCB", 4) != 0) return fail(ENC_ERR_BAD_STREAM, "bad magic");
+  if (get_le(h + 16, 4) != kSegBlocks || get_le(h + 20, 4) != 0)
+    return fail(ENC_ERR_BAD_STREAM, "segment size field is not 64");
+  for (uint32_t k = 104; k < kHeaderBytes; ++k)
+    if (h[k]) return fail(ENC_ERR_BAD_STREAM, "reserved header byte %u is not zero", k);
+  enc_info i;
+  i.version = (uint32_t)get_le(h + 4, 2);
+  i.dtype = (uint32_t)get_le(h + 6, 2);
+  i.flags = (uint32_t)get_le(h + 8, 4);
+  i.block_size = (uint32_t)get_le(h + 12, 4);
+  uint64_t *f[] = {&i.n_elems,  &i.n_blocks,    &i.n_segments,    &i.sm_off,  &i.meta_off,
+                   &i.segoff_off, &i.payload_off, &i.payload_bytes, &i.raw_off, &i.total_bytes};
+  for (int k = 0; k < 10; ++k) *f[k] = get_le(h + 24 + 8 * k, 8);
+  if (i.flags == 1 && log2_block(i.block_size) < 0 && (i.block_size < 8 || i.block_size > 4096 ||
+                                                       i.block_size % 8))
+    return fail(ENC_ERR_BAD_STREAM, "block size %u", i.block_size);
+  const enc_status st = check_info(&i);
+  if (st != ENC_OK) return st;
+  if (i.total_bytes > comp_bytes)
+    return fail(ENC_ERR_BAD_STREAM, "stream claims %llu bytes, buffer holds %llu",
+                (unsigned long long)i.total_bytes, (unsigned long long)comp_bytes);
+  *h_info = i;
+  return ENC_OK;
+}
+
+enc_status enc_read_info(const void *d_comp, uint64_t comp_bytes, void *stream, enc_info *h_info) {
+  clear_err();
+  if (!d_comp || !h_info) return fail(ENC_ERR_INVALID_ARG, "NULL argument");
+  if (comp_bytes < kHeaderBytes) return fail(ENC_ERR_BAD_STREAM, "stream shorter than its header");
+  uint8_t h[kHeaderBytes];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h, d_comp, kHeaderBytes, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "header read-back");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  return enc_parse_header(h, kHeaderBytes, comp_bytes, h_info);
+}
+
+enc_status enc_decompress(const void *d_comp, const enc_info *h_info, uint16_t *d_out,
+                          uint64_t out_elems, void *stream) {
+  clear_err();
+  const enc_status st = check_info(h_info);
+  if (st != ENC_OK) return st;
+  if (!d_comp) return fail(ENC_ERR_INVALID_ARG, "d_comp is NULL");
+  if (out_elems != h_info->n_elems)
+    return fail(ENC_ERR_SHAPE, "out_elems %llu != stream elements %llu",
+                (unsigned long long)out_elems, (unsigned long long)h_info->n_elems);
+  if (out_elems > 0 && !d_out) return fail(ENC_ERR_INVALID_ARG, "d_out is NULL");
+  if (!aligned16(d_comp) || !aligned16(d_out))
+    return fail(ENC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (out_elems == 0) return ENC_OK;
+  const hipError_t e = launch_decode(desc_of(d_comp, *h_info, d_out), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ENC_OK;
+}
+
+uint64_t enc_batch_table_bytes(int count) { return count < 0 ? 0 : batch_bytes(count); }
+
+enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, uint64_t table_bytes,
+                             void *stream) {
+  clear_err();
+  if (count < 0) return fail(ENC_ERR_INVALID_ARG, "negative count");
+  if (count > 0 && !h_items) return fail(ENC_ERR_INVALID_ARG, "h_items is NULL");
+  if (!d_table || !aligned16(d_table)) return fail(ENC_ERR_INVALID_ARG, "d_table NULL or unaligned");
+  const uint64_t need = batch_bytes(count);
+  if (table_bytes < need)
+    return fail(ENC_ERR_CAPACITY, "table needs %llu bytes", (unsigned long long)need);
+  std::vector<uint8_t> host(need, 0);
+  BatchHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.count = (uint32_t)count;
+  hdr.magic = kBatchMagic;
+  DecodeDesc *descs = reinterpret_cast<DecodeDesc *>(host.data() + sizeof(BatchHeader));
+  uint64_t *tiles = reinterpret_cast<uint64_t *>(host.data() + sizeof(BatchHeader) +
+                                                 (uint64_t)count * sizeof(DecodeDesc));
+  uint64_t t = 0;
+  for (int k = 0; k < count; ++k) {
+    const enc_item &it = h_items[k];
+    const enc_status st = check_info(&it.info);
+    if (st != ENC_OK) {
+      char why[sizeof g_err];
+      memcpy(why, g_err, sizeof why);
+      return fail(st, "item %d: %s", k, why);
+    }
+    if (!it.d_comp || (it.info.n_elems && !it.d_out))
+      return fail(ENC_ERR_INVALID_ARG, "item %d: NULL pointer", k);
+    if (!aligned16(it.d_comp) || !aligned16(it.d_out))
+      return fail(ENC_ERR_INVALID_ARG, "item %d: unaligned pointer", k);
+    descs[k] = desc_of(it.d_comp, it.info, it.d_out);
+    tiles[k] = t;
+    t += tiles_for(it.info.n_elems);
+  }
+  tiles[count] = t;
+  hdr.total_tiles = t;
+  memcpy(host.data(), &hdr, sizeof hdr);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(d_table, host.data(), need, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "table upload");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  return ENC_OK;
+}
+
+enc_status enc_decompress_batch(const void *d_table, int count, void *stream) {
+  clear_err();
+  if (count < 0) return fail(ENC_ERR_INVALID_ARG, "negative count");
+  if (!d_table || !aligned16(d_table)) return fail(ENC_ERR_INVALID_ARG, "d_table NULL or unaligned");
+  if (count == 0) return ENC_OK;
+  const hipError_t e = launch_decode_batch(d_table, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "batch decode launch");
+  return ENC_OK;
+}
+
+uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size) {
+  if (log2_block(block_size) < 0 || M == 0 || K == 0 || N == 0) return 0;
+  return gemm_workspace_bytes(M, K, N);
+}
+
+static enc_status gemm_common(const uint16_t *d_x, uint32_t M, uint32_t K, uint32_t N, float *d_y,
+                              void *d_ws, uint64_t ws_bytes, GemmArgs *a) {
+  if (!d_x || !d_y || !d_ws) return fail(ENC_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(d_x) || !aligned16(d_y) || !aligned16(d_ws))
+    return fail(ENC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (M == 0 || M > 4096 || K == 0 || N == 0)
+    return fail(ENC_ERR_SHAPE, "M=%u K=%u N=%u out of range", M, K, N);
+  if (N % 512) return fail(ENC_ERR_UNSUPPORTED, "N=%u must be a multiple of 512", N);
+  if (K % 8) return fail(ENC_ERR_UNSUPPORTED, "K=%u must be a multiple of 8", K);
+  const uint64_t need = gemm_workspace_bytes(M, K, N);
+  if (ws_bytes < need)
+    return fail(ENC_ERR_CAPACITY, "GEMM workspace of %llu bytes needed", (unsigned long long)need);
+  memset(a, 0, sizeof *a);
+  a->x = d_x;
+  a->y = d_y;
+  a->M = M;
+  a->K = K;
+  a->N = N;
+  gemm_plan(M, K, N, &a->ksplit, &a->krows);
+  a->counters = static_cast<uint32_t *>(d_ws);
+  a->partial = reinterpret_cast<float *>(static_cast<uint8_t *>(d_ws) + kSectionAlign * 64);
+  return ENC_OK;
+}
+
+enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
+                               const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
+                               uint64_t ws_bytes, void *stream) {
+  clear_err();
+  enc_status st = check_info(h_winfo);
+  if (st != ENC_OK) return st;
+  if (!d_wcomp || !aligned16(d_wcomp)) return fail(ENC_ERR_INVALID_ARG, "d_wcomp NULL or unaligned");
+  if ((uint64_t)K * N != h_winfo->n_elems)
+    return fail(ENC_ERR_SHAPE, "K*N=%llu but the stream holds %llu elements",
+                (unsigned long long)K * N, (unsigned long long)h_winfo->n_elems);
+  if (h_winfo->flags == 0 && N % h_winfo->block_size)
+    return fail(ENC_ERR_UNSUPPORTED, "N=%u not a multiple of the block size %u", N,
+                h_winfo->block_size);
+  GemmArgs a;
+  st = gemm_common(d_x, M, K, N, d_y, d_ws, ws_bytes, &a);
+  if (st != ENC_OK) return st;
+  const uint8_t *w = static_cast<const uint8_t *>(d_wcomp);
+  if (h_winfo->flags == 1) {
+    a.wdense = reinterpret_cast<const uint16_t *>(w + kHeaderBytes);
+  } else {
+    a.wstream = w;
+    a.log2b = (uint32_t)log2_block(h_winfo->block_size);
+    a.nb = h_winfo->n_blocks;
+    a.meta_off = h_winfo->meta_off;
+    a.segoff_off = h_winfo->segoff_off;
+    a.payload_off = h_winfo->payload_off;
+  }
+  const hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+  return ENC_OK;
+}
+
+enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
+                          uint32_t N, float *d_y, void *d_ws, uint64_t ws_bytes, void *stream) {
+  clear_err();
+  if (!d_w || !aligned16(d_w)) return fail(ENC_ERR_INVALID_ARG, "d_w NULL or unaligned");
+  GemmArgs a;
+  const enc_status st = gemm_common(d_x, M, K, N, d_y, d_ws, ws_bytes, &a);
+  if (st != ENC_OK) return st;
+  a.wdense = d_w;
+  const hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+  return ENC_OK;
+}
+
+const char *enc_status_string(enc_status s) {
+  switch (s) {
+    case ENC_OK: return "ok";
+    case ENC_ERR_INVALID_ARG: return "invalid argument";
+    case ENC_ERR_UNSUPPORTED: return "unsupported";
+    case ENC_ERR_CAPACITY: return "buffer too small";
+    case ENC_ERR_BAD_STREAM: return "bad stream";
+    case ENC_ERR_SHAPE: return "shape mismatch";
+    case ENC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *enc_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// enc_common.h -- internal definitions shared by the gfx950 kernels and the
+// host side of libenc.so. Not part of the C ABI.
+//
+// Work decomposition used by every codec kernel:
+//  * group   = 8 consecutive elements, owned by one lane. 8 codes of w bits
+//              fill exactly w bytes, so every group's codes start on a byte
+//              boundary for any width and any block size that is a multiple
+//              of 8.
+//  * block   = B elements = B/8 groups (B a power of two, 128..4096).
+//  * segment = 64 blocks, one per lane of a wave64 for the intra-segment
+//              scan of block payload sizes ("ENEC: A Lossless AI Model
+//              Compression Method Enabling Fast Inference on Ascend NPUs",
+//              Abstract: dependency-decoupled intra-segment scan).
+//  * tile    = kTileGroups consecutive groups handled by one 256-thread
+//              workgroup; a tile never straddles a segment (segments hold
+//              64*B/8 >= 1024 groups) and always holds whole blocks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace enc {
+
+constexpr uint32_t kHeaderBytes = 256;
+constexpr uint32_t kSegBlocks = 64;
+constexpr uint32_t kSectionAlign = 256;
+constexpr uint32_t kPayloadAlign = 16;
+constexpr uint32_t kThreads = 256;                                // 4 x wave64
+constexpr uint32_t kGroupsPerThread = 4;
+constexpr uint32_t kTileGroups = kThreads * kGroupsPerThread;     // 1024
+constexpr uint64_t kTileElems = uint64_t(kTileGroups) * 8;        // 8192
+constexpr uint32_t kMinLog2B = 7, kMaxLog2B = 12;
+
+__host__ __device__ inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// One stream to decode (by value for a single call, in the batch table for
+// batched calls). 80 bytes.
+struct DecodeDesc {
+  const uint8_t *stream;   // device stream base
+  uint16_t *out;           // device output
+  uint64_t n;              // elements
+  uint64_t nb;             // blocks (0 for RAW)
+  uint64_t meta_off;       // section offsets inside the stream
+  uint64_t segoff_off;
+  uint64_t payload_off;
+  uint64_t total;          // stream bytes (reads never go past it)
+  uint32_t log2b;          // log2 of the block size
+  uint32_t raw;            // 1 = RAW stream (verbatim values at offset 256)
+  uint64_t reserved;
+};
+static_assert(sizeof(DecodeDesc) == 80, "table entry layout");
+
+// Batch table in device memory: header, then `count` DecodeDesc, then
+// `count + 1` u64 tile prefixes (first tile of each item, then the total).
+struct BatchHeader {
+  uint64_t total_tiles;
+  uint32_t count;
+  uint32_t magic;
+  uint64_t reserved[6];
+};
+static_assert(sizeof(BatchHeader) == 64, "table header layout");
+constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"
+
+inline uint64_t tiles_for(uint64_t n) { return (n + kTileElems - 1) / kTileElems; }
+
+// ---- launchers (defined in the .hip files) --------------------------------
+hipError_t launch_decode(const DecodeDesc &d, hipStream_t s);
+hipError_t launch_decode_batch(const void *table, hipStream_t s);
+
+struct EncodeArgs {
+  const uint16_t *in;
+  uint8_t *out;          // stream base
+  uint8_t *ws_meta;      // 2 bytes per block
+  uint64_t *ws_segsum;   // per-segment payload bytes, scanned in place to offsets
+  uint64_t *ws_total;    // payload bytes (one u64)
+  uint64_t n, nb, nseg;
+  uint64_t meta_off, segoff_off, payload_off;
+  uint32_t log2b;
+};
+hipError_t launch_encode_params(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_encode_scan(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_encode_pack(const EncodeArgs &a, hipStream_t s);
+
+struct HeaderImage {
+  uint8_t bytes[256];
+};
+hipError_t launch_encode_finish(const EncodeArgs &a, const HeaderImage &h, hipStream_t s);
+hipError_t launch_encode_raw(const uint16_t *in, uint8_t *out, uint64_t n, const HeaderImage &h,
+                             hipStream_t s);
+
+// ---- fused decompress-GEMM ------------------------------------------------
+struct GemmArgs {
+  const uint16_t *x;       // X [M, K] bf16
+  const uint8_t *wstream;  // compressed W stream (nullptr for dense)
+  const uint16_t *wdense;  // dense W [K, N] bf16 (RAW stream data or dense GEMM)
+  float *y;                // Y [M, N] fp32
+  float *partial;          // [ksplit, M, N] split-K partial sums
+  uint32_t *counters;      // per output tile arrival counters (zero between calls)
+  uint32_t M, K, N;
+  uint32_t log2b;
+  uint64_t nb;
+  uint64_t meta_off, segoff_off, payload_off;
+  uint32_t ksplit;         // number of K ranges
+  uint32_t krows;          // rows per K range
+};
+uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N);
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows);
+
+}  // namespace enc

@@ -1,0 +1,436 @@
+// gemm.hip -- fused decompress-GEMM on gfx950:  Y[M,N] (fp32) = X[M,K] (bf16) x W[K,N]
+// with W row-major and held only in compressed form.
+//
+// "ZipServ: Fast and Memory-Efficient LLM Inference with Hardware-Aware
+// Lossless Compression", Abstract: the weights are decompressed on the fly
+// inside the GEMM kernel ("load-compressed, compute-decompressed"), so the
+// decoded W never goes back to HBM and the kernel reads only the compressed
+// bytes.
+//
+// Both paths locate the block of a row the way the decoder does: the stored
+// offset of the block's 64-block segment plus the payload sizes of the earlier
+// blocks of that segment. Every block of W is full (N % B == 0), so a block's
+// payload is w * B / 8 bytes.
+//
+//  * M < 16  (k_gemm_valu): HBM-bound streaming. A wave owns a 512-column
+//    strip (lane: 8 columns) and a run of rows; each lane decodes its group of
+//    every row in registers and does M x 8 fp32 FMAs with X[m][k] read by
+//    scalar loads (uniform across the wave). The four waves of a workgroup
+//    reduce in LDS in a fixed order.
+//  * M >= 16 (k_gemm_mfma): a 128-column x 32-row W tile is decoded into LDS
+//    as BF16 per K step (two groups per thread), the X tile is staged in LDS,
+//    and v_mfma_f32_16x16x32_bf16 accumulates in fp32; the next step's
+//    compressed bytes are loaded while the current step's MFMAs run.
+//  * split K: workgroups over K ranges write fp32 partial tiles; the last
+//    workgroup to finish a tile (atomic arrival counter) adds the partials in
+//    K order, writes Y and resets the counter -- one launch, deterministic.
+#include "enc_common.h"
+#include "group_math.h"
+
+namespace enc {
+namespace {
+
+constexpr uint32_t kStrip = 512;               // VALU path: columns per workgroup
+constexpr uint32_t kValuRowsPerWave = 32;
+constexpr uint32_t kValuRows = 4 * kValuRowsPerWave;
+constexpr uint32_t kTileN = 128;               // MFMA path: columns per workgroup
+constexpr uint32_t kKStep = 32;                // MFMA path: rows per K step
+constexpr uint32_t kWPitch = kTileN + 2;       // bf16 per LDS row of the W tile
+constexpr uint32_t kXPitch = kKStep + 8;       // bf16 per LDS row of the X tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Stream offset of the payload of block i (a full block of W):
+// payload_off + segment offset + (B/8) * sum of the widths of the earlier
+// blocks of the segment.
+__device__ __forceinline__ uint64_t block_offset(const GemmArgs &a, uint64_t i) {
+  const uint64_t seg = i >> 6;
+  const uint32_t t = (uint32_t)(i & 63);
+  const uint8_t *meta = a.wstream + a.meta_off + 2 * (seg << 6);
+  uint32_t wsum = 0;
+  uint32_t j = 0;
+  for (; j + 2 <= t; j += 2) {
+    const uint32_t d = ld32(meta + 2 * j);
+    wsum += ((d >> 8) & 0xFFu) + (d >> 24);
+  }
+  if (t & 1) wsum += meta[2 * j + 1];
+  const uint64_t so = *reinterpret_cast<const uint64_t *>(a.wstream + a.segoff_off + 8 * seg);
+  return a.payload_off + so + ((uint64_t)wsum << (a.log2b - 3));
+}
+
+// Raw material of one group of a compressed row: sign+mantissa dwords, code
+// dwords, and the packed {base, width, lead} needed to decode it.
+struct GroupRaw {
+  uint32_t sml, smh, q0, q1, q2, info;
+};
+
+// Group `lane_group` (0-based group index inside a run of columns starting at
+// element e, e a multiple of the run width and the run within one strip) of
+// the compressed row holding element e. `blk_off` is the stream offset of
+// block e >> log2b. For B < 512 a 512-column run spans 512/B blocks of one
+// segment; the lane adds the sizes of the run's earlier blocks.
+__device__ __forceinline__ GroupRaw load_group(const GemmArgs &a, uint64_t e, uint32_t g,
+                                               uint64_t blk_off) {
+  const uint8_t *__restrict__ s = a.wstream;
+  const uint32_t log2b = a.log2b;
+  const uint64_t i0 = e >> log2b;
+  uint32_t meta, extra = 0, u;
+  if (log2b >= 9 || g < (1u << (log2b - 3))) {
+    // the group lies in block i0
+    meta = *reinterpret_cast<const uint16_t *>(s + a.meta_off + 2 * i0);
+    u = (uint32_t)((e & ((1u << log2b) - 1)) >> 3) + g;
+  } else {
+    const uint32_t bl = g >> (log2b - 3);       // block of the run (1..3)
+    const uint64_t mw = (log2b == 8) ? (uint64_t)ld32(s + a.meta_off + 2 * i0)
+                                     : *reinterpret_cast<const uint64_t *>(s + a.meta_off + 2 * i0);
+    meta = (uint32_t)(mw >> (16 * bl)) & 0xFFFFu;
+    for (uint32_t j = 0; j < bl; ++j) extra += (uint32_t)((mw >> (16 * j + 8)) & 0xFFu);
+    extra <<= (log2b - 3);
+    u = g & ((1u << (log2b - 3)) - 1);
+  }
+  const uint32_t w = meta >> 8;
+  const uint64_t sm_addr = kHeaderBytes + e + 8 * (uint64_t)g;
+  const uint2 sm = *reinterpret_cast<const uint2 *>(s + sm_addr);
+  GroupRaw r;
+  r.sml = sm.x;
+  r.smh = sm.y;
+  uint32_t lead;
+  load_codes(s, blk_off + extra + (uint64_t)u * w, w, sm_addr, r.q0, r.q1, r.q2, lead);
+  r.info = (meta << 16) | (lead << 3);
+  return r;
+}
+
+__device__ __forceinline__ uint4 decode_raw(const GroupRaw &r) {
+  const uint32_t w = (r.info >> 24) & 15u;
+  const uint32_t base4 = ((r.info >> 16) & 0xFFu) * 0x01010101u;
+  uint32_t lo, hi;
+  align_codes(r.q0, r.q1, r.q2, (r.info >> 3) & 3u, lo, hi);
+  return join_group(lo, hi, w, base4, r.sml, r.smh);
+}
+
+// Split-K epilogue shared by both kernels: the workgroup's fp32 tile
+// `vals(i)` for i in [0, count) maps to Y element ymap(i). With one K range it
+// writes Y; otherwise it writes its partial slice, and the last arriving
+// workgroup of the tile sums the slices in K order into Y.
+template <class Vals, class YMap>
+__device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t tile_id, uint32_t ks,
+                                              uint32_t count, Vals vals, YMap ymap) {
+  __shared__ uint32_t s_last;
+  const uint32_t tid = threadIdx.x;
+  if (a.ksplit == 1) {
+    for (uint32_t i = tid; i < count; i += blockDim.x) {
+      const int64_t y = ymap(i);
+      if (y >= 0) a.y[y] = vals(i);
+    }
+    return;
+  }
+  const uint64_t MN = (uint64_t)a.M * a.N;
+  for (uint32_t i = tid; i < count; i += blockDim.x) {
+    const int64_t y = ymap(i);
+    if (y >= 0) a.partial[(uint64_t)ks * MN + (uint64_t)y] = vals(i);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&a.counters[tile_id], 1u) == a.ksplit - 1) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (uint32_t i = tid; i < count; i += blockDim.x) {
+    const int64_t y = ymap(i);
+    if (y < 0) continue;
+    float sum = 0.f;
+    for (uint32_t k = 0; k < a.ksplit; ++k) sum += __builtin_nontemporal_load(a.partial + (uint64_t)k * MN + (uint64_t)y);
+    a.y[y] = sum;
+  }
+  if (tid == 0) atomicExch(&a.counters[tile_id], 0u);
+}
+
+// --------------------------------------------------------------------------
+// M < 16: VALU FMA path.
+// --------------------------------------------------------------------------
+template <int MM, bool DENSE>
+__global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
+  __shared__ float red[MM * kStrip];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t c = blockIdx.x, ks = blockIdx.y;
+  const uint32_t N = a.N, K = a.K;
+  const uint32_t rows_w = a.krows / 4;
+  const uint32_t kw0 = ks * a.krows + wave * rows_w;
+  const uint32_t kw1 = min(kw0 + rows_w, K);
+  float acc[MM][8];
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[m][q] = 0.f;
+
+  for (uint32_t kb = kw0; kb < kw1; kb += 64) {
+    const uint32_t kbe = min(kb + 64, kw1);
+    uint64_t my_off = 0;   // stream offset of block holding row (kb+lane)'s strip start
+    if (!DENSE && kb + lane < kbe)
+      my_off = block_offset(a, ((uint64_t)(kb + lane) * N + (uint64_t)c * kStrip) >> a.log2b);
+    for (uint32_t k = kb; k < kbe; k += 4) {
+      GroupRaw raw[4];
+      uint4 dv[4];
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t kr = k + j;
+        if (kr < kbe) {
+          const uint64_t e = (uint64_t)kr * N + (uint64_t)c * kStrip;
+          if (DENSE) {
+            dv[j] = *reinterpret_cast<const uint4 *>(a.wdense + e + 8 * lane);
+          } else {
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)my_off, kr - kb);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(my_off >> 32), kr - kb);
+            raw[j] = load_group(a, e, lane, ((uint64_t)hi << 32) | lo);
+          }
+        }
+      }
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t kr = k + j;
+        if (kr >= kbe) break;
+        const uint4 v = DENSE ? dv[j] : decode_raw(raw[j]);
+        const float f[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                            bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          const float xm = bf_lo(a.x[(uint64_t)m * K + kr]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[m][q] = fmaf(xm, f[q], acc[m][q]);
+        }
+      }
+    }
+  }
+  // deterministic reduction of the four waves' rows: wave 0, then 1, 2, 3
+  for (uint32_t w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t idx = m * kStrip + 8 * lane + q;
+          red[idx] = (w == 0 ? 0.f : red[idx]) + acc[m][q];
+        }
+    }
+    __syncthreads();
+  }
+  splitk_finish(
+      a, c, ks, MM * kStrip, [&](uint32_t i) { return red[i]; },
+      [&](uint32_t i) -> int64_t {
+        return (int64_t)(i / kStrip) * N + (int64_t)c * kStrip + (i % kStrip);
+      });
+}
+
+// --------------------------------------------------------------------------
+// M >= 16: MFMA path.
+// --------------------------------------------------------------------------
+template <int MT, bool DENSE>
+__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
+  constexpr int MSUB = MT / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kKStep * kWPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[MT * kXPitch];
+  __shared__ uint32_t row_off_lo[1024], row_off_hi[1024];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t nt = blockIdx.x, ks = blockIdx.y, mt = blockIdx.z;
+  const uint32_t N = a.N, K = a.K, M = a.M;
+  const uint32_t n0 = nt * kTileN, m0 = mt * MT;
+  const uint32_t k0 = ks * a.krows;
+  const uint32_t k1 = min(k0 + a.krows, K);
+  const uint32_t nsteps = (k1 - k0 + kKStep - 1) / kKStep;
+
+  if (!DENSE) {
+    for (uint32_t r = tid; r < k1 - k0; r += 256) {
+      const uint64_t off = block_offset(a, ((uint64_t)(k0 + r) * N + n0) >> a.log2b);
+      row_off_lo[r] = (uint32_t)off;
+      row_off_hi[r] = (uint32_t)(off >> 32);
+    }
+    __syncthreads();
+  }
+
+  // each thread: two W groups per step (rows tr and tr + 16, 8 columns at tg)
+  const uint32_t tr = tid >> 4, tg = tid & 15;
+  // X tile: MT x 32 bf16 = MT*4 16-byte pieces
+  constexpr uint32_t XPIECES = MT * 4;
+
+  GroupRaw raw[2];
+  uint4 dv[2];
+  uint4 xv[(XPIECES + 255) / 256];
+
+  auto load_step = [&](uint32_t step) {
+    const uint32_t kb = k0 + step * kKStep;
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+      const uint32_t kr = kb + tr + 16 * h;
+      if (kr < k1) {
+        const uint64_t e = (uint64_t)kr * N + n0;
+        if (DENSE) {
+          dv[h] = *reinterpret_cast<const uint4 *>(a.wdense + e + 8 * tg);
+        } else {
+          const uint32_t r = kr - k0;
+          const uint64_t off = ((uint64_t)row_off_hi[r] << 32) | row_off_lo[r];
+          raw[h] = load_group(a, e, tg, off);
+        }
+      }
+    }
+#pragma unroll
+    for (uint32_t p = 0; p < (XPIECES + 255) / 256; ++p) {
+      const uint32_t piece = tid + 256 * p;
+      const uint32_t m = piece >> 2, q = piece & 3;
+      const uint32_t kx = kb + 8 * q;
+      xv[p] = make_uint4(0, 0, 0, 0);
+      if (piece < XPIECES && m0 + m < M && kx < k1)
+        xv[p] = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)(m0 + m) * K + kx);
+    }
+  };
+
+  f32x4 acc[MSUB][2];
+#pragma unroll
+  for (int t = 0; t < MSUB; ++t)
+    for (int s = 0; s < 2; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nsteps) load_step(0);
+  for (uint32_t step = 0; step < nsteps; ++step) {
+    const uint32_t kb = k0 + step * kKStep;
+    // decoded W groups -> LDS (row-major, rows past K are zero)
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+      const uint32_t r = tr + 16 * h;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kb + r < k1) v = DENSE ? dv[h] : decode_raw(raw[h]);
+      uint32_t *dst = reinterpret_cast<uint32_t *>(wt + r * kWPitch + 8 * tg);
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
+    }
+#pragma unroll
+    for (uint32_t p = 0; p < (XPIECES + 255) / 256; ++p) {
+      const uint32_t piece = tid + 256 * p;
+      if (piece < XPIECES)
+        *reinterpret_cast<uint4 *>(xt + (piece >> 2) * kXPitch + 8 * (piece & 3)) = xv[p];
+    }
+    __syncthreads();
+    if (step + 1 < nsteps) load_step(step + 1);
+    // MFMA: wave owns columns [32 wave, 32 wave + 32) of the tile
+    const uint32_t kq = 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t n = 32 * wave + 16 * s + (lane & 15);
+      bf16x8 b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(__bf16, wt[(kq + j) * kWPitch + n]);
+#pragma unroll
+      for (int t = 0; t < MSUB; ++t) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(xt + (16 * t + (lane & 15)) * kXPitch + kq);
+        acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc[t][s], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // results: lane holds D[4 (lane >> 4) + j][lane & 15] of each 16x16 subtile;
+  // stage through LDS (reuse the X tile area is too small: use a flat float view
+  // of registers instead) -> write directly with the split-K epilogue.
+  const uint32_t tile_id = mt * (N / kTileN) + nt;
+  splitk_finish(
+      a, tile_id, ks, MT * kTileN,
+      [&](uint32_t i) -> float {
+        // i enumerates this thread's own values only (see ymap)
+        const uint32_t idx = i / 256;            // 0 .. MSUB*2*4-1
+        const uint32_t t = idx / 8, s = (idx / 4) & 1, j = idx & 3;
+        float v = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < MSUB; ++tt)
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if ((uint32_t)tt == t && (uint32_t)ss == s && (uint32_t)jj == j) v = acc[tt][ss][jj];
+        return v;
+      },
+      [&](uint32_t i) -> int64_t {
+        const uint32_t idx = i / 256;
+        const uint32_t t = idx / 8, s = (idx / 4) & 1, j = idx & 3;
+        const uint32_t m = m0 + 16 * t + 4 * (lane >> 4) + j;
+        const uint32_t n = n0 + 32 * wave + 16 * s + (lane & 15);
+        if (m >= M) return -1;
+        return (int64_t)m * N + n;
+      });
+}
+
+template <bool DENSE>
+hipError_t launch_valu(const GemmArgs &a, hipStream_t s) {
+  const dim3 grid(a.N / kStrip, a.ksplit);
+  switch (a.M) {
+#define CASE(m) \
+  case m: hipLaunchKernelGGL((k_gemm_valu<m, DENSE>), grid, dim3(256), 0, s, a); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+uint32_t mfma_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
+
+template <bool DENSE>
+hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
+  const uint32_t MT = mfma_tile_m(a.M);
+  const dim3 grid(a.N / kTileN, a.ksplit, (a.M + MT - 1) / MT);
+  switch (MT) {
+    case 16: hipLaunchKernelGGL((k_gemm_mfma<16, DENSE>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_mfma<32, DENSE>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_gemm_mfma<64, DENSE>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfma<128, DENSE>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows) {
+  if (M < 16) {
+    const uint32_t rows = kValuRows;
+    *ksplit = (K + rows - 1) / rows;
+    *krows = rows;
+    return;
+  }
+  const uint32_t MT = mfma_tile_m(M);
+  const uint64_t tiles = (uint64_t)(N / kTileN) * ((M + MT - 1) / MT);
+  const uint64_t target = M <= 32 ? 512 : 256;
+  uint32_t ks = (uint32_t)((target + tiles - 1) / tiles);
+  const uint32_t max_ks = (K + 1023) / 1024 > (K + 63) / 64 ? (K + 1023) / 1024 : (K + 63) / 64;
+  if (ks < (K + 1023) / 1024) ks = (K + 1023) / 1024;   // at most 1024 rows per range (LDS table)
+  if (ks > max_ks) ks = max_ks;
+  if (ks < 1) ks = 1;
+  uint32_t rows = (K + ks - 1) / ks;
+  rows = (rows + kKStep - 1) / kKStep * kKStep;
+  *krows = rows;
+  *ksplit = (K + rows - 1) / rows;
+}
+
+uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
+  uint32_t ks, kr;
+  gemm_plan(M, K, N, &ks, &kr);
+  const uint64_t tiles = M < 16 ? N / kStrip : (uint64_t)(N / kTileN) * ((M + 127) / 16 + 1);
+  const uint64_t counters = align_up(4 * tiles, 256);
+  const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
+  return counters + partial;
+}
+
+hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
+  GemmArgs a = a_in;
+  const uint32_t tiles = a.M < 16 ? a.N / kStrip : (a.N / kTileN) * ((a.M + 127) / 16 + 1);
+  a.partial = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(a.counters) +
+                                        align_up(4ull * tiles, 256));
+  const bool dense = a.wstream == nullptr;
+  if (a.M < 16) return dense ? launch_valu<true>(a, s) : launch_valu<false>(a, s);
+  return dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
+}
+
+}  // namespace enc

@@ -1,0 +1,247 @@
+"""ctypes binding of libenc.so (C ABI in include/enc.h), same entry-point names.
+
+Argument marshalling only: every step of compression, decompression and the
+fused GEMM runs in the library's gfx950 kernels. torch is used for device
+memory (``torch.empty`` on ``cuda``) and for the current HIP stream. If the
+library has not been built, the first call raises -- there is no fallback.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libenc.so")
+
+ENC_OK = 0
+STATUS_NAMES = {0: "ENC_OK", -1: "ENC_ERR_INVALID_ARG", -2: "ENC_ERR_UNSUPPORTED",
+                -3: "ENC_ERR_CAPACITY", -4: "ENC_ERR_BAD_STREAM", -5: "ENC_ERR_SHAPE",
+                -6: "ENC_ERR_HIP"}
+
+
+class EncError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (%d): %s" % (STATUS_NAMES.get(status, "?"), status, message))
+        self.status = status
+
+
+class EncInfo(ctypes.Structure):
+    _fields_ = [("version", ctypes.c_uint32), ("dtype", ctypes.c_uint32),
+                ("flags", ctypes.c_uint32), ("block_size", ctypes.c_uint32),
+                ("n_elems", ctypes.c_uint64), ("n_blocks", ctypes.c_uint64),
+                ("n_segments", ctypes.c_uint64), ("sm_off", ctypes.c_uint64),
+                ("meta_off", ctypes.c_uint64), ("segoff_off", ctypes.c_uint64),
+                ("payload_off", ctypes.c_uint64), ("payload_bytes", ctypes.c_uint64),
+                ("raw_off", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+    def __repr__(self):
+        return "EncInfo(%s)" % ", ".join("%s=%s" % kv for kv in self.as_dict().items())
+
+
+class EncItem(ctypes.Structure):
+    _fields_ = [("d_comp", ctypes.c_void_p), ("d_out", ctypes.c_void_p), ("info", EncInfo)]
+
+
+_VP = ctypes.c_void_p
+_U32 = ctypes.c_uint32
+_U64 = ctypes.c_uint64
+_ST = ctypes.c_int
+_INFO_P = ctypes.POINTER(EncInfo)
+
+# name -> (restype, argtypes); exactly the functions include/enc.h declares
+SIGNATURES = {
+    "enc_compress_bound": (_U64, [_U64]),
+    "enc_compress_workspace_bytes": (_U64, [_U64, _U32]),
+    "enc_compress": (_ST, [_VP, _U64, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
+    "enc_parse_header": (_ST, [_VP, _U64, _U64, _INFO_P]),
+    "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
+    "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
+    "enc_batch_table_bytes": (_U64, [ctypes.c_int]),
+    "enc_batch_prepare": (_ST, [ctypes.POINTER(EncItem), ctypes.c_int, _VP, _U64, _VP]),
+    "enc_decompress_batch": (_ST, [_VP, ctypes.c_int, _VP]),
+    "enc_gemm_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
+    "enc_decompress_gemm": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP, _U64, _VP]),
+    "enc_gemm_dense": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
+    "enc_status_string": (ctypes.c_char_p, [_ST]),
+    "enc_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libenc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libenc.so is not built (%s); run "
+                               "`python -m lossless_weight_compression_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != ENC_OK:
+        raise EncError(status, lib().enc_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _bits(x):
+    """A 16-bit CUDA tensor's storage viewed as int16 (BF16 bit patterns)."""
+    import torch
+    if x.element_size() != 2:
+        raise TypeError("expected a 16-bit tensor of BF16 values or bit patterns")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("expected a contiguous CUDA tensor")
+    return x.view(torch.int16)
+
+
+def _empty_u8(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------- entry points
+def enc_compress_bound(n_elems):
+    return int(lib().enc_compress_bound(n_elems))
+
+
+def enc_compress_workspace_bytes(n_elems, block_size):
+    return int(lib().enc_compress_workspace_bytes(n_elems, block_size))
+
+
+def enc_compress(x, block_size=512, out=None, ws=None, stream=None):
+    """Compress the BF16 tensor x. Returns (stream bytes as a uint8 CUDA tensor
+    sliced to the stream size, EncInfo)."""
+    x = _bits(x)
+    n = x.numel()
+    if out is None:
+        out = _empty_u8(enc_compress_bound(n), x.device)
+    if ws is None:
+        ws = _empty_u8(enc_compress_workspace_bytes(n, block_size), x.device)
+    info = EncInfo()
+    _check(lib().enc_compress(_ptr(x), n, block_size, _ptr(out), out.numel(), _ptr(ws), ws.numel(),
+                              _stream(stream), ctypes.byref(info)))
+    return out[:info.total_bytes], info
+
+
+def enc_parse_header(header, comp_bytes=None):
+    """Parse a stream header held in host memory (bytes-like or numpy array)."""
+    buf = bytes(memoryview(header).cast("B"))
+    if comp_bytes is None:
+        comp_bytes = len(buf)
+    info = EncInfo()
+    cbuf = ctypes.create_string_buffer(buf, len(buf))
+    _check(lib().enc_parse_header(cbuf, len(buf), comp_bytes, ctypes.byref(info)))
+    return info
+
+
+def enc_read_info(comp, stream=None):
+    info = EncInfo()
+    _check(lib().enc_read_info(_ptr(comp), comp.numel() * comp.element_size(), _stream(stream),
+                               ctypes.byref(info)))
+    return info
+
+
+def enc_decompress(comp, info, out=None, stream=None):
+    """Decode a stream into an int16 CUDA tensor of info.n_elems BF16 bit patterns."""
+    import torch
+    if out is None:
+        out = torch.empty(max(info.n_elems, 1), dtype=torch.int16, device=comp.device)[:info.n_elems]
+    _check(lib().enc_decompress(_ptr(comp), ctypes.byref(info), _ptr(out), out.numel(),
+                                _stream(stream)))
+    return out
+
+
+def enc_batch_table_bytes(count):
+    return int(lib().enc_batch_table_bytes(count))
+
+
+def enc_batch_prepare(items, table=None, stream=None):
+    """items: sequence of (comp tensor, EncInfo, out tensor). Returns the device table."""
+    count = len(items)
+    arr = (EncItem * max(count, 1))()
+    device = None
+    for k, (comp, info, out) in enumerate(items):
+        arr[k].d_comp = comp.data_ptr()
+        arr[k].d_out = out.data_ptr()
+        arr[k].info = info
+        device = comp.device
+    if table is None:
+        import torch
+        table = _empty_u8(enc_batch_table_bytes(count), device or torch.device("cuda"))
+    _check(lib().enc_batch_prepare(arr, count, _ptr(table), table.numel(), _stream(stream)))
+    return table
+
+
+def enc_decompress_batch(table, count, stream=None):
+    _check(lib().enc_decompress_batch(_ptr(table), count, _stream(stream)))
+
+
+def enc_gemm_workspace_bytes(M, K, N, block_size=512):
+    return int(lib().enc_gemm_workspace_bytes(M, K, N, block_size))
+
+
+def gemm_workspace(M, K, N, block_size=512, device="cuda"):
+    """A zero-filled workspace for the GEMM entry points (zero on first use)."""
+    import torch
+    return torch.zeros(max(enc_gemm_workspace_bytes(M, K, N, block_size), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def enc_decompress_gemm(x, comp, info, N, y=None, ws=None, stream=None):
+    """Y[M,N] fp32 = X[M,K] bf16 @ W[K,N], W given compressed."""
+    import torch
+    x = _bits(x)
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = gemm_workspace(M, K, N, info.block_size, x.device)
+    _check(lib().enc_decompress_gemm(_ptr(x), M, K, _ptr(comp), ctypes.byref(info), N, _ptr(y),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def enc_gemm_dense(x, w, y=None, ws=None, stream=None):
+    """Y[M,N] fp32 = X[M,K] bf16 @ W[K,N] bf16 (uncompressed baseline)."""
+    import torch
+    x = _bits(x)
+    w = _bits(w)
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = gemm_workspace(M, K, N, 512, x.device)
+    _check(lib().enc_gemm_dense(_ptr(x), M, K, _ptr(w), N, _ptr(y), _ptr(ws), ws.numel(),
+                                _stream(stream)))
+    return y
+
+
+def enc_status_string(status):
+    return lib().enc_status_string(status).decode()
+
+
+def enc_last_error():
+    return lib().enc_last_error().decode()

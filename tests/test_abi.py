@@ -1,0 +1,131 @@
+"""The C-ABI library without a GPU: it loads, exports exactly what
+include/enc.h declares, and its host-side checks reject bad arguments and bad
+stream headers before any HIP call. Stream headers written by the CPU oracle
+parse to the fields the format defines."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from lossless_weight_compression_amd import enc, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "enc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(enc_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(enc.LIB_PATH):
+        from lossless_weight_compression_amd import build
+        build.build(verbose=False)
+    return enc.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(enc.SIGNATURES) == declared
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(enc.EncInfo) == 96
+    assert ctypes.sizeof(enc.EncItem) == 112
+
+
+def test_sizes(L):
+    assert enc.enc_compress_bound(0) == 256
+    assert enc.enc_compress_bound(1000) == 2256
+    # meta A(2*nb) + seg A(8*nseg) + one 256-byte slot
+    assert enc.enc_compress_workspace_bytes(1 << 20, 512) == 4096 + 256 + 256
+    assert enc.enc_compress_workspace_bytes(1 << 20, 24) == 0
+    assert enc.enc_batch_table_bytes(0) % 256 == 0
+    assert enc.enc_batch_table_bytes(226) >= 64 + 226 * 80 + 227 * 8
+    assert enc.enc_status_string(-4) == "bad stream"
+
+
+@pytest.mark.parametrize("B", [128, 512, 4096])
+def test_parse_oracle_headers(L, orc, B):
+    x = synth.gaussian_bits((100, 1000), 0.02, 80, B)
+    s = orc.encode(x, B)
+    info = enc.enc_parse_header(s[:256], s.size)
+    n = x.size
+    nb = -(-n // B)
+    assert (info.version, info.dtype, info.flags, info.block_size) == (1, 1, 0, B)
+    assert (info.n_elems, info.n_blocks, info.n_segments) == (n, nb, -(-nb // 64))
+    assert info.total_bytes == s.size
+    assert info.payload_off + info.payload_bytes == s.size
+    raw = orc.encode(synth.random_bits(5000, 3), B)
+    ri = enc.enc_parse_header(raw[:256], raw.size)
+    assert (ri.flags, ri.raw_off, ri.total_bytes) == (1, 256, 256 + 10000)
+
+
+def test_parse_rejects_bad_headers(L, orc):
+    s = orc.encode(synth.tiny()[:128], 512)
+    h = np.array(s[:256])
+    enc.enc_parse_header(h, s.size)
+    cases = []
+    b = h.copy(); b[0] = 0; cases.append((b, s.size, -4))
+    b = h.copy(); b[4] = 2; cases.append((b, s.size, -4))
+    b = h.copy(); b[16] = 32; cases.append((b, s.size, -4))
+    b = h.copy(); b[150] = 1; cases.append((b, s.size, -4))
+    b = h.copy(); b[12:16] = np.frombuffer(np.uint32(768).tobytes(), np.uint8); cases.append((b, s.size, -2))
+    b = h.copy(); b[56] += 16; cases.append((b, s.size, -4))   # meta offset moved
+    cases.append((h, s.size - 16, -4))                          # truncated buffer
+    for hdr, size, status in cases:
+        with pytest.raises(enc.EncError) as e:
+            enc.enc_parse_header(hdr, size)
+        assert e.value.status == status
+    with pytest.raises(enc.EncError):
+        enc.enc_parse_header(h[:100], s.size)
+
+
+def test_odd_block_size_streams_are_unsupported_not_crashes(L, orc):
+    # the oracle accepts any multiple of 8; the library only powers of two
+    x = np.full(64 * 24 * 3, 0x3F80, np.uint16)
+    s = orc.encode(x, 24)
+    with pytest.raises(enc.EncError) as e:
+        enc.enc_parse_header(s[:256], s.size)
+    assert e.value.status == -2
+
+
+def test_host_validation_before_any_launch(L):
+    info = enc.EncInfo()
+    vp = ctypes.c_void_p
+    # decompress: inconsistent info is rejected on the host
+    st = L.enc_decompress(vp(16), ctypes.byref(info), vp(16), 0, vp(0))
+    assert st == -4
+    info.version, info.dtype, info.flags = 1, 1, 1
+    info.n_elems, info.raw_off, info.total_bytes = 10, 256, 276
+    st = L.enc_decompress(vp(16), ctypes.byref(info), vp(16), 11, vp(0))
+    assert st == -5                                          # element count mismatch
+    st = L.enc_decompress(vp(17), ctypes.byref(info), vp(16), 10, vp(0))
+    assert st == -1                                          # unaligned
+    # compress: bad block size / missing workspace, before any launch
+    out = enc.EncInfo()
+    assert L.enc_compress(vp(16), 100, 300, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -2
+    assert L.enc_compress(vp(16), 100000, 512, vp(16), 300000, vp(0), 0, vp(0), ctypes.byref(out)) == -3
+    assert L.enc_compress(vp(0), 100, 512, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -1
+    assert "NULL" in enc.enc_last_error()
+    # GEMM: shape checks
+    winfo = enc.EncInfo()
+    winfo.version, winfo.dtype, winfo.flags = 1, 1, 1
+    winfo.n_elems, winfo.raw_off, winfo.total_bytes = 4096 * 1024, 256, 256 + 2 * 4096 * 1024
+    assert L.enc_decompress_gemm(vp(16), 1, 4096, vp(16), ctypes.byref(winfo), 1000, vp(16), vp(16),
+                                 1 << 30, vp(0)) == -5
+    winfo.n_elems, winfo.total_bytes = 4096 * 1000, 256 + 2 * 4096 * 1000
+    assert L.enc_decompress_gemm(vp(16), 1, 4096, vp(16), ctypes.byref(winfo), 1000, vp(16), vp(16),
+                                 1 << 30, vp(0)) == -2
+    # batch: negative count, missing table
+    assert L.enc_decompress_batch(vp(16), -1, vp(0)) == -1
+    assert L.enc_decompress_batch(vp(0), 3, vp(0)) == -1
+    assert L.enc_batch_prepare(None, 1, vp(16), 1 << 20, vp(0)) == -1

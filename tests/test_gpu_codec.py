@@ -1,0 +1,231 @@
+"""GPU parity of the codec against the CPU oracle, through the C ABI.
+
+Bit-exact everywhere: GPU streams equal the oracle's streams byte for byte,
+and GPU decoding of oracle streams (and of GPU streams) returns the input
+bits. Inputs come from the seeded generators; expected values come only from
+the oracle. Full-size cases cover every matrix of the Llama-shaped layer at
+B = 256/512/1024 and the five 2^27-element stress distributions; the 8B-shaped
+set is checked by round trip on all 226 tensors through one batched launch
+plus full oracle comparisons of selected tensors (including the largest).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from lossless_weight_compression_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BLOCKS = [128, 256, 512, 1024, 2048, 4096]
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def E():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_weight_compression_amd import enc
+    enc.lib()
+    return enc
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(np.int16)).cuda()
+
+
+def host_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def host_u8(t):
+    return t.cpu().numpy()
+
+
+def check_both_ways(E, orc, x, B, label=""):
+    """GPU stream == oracle stream; GPU decode of both == x."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    say("encode/decode", label, "n=%d B=%d" % (x.size, B))
+    ref = orc.encode(x, B)
+    xd = dev(x)
+    comp, info = E.enc_compress(xd, B)
+    torch.cuda.synchronize()
+    assert info.total_bytes == ref.size
+    got = host_u8(comp)
+    if not np.array_equal(got, ref):
+        bad = np.flatnonzero(got != ref)
+        raise AssertionError("stream differs at %d bytes, first at %d (%s)" % (bad.size, bad[0], label))
+    out = E.enc_decompress(comp, info)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out), x), label
+    # decode the oracle's own stream on the GPU
+    oc = torch.from_numpy(ref).cuda()
+    oinfo = E.enc_read_info(oc)
+    out2 = E.enc_decompress(oc, oinfo)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out2), x), label
+    return info
+
+
+# ------------------------------------------------------------- tiny config
+@pytest.mark.parametrize("B", BLOCKS)
+def test_tiny_all_block_sizes(E, orc, B):
+    info = check_both_ways(E, orc, synth.tiny(), B, "tiny")
+    assert info.flags == 0
+
+
+# ------------------------------------------------------------- edge sizes
+EDGE_N = [1, 2, 7, 8, 9, 127, 128, 129, 511, 512, 513, 600, 8191, 8192, 8193, 8200,
+          64 * 512 - 1, 64 * 512, 64 * 512 + 1, 3 * 64 * 512 + 517, 1_000_003]
+
+
+@pytest.mark.parametrize("n", EDGE_N)
+def test_edge_sizes_b512(E, orc, n):
+    x = synth.gaussian_bits((n,), 0.02, 90, n)
+    check_both_ways(E, orc, x, 512, "edge")
+
+
+@pytest.mark.parametrize("B", [128, 4096])
+@pytest.mark.parametrize("n", [129, 8193, 64 * 128 + 3, 64 * 4096 + 9, 300_001])
+def test_edge_sizes_other_blocks(E, orc, B, n):
+    x = synth.gaussian_bits((n,), 0.02, 91, n)
+    check_both_ways(E, orc, x, B, "edge")
+
+
+def test_empty(E):
+    say("empty stream")
+    comp, info = E.enc_compress(torch.empty(0, dtype=torch.int16, device="cuda"), 512)
+    torch.cuda.synchronize()
+    assert info.total_bytes == 256 and info.flags == 1
+    out = E.enc_decompress(comp, info)
+    assert out.numel() == 0
+
+
+# ------------------------------------------------------------- special inputs
+def test_all_patterns_raw_and_coded(E, orc):
+    allp = np.arange(65536, dtype=np.uint16)
+    rng = np.random.default_rng(77)
+    shuffled = rng.permutation(allp)
+    grouped = allp[np.argsort(((allp >> 7) & 0xFF).astype(np.int64) * 65536 + rng.permutation(65536),
+                              kind="stable")]
+    for B in (128, 256, 512):
+        check_both_ways(E, orc, shuffled, B, "all-patterns shuffled")
+        info = check_both_ways(E, orc, grouped, B, "all-patterns grouped")
+        assert info.flags == 0
+
+
+def test_extreme_widths(E, orc):
+    # every width 0..8 in neighbouring blocks, bases near 0 and near 255
+    B = 512
+    rng = np.random.default_rng(3)
+    blocks = []
+    for w in range(9):
+        for base in (0, 17, 255 - ((1 << w) - 1)):
+            e = np.full(B, base)
+            if w:
+                e[rng.integers(0, B, 40)] = base + rng.integers(0, 1 << w, 40)
+                e[5] = base + (1 << w) - 1
+            blocks.append(e)
+    exps = np.concatenate(blocks)
+    sms = rng.integers(0, 256, exps.size)
+    x = (((sms & 0x80) << 8) | (exps << 7) | (sms & 0x7F)).astype(np.uint16)
+    x = np.tile(x, 8)
+    info = check_both_ways(E, orc, x, B, "widths 0..8")
+    assert info.flags == 0
+
+
+# ------------------------------------------------------- Llama-shaped layer
+@pytest.mark.parametrize("B", [256, 512, 1024])
+def test_layer_full_size(E, orc, B):
+    for name, x in synth.layer().items():
+        check_both_ways(E, orc, x, B, "layer." + name)
+
+
+# ------------------------------------------------------ distribution stress
+@pytest.mark.parametrize("kind", synth.STRESS_KINDS)
+def test_stress_full_size(E, orc, kind):
+    x = synth.stress(kind)
+    for B in (256, 512, 1024):
+        info = check_both_ways(E, orc, x, B, "stress." + kind)
+        assert (info.flags == 1) == (kind == "uniform16")
+
+
+# ------------------------------------------------------------ batched decode
+def test_batch_mixed_items(E, orc):
+    xs = [synth.tiny(), synth.random_bits(70_001, 1), synth.gaussian_bits((3, 77777), 0.03, 5, 5),
+          np.zeros(0, np.uint16), synth.gaussian_bits((513,), 0.02, 6, 6),
+          synth.stress("const_exp", shape=(16, 4096))]
+    blocks = [512, 512, 128, 512, 4096, 1024]
+    items, outs = [], []
+    say("batch of", len(xs))
+    for x, B in zip(xs, blocks):
+        ref = orc.encode(x.reshape(-1), B)
+        comp = torch.from_numpy(ref).cuda()
+        info = E.enc_read_info(comp)
+        out = torch.full((max(x.size, 1),), -1, dtype=torch.int16, device="cuda")[:x.size]
+        items.append((comp, info, out))
+        outs.append(out)
+    table = E.enc_batch_prepare(items)
+    E.enc_decompress_batch(table, len(items))
+    torch.cuda.synchronize()
+    for x, out in zip(xs, outs):
+        assert np.array_equal(host_u16(out), x.reshape(-1))
+    # a second launch over the same table gives the same result
+    for out in outs:
+        out.fill_(7)
+    E.enc_decompress_batch(table, len(items))
+    torch.cuda.synchronize()
+    for x, out in zip(xs, outs):
+        assert np.array_equal(host_u16(out), x.reshape(-1))
+
+
+# ------------------------------------------------------------------ errors
+def test_capacity_error_leaves_output_untouched(E):
+    x = dev(synth.tiny())
+    out = torch.full((1000,), 0x5A, dtype=torch.uint8, device="cuda")
+    with pytest.raises(E.EncError) as e:
+        E.enc_compress(x, 512, out=out)
+    assert e.value.status == -3
+    torch.cuda.synchronize()
+    assert bool((out == 0x5A).all())
+
+
+# ----------------------------------------------------- 8B-shaped weight set
+def test_set8b_full_size(E, orc):
+    """All 226 tensors (8.03e9 values): GPU-compressed, decoded in one batched
+    launch, every output bit-exact; selected tensors also byte-exact against
+    the oracle's stream (smallest, a 4096x14336, and the 128256x4096 LM head)."""
+    shapes = synth.set8b_shapes()
+    streams = []
+    total_in = total_out = 0
+    for i, (name, r, c) in enumerate(shapes):
+        x = synth.set8b_tensor_gpu(i)
+        comp, info = E.enc_compress(x, 512)
+        streams.append((comp.clone(), info))
+        total_in += 2 * x.numel()
+        total_out += info.total_bytes
+        del x, comp
+    torch.cuda.synchronize()
+    say("set8b compressed: ratio %.4f" % (total_in / total_out))
+    assert 1.25 < total_in / total_out < 1.40
+    outs = [torch.empty(r * c, dtype=torch.int16, device="cuda") for _, r, c in shapes]
+    table = E.enc_batch_prepare([(cp, inf, o) for (cp, inf), o in zip(streams, outs)])
+    E.enc_decompress_batch(table, len(outs))
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        x = synth.set8b_tensor_gpu(i).reshape(-1)
+        assert torch.equal(outs[i], x), shapes[i][0]
+    del outs
+    for i in (1, 4 + 7 * 5, len(shapes) - 1):
+        name = shapes[i][0]
+        say("set8b oracle comparison", name)
+        x = synth.set8b_tensor_gpu(i)
+        ref = orc.encode(host_u16(x).reshape(-1), 512)
+        comp, info = streams[i]
+        assert info.total_bytes == ref.size, name
+        assert np.array_equal(host_u8(comp), ref), name
