@@ -45,8 +45,8 @@ def parse():
                    help="decoder layers in the set (32 = the full 8B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true")
-    p.add_argument("--cpu-sample-tensors", type=int, default=7,
-                   help="tensors of layer 0 the CPU oracle decodes (bounded sample)")
+    p.add_argument("--cpu-sample-tensors", type=int, default=21,
+                   help="first tensors of the set the CPU oracle decodes (bounded sample)")
     return p.parse_args()
 
 
@@ -291,7 +291,7 @@ def bench_gemm(enc, synth, torch, np, dev, stream):
 
 def cpu_baseline(synth, np, torch, dev, ntensors, B):
     """The CPU oracle, as it is (plain C, one thread), decoding the oracle's
-    own streams of the first `ntensors` tensors of layer 0 of the set."""
+    own streams of the first `ntensors` tensors of the set (21 = layers 0-2)."""
     from oracle import oracle as orc
     orc.build()
     n_total = 0

@@ -433,6 +433,7 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
     a.meta_off = h_winfo->meta_off;
     a.segoff_off = h_winfo->segoff_off;
     a.payload_off = h_winfo->payload_off;
+    a.total = h_winfo->total_bytes;
   }
   const hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "GEMM launch");

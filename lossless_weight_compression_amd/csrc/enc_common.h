@@ -99,6 +99,7 @@ struct GemmArgs {
   uint32_t log2b;
   uint64_t nb;
   uint64_t meta_off, segoff_off, payload_off;
+  uint64_t total;          // stream bytes (reads never go past it)
   uint32_t ksplit;         // number of K ranges
   uint32_t krows;          // rows per K range
 };

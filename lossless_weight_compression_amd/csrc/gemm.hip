@@ -13,10 +13,11 @@
 // payload is w * B / 8 bytes.
 //
 //  * M < 16  (k_gemm_valu): HBM-bound streaming. A wave owns a 512-column
-//    strip (lane: 8 columns) and a run of rows; each lane decodes its group of
-//    every row in registers and does M x 8 fp32 FMAs with X[m][k] read by
-//    scalar loads (uniform across the wave). The four waves of a workgroup
-//    reduce in LDS in a fixed order.
+//    strip (lane: 8 columns) and a run of 64 rows; a prologue finds every
+//    row's block offset, meta word and X[:, row] with independent loads (one
+//    row per lane), then rows are broadcast with v_readlane and decoded in
+//    registers, two batches of rows in flight, with M x 8 fp32 FMAs per row.
+//    The four waves of a workgroup reduce in LDS in a fixed order.
 //  * M >= 16 (k_gemm_mfma): a 128-column x 32-row W tile is decoded into LDS
 //    as BF16 per K step (two groups per thread), the X tile is staged in LDS,
 //    and v_mfma_f32_16x16x32_bf16 accumulates in fp32; the next step's
@@ -31,7 +32,7 @@ namespace enc {
 namespace {
 
 constexpr uint32_t kStrip = 512;               // VALU path: columns per workgroup
-constexpr uint32_t kValuRowsPerWave = 32;
+constexpr uint32_t kValuRowsPerWave = 64;
 constexpr uint32_t kValuRows = 4 * kValuRowsPerWave;
 constexpr uint32_t kTileN = 128;               // MFMA path: columns per workgroup
 constexpr uint32_t kKStep = 32;                // MFMA path: rows per K step
@@ -44,22 +45,40 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// Stream offset of the payload of block i (a full block of W):
-// payload_off + segment offset + (B/8) * sum of the widths of the earlier
-// blocks of the segment.
-__device__ __forceinline__ uint64_t block_offset(const GemmArgs &a, uint64_t i) {
-  const uint64_t seg = i >> 6;
-  const uint32_t t = (uint32_t)(i & 63);
-  const uint8_t *meta = a.wstream + a.meta_off + 2 * (seg << 6);
-  uint32_t wsum = 0;
-  uint32_t j = 0;
-  for (; j + 2 <= t; j += 2) {
-    const uint32_t d = ld32(meta + 2 * j);
-    wsum += ((d >> 8) & 0xFFu) + (d >> 24);
-  }
-  if (t & 1) wsum += meta[2 * j + 1];
+// Payload offset of block i0 (a full block of W) and its meta word: segment
+// offset plus (B/8) x the widths of the earlier blocks of the segment. With
+// `run512` (i0 starts a 512-column run, so i0 is a multiple of 512/B) the
+// word holds the 512/B {base, width} pairs of the run for B < 512 (naturally
+// aligned); otherwise only block i0's pair. All loads are issued at once (the
+// segment's 64 metas are 128 bytes inside the meta section).
+template <bool run512>
+__device__ __forceinline__ void row_block(const GemmArgs &a, uint64_t i0, uint64_t &off,
+                                          uint64_t &mw) {
+  const uint64_t seg = i0 >> 6;
+  const uint32_t t = (uint32_t)(i0 & 63);
+  const uint4 *m4 = reinterpret_cast<const uint4 *>(a.wstream + a.meta_off + 128 * seg);
+  const uint8_t *mp = a.wstream + a.meta_off + 2 * i0;
   const uint64_t so = *reinterpret_cast<const uint64_t *>(a.wstream + a.segoff_off + 8 * seg);
-  return a.payload_off + so + ((uint64_t)wsum << (a.log2b - 3));
+  if (!run512 || a.log2b >= 9)
+    mw = *reinterpret_cast<const uint16_t *>(mp);
+  else if (a.log2b == 8)
+    mw = ld32(mp);
+  else
+    mw = *reinterpret_cast<const uint64_t *>(mp);
+  uint4 v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = m4[q];
+  uint32_t wsum = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t d[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t b = 8 * q + 2 * h;   // blocks b, b+1 of the segment
+      wsum += (b < t ? (d[h] >> 8) & 0xFFu : 0u) + (b + 1 < t ? d[h] >> 24 : 0u);
+    }
+  }
+  off = a.payload_off + so + ((uint64_t)wsum << (a.log2b - 3));
 }
 
 // Raw material of one group of a compressed row: sign+mantissa dwords, code
@@ -68,39 +87,39 @@ struct GroupRaw {
   uint32_t sml, smh, q0, q1, q2, info;
 };
 
-// Group `lane_group` (0-based group index inside a run of columns starting at
-// element e, e a multiple of the run width and the run within one strip) of
-// the compressed row holding element e. `blk_off` is the stream offset of
-// block e >> log2b. For B < 512 a 512-column run spans 512/B blocks of one
-// segment; the lane adds the sizes of the run's earlier blocks.
+// Loads group g of the run of columns that starts at element e (e is the
+// first element of a 512- or 128-column run; the run lies in one segment).
+// blk_off / mw are row_block()'s results for block e >> log2b. For B < 512 a
+// 512-column run spans 512/B blocks; the lane adds the sizes of the earlier
+// ones, read from the meta word.
 __device__ __forceinline__ GroupRaw load_group(const GemmArgs &a, uint64_t e, uint32_t g,
-                                               uint64_t blk_off) {
+                                               uint64_t blk_off, uint64_t mw) {
   const uint8_t *__restrict__ s = a.wstream;
   const uint32_t log2b = a.log2b;
-  const uint64_t i0 = e >> log2b;
   uint32_t meta, extra = 0, u;
   if (log2b >= 9 || g < (1u << (log2b - 3))) {
-    // the group lies in block i0
-    meta = *reinterpret_cast<const uint16_t *>(s + a.meta_off + 2 * i0);
+    meta = (uint32_t)mw & 0xFFFFu;
     u = (uint32_t)((e & ((1u << log2b) - 1)) >> 3) + g;
   } else {
     const uint32_t bl = g >> (log2b - 3);       // block of the run (1..3)
-    const uint64_t mw = (log2b == 8) ? (uint64_t)ld32(s + a.meta_off + 2 * i0)
-                                     : *reinterpret_cast<const uint64_t *>(s + a.meta_off + 2 * i0);
     meta = (uint32_t)(mw >> (16 * bl)) & 0xFFFFu;
     for (uint32_t j = 0; j < bl; ++j) extra += (uint32_t)((mw >> (16 * j + 8)) & 0xFFu);
     extra <<= (log2b - 3);
     u = g & ((1u << (log2b - 3)) - 1);
   }
-  const uint32_t w = meta >> 8;
+  uint32_t w = meta >> 8;
+  // corrupted stream guard: a width above 8, or a block running past the
+  // stream end, decodes as width 0 (wrong values, but no stray reads)
+  if (w > 8 || blk_off + extra + ((uint64_t)w << (log2b - 3)) > a.total) w = 0;
+  const uint64_t pb = blk_off + extra + (uint64_t)u * w;
   const uint64_t sm_addr = kHeaderBytes + e + 8 * (uint64_t)g;
   const uint2 sm = *reinterpret_cast<const uint2 *>(s + sm_addr);
   GroupRaw r;
   r.sml = sm.x;
   r.smh = sm.y;
   uint32_t lead;
-  load_codes(s, blk_off + extra + (uint64_t)u * w, w, sm_addr, r.q0, r.q1, r.q2, lead);
-  r.info = (meta << 16) | (lead << 3);
+  load_codes(s, pb, w, sm_addr, r.q0, r.q1, r.q2, lead);
+  r.info = ((meta & 0xFFu) << 16) | (w << 24) | (lead << 3);
   return r;
 }
 
@@ -113,9 +132,21 @@ __device__ __forceinline__ uint4 decode_raw(const GroupRaw &r) {
 }
 
 // Split-K epilogue shared by both kernels: the workgroup's fp32 tile
-// `vals(i)` for i in [0, count) maps to Y element ymap(i). With one K range it
-// writes Y; otherwise it writes its partial slice, and the last arriving
-// workgroup of the tile sums the slices in K order into Y.
+// `vals(i)` for i in [0, count) maps to Y element ymap(i) (-1 = none). With
+// one K range it writes Y. Otherwise, in one launch:
+//  1. the partial slice is written with agent-scope stores (global_store sc1:
+//     written through this XCD's L2 to the device-coherent level);
+//  2. s_waitcnt vmcnt(0) waits until every one of those stores is
+//     acknowledged, then the workgroup barrier;
+//  3. one agent-scope atomic add counts the workgroup in;
+//  4. the workgroup that sees the count reach ksplit - 1 reads all slices with
+//     agent-scope loads (global_load sc1, never served by a stale line of its
+//     own L2), adds them in K order -- deterministic -- writes Y and resets
+//     the counter for the next call.
+// No __threadfence(): on gfx950 an agent-scope release fence writes back the
+// whole XCD L2 (buffer_wbl2), which measured as the dominant cost of this
+// kernel when every workgroup issued one. Nothing here relies on L2
+// write-back: the only cross-workgroup data is written through.
 template <class Vals, class YMap>
 __device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t tile_id, uint32_t ks,
                                               uint32_t count, Vals vals, YMap ymap) {
@@ -131,22 +162,36 @@ __device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t tile_i
   const uint64_t MN = (uint64_t)a.M * a.N;
   for (uint32_t i = tid; i < count; i += blockDim.x) {
     const int64_t y = ymap(i);
-    if (y >= 0) a.partial[(uint64_t)ks * MN + (uint64_t)y] = vals(i);
+    if (y >= 0)
+      __hip_atomic_store(a.partial + (uint64_t)ks * MN + (uint64_t)y, vals(i), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.counters[tile_id], 1u) == a.ksplit - 1) ? 1u : 0u;
+  if (tid == 0)
+    s_last = (__hip_atomic_fetch_add(&a.counters[tile_id], 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == a.ksplit - 1) ? 1u : 0u;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   for (uint32_t i = tid; i < count; i += blockDim.x) {
     const int64_t y = ymap(i);
     if (y < 0) continue;
+    const float *p = a.partial + (uint64_t)y;
     float sum = 0.f;
-    for (uint32_t k = 0; k < a.ksplit; ++k) sum += __builtin_nontemporal_load(a.partial + (uint64_t)k * MN + (uint64_t)y);
+    uint32_t k = 0;
+    for (; k + 8 <= a.ksplit; k += 8) {   // eight loads in flight, added in K order
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = __hip_atomic_load(p + (uint64_t)(k + j) * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += v[j];
+    }
+    for (; k < a.ksplit; ++k)
+      sum += __hip_atomic_load(p + (uint64_t)k * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.y[y] = sum;
   }
-  if (tid == 0) atomicExch(&a.counters[tile_id], 0u);
+  if (tid == 0) __hip_atomic_store(&a.counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------------------
@@ -154,56 +199,80 @@ __device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t tile_i
 // --------------------------------------------------------------------------
 template <int MM, bool DENSE>
 __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
+  constexpr uint32_t RB = MM <= 4 ? 8 : 4;      // rows per batch; two batches in flight
   __shared__ float red[MM * kStrip];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t c = blockIdx.x, ks = blockIdx.y;
   const uint32_t N = a.N, K = a.K;
-  const uint32_t rows_w = a.krows / 4;
+  const uint32_t rows_w = a.krows / 4;          // <= 64
   const uint32_t kw0 = ks * a.krows + wave * rows_w;
   const uint32_t kw1 = min(kw0 + rows_w, K);
+  const uint32_t nrows = kw1 > kw0 ? kw1 - kw0 : 0;
+  const uint64_t col0 = (uint64_t)c * kStrip;
+
+  // Prologue: lane l describes row kw0 + l -- block offset and meta word of
+  // the strip's first block, and X[m][row]. Rows are then broadcast with
+  // v_readlane, so the row loop has no dependent loads.
+  uint64_t r_off = 0, r_mw = 0;
+  float xr[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) xr[m] = 0.f;
+  if (lane < nrows) {
+    const uint32_t kr = kw0 + lane;
+    if (!DENSE) row_block<true>(a, ((uint64_t)kr * N + col0) >> a.log2b, r_off, r_mw);
+#pragma unroll
+    for (int m = 0; m < MM; ++m) xr[m] = bf_lo(a.x[(uint64_t)m * K + kr]);
+  }
+
   float acc[MM][8];
 #pragma unroll
   for (int m = 0; m < MM; ++m)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[m][q] = 0.f;
 
-  for (uint32_t kb = kw0; kb < kw1; kb += 64) {
-    const uint32_t kbe = min(kb + 64, kw1);
-    uint64_t my_off = 0;   // stream offset of block holding row (kb+lane)'s strip start
-    if (!DENSE && kb + lane < kbe)
-      my_off = block_offset(a, ((uint64_t)(kb + lane) * N + (uint64_t)c * kStrip) >> a.log2b);
-    for (uint32_t k = kb; k < kbe; k += 4) {
-      GroupRaw raw[4];
-      uint4 dv[4];
+  auto load_batch = [&](uint32_t r0, GroupRaw(&raw)[RB], uint4(&dv)[RB]) {
 #pragma unroll
-      for (uint32_t j = 0; j < 4; ++j) {
-        const uint32_t kr = k + j;
-        if (kr < kbe) {
-          const uint64_t e = (uint64_t)kr * N + (uint64_t)c * kStrip;
-          if (DENSE) {
-            dv[j] = *reinterpret_cast<const uint4 *>(a.wdense + e + 8 * lane);
-          } else {
-            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)my_off, kr - kb);
-            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(my_off >> 32), kr - kb);
-            raw[j] = load_group(a, e, lane, ((uint64_t)hi << 32) | lo);
-          }
+    for (uint32_t j = 0; j < RB; ++j) {
+      const uint32_t r = r0 + j;
+      if (r < nrows) {
+        const uint64_t e = (uint64_t)(kw0 + r) * N + col0;
+        if (DENSE) {
+          dv[j] = *reinterpret_cast<const uint4 *>(a.wdense + e + 8 * lane);
+        } else {
+          const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(r_off >> 32), r) << 32) |
+                               __builtin_amdgcn_readlane((uint32_t)r_off, r);
+          const uint64_t mw = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(r_mw >> 32), r) << 32) |
+                              __builtin_amdgcn_readlane((uint32_t)r_mw, r);
+          raw[j] = load_group(a, e, lane, off, mw);
         }
       }
+    }
+  };
+  auto compute_batch = [&](uint32_t r0, const GroupRaw(&raw)[RB], const uint4(&dv)[RB]) {
 #pragma unroll
-      for (uint32_t j = 0; j < 4; ++j) {
-        const uint32_t kr = k + j;
-        if (kr >= kbe) break;
+    for (uint32_t j = 0; j < RB; ++j) {
+      const uint32_t r = r0 + j;
+      if (r < nrows) {
         const uint4 v = DENSE ? dv[j] : decode_raw(raw[j]);
         const float f[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
                             bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
-          const float xm = bf_lo(a.x[(uint64_t)m * K + kr]);
+          const float xm = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(xr[m]), r));
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc[m][q] = fmaf(xm, f[q], acc[m][q]);
         }
       }
     }
+  };
+  GroupRaw rawA[RB], rawB[RB];
+  uint4 dvA[RB], dvB[RB];
+  if (nrows) load_batch(0, rawA, dvA);
+  for (uint32_t r0 = 0; r0 < nrows; r0 += 2 * RB) {
+    if (r0 + RB < nrows) load_batch(r0 + RB, rawB, dvB);
+    compute_batch(r0, rawA, dvA);
+    if (r0 + 2 * RB < nrows) load_batch(r0 + 2 * RB, rawA, dvA);
+    if (r0 + RB < nrows) compute_batch(r0 + RB, rawB, dvB);
   }
   // deterministic reduction of the four waves' rows: wave 0, then 1, 2, 3
   for (uint32_t w = 0; w < 4; ++w) {
@@ -220,9 +289,7 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
   }
   splitk_finish(
       a, c, ks, MM * kStrip, [&](uint32_t i) { return red[i]; },
-      [&](uint32_t i) -> int64_t {
-        return (int64_t)(i / kStrip) * N + (int64_t)c * kStrip + (i % kStrip);
-      });
+      [&](uint32_t i) -> int64_t { return (int64_t)(i / kStrip) * N + (int64_t)col0 + (i % kStrip); });
 }
 
 // --------------------------------------------------------------------------
@@ -233,7 +300,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   constexpr int MSUB = MT / 16;
   __shared__ __attribute__((aligned(16))) uint16_t wt[kKStep * kWPitch];
   __shared__ __attribute__((aligned(16))) uint16_t xt[MT * kXPitch];
-  __shared__ uint32_t row_off_lo[1024], row_off_hi[1024];
+  __shared__ uint32_t row_off_lo[1024], row_off_hi[1024], row_meta[1024];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t nt = blockIdx.x, ks = blockIdx.y, mt = blockIdx.z;
   const uint32_t N = a.N, K = a.K, M = a.M;
@@ -244,9 +311,11 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
 
   if (!DENSE) {
     for (uint32_t r = tid; r < k1 - k0; r += 256) {
-      const uint64_t off = block_offset(a, ((uint64_t)(k0 + r) * N + n0) >> a.log2b);
+      uint64_t off, mw;
+      row_block<false>(a, ((uint64_t)(k0 + r) * N + n0) >> a.log2b, off, mw);
       row_off_lo[r] = (uint32_t)off;
       row_off_hi[r] = (uint32_t)(off >> 32);
+      row_meta[r] = (uint32_t)mw & 0xFFFFu;
     }
     __syncthreads();
   }
@@ -272,7 +341,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
         } else {
           const uint32_t r = kr - k0;
           const uint64_t off = ((uint64_t)row_off_hi[r] << 32) | row_off_lo[r];
-          raw[h] = load_group(a, e, tg, off);
+          raw[h] = load_group(a, e, tg, off, row_meta[r]);
         }
       }
     }
@@ -395,20 +464,21 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
 
 void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows) {
   if (M < 16) {
-    const uint32_t rows = kValuRows;
-    *ksplit = (K + rows - 1) / rows;
-    *krows = rows;
+    *krows = kValuRows;
+    *ksplit = (K + kValuRows - 1) / kValuRows;
     return;
   }
+  // enough workgroups to cover the CUs; at most 1024 rows per K range (the
+  // per-row block offsets are kept in LDS), at least 64
   const uint32_t MT = mfma_tile_m(M);
   const uint64_t tiles = (uint64_t)(N / kTileN) * ((M + MT - 1) / MT);
   const uint64_t target = M <= 32 ? 512 : 256;
-  uint32_t ks = (uint32_t)((target + tiles - 1) / tiles);
-  const uint32_t max_ks = (K + 1023) / 1024 > (K + 63) / 64 ? (K + 1023) / 1024 : (K + 63) / 64;
-  if (ks < (K + 1023) / 1024) ks = (K + 1023) / 1024;   // at most 1024 rows per range (LDS table)
-  if (ks > max_ks) ks = max_ks;
+  uint64_t ks = (target + tiles - 1) / tiles;
+  const uint64_t ks_min = (K + 1023) / 1024, ks_max = (K + 63) / 64;
+  if (ks < ks_min) ks = ks_min;
+  if (ks > ks_max) ks = ks_max;
   if (ks < 1) ks = 1;
-  uint32_t rows = (K + ks - 1) / ks;
+  uint32_t rows = (uint32_t)((K + ks - 1) / ks);
   rows = (rows + kKStep - 1) / kKStep * kKStep;
   *krows = rows;
   *ksplit = (K + rows - 1) / rows;

@@ -1,0 +1,161 @@
+"""GPU parity of the fused decompress-GEMM (and its uncompressed twin) against
+the oracle's fp64 product, through the C ABI.
+
+Acceptance per output: |y_gpu - y_ref| <= 1e-4 * sum_k |x[m,k] * w[k,n]|,
+both reference terms in fp64 from the oracle, with W the oracle-decoded
+weight. One-hot rows of X must reproduce rows of W exactly (pins indexing and
+layout). Full size: W 4096x14336 (N(0, 0.02), B=512), M in {1, 16, 128};
+M = 128 is checked on a sample of columns the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from lossless_weight_compression_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def E():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_weight_compression_amd import enc
+    enc.lib()
+    return enc
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+
+
+def bf16_f64(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_fused(E, X, comp, info, N, ws=None):
+    y = E.enc_decompress_gemm(dev(X), comp, info, N, ws=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def run_dense(E, X, W, ws=None):
+    y = E.enc_gemm_dense(dev(X), dev(W), ws=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def assert_within(y, Y, A, label):
+    err = np.abs(y - Y)
+    bad = err > TOL * A
+    assert not bad.any(), "%s: %d outputs out of tolerance, worst err %g (bound %g)" % (
+        label, int(bad.sum()), err[bad].max(), (TOL * A)[bad][np.argmax(err[bad])])
+
+
+def compress_oracle(orc, W, B):
+    """Upload the oracle's stream of W (expected values never come from the GPU)."""
+    ref = orc.encode(W.reshape(-1), B)
+    comp = torch.from_numpy(ref).cuda()
+    return comp, None
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 15, 16, 17, 40, 128, 129])
+def test_one_hot_rows_exact(E, orc, M):
+    K, N = 256, 1024
+    W = synth.gaussian_bits((K, N), 0.02, 200, M)
+    rng = np.random.default_rng(M)
+    X = np.zeros((M, K), np.uint16)
+    ks = rng.integers(0, K, M)
+    X[np.arange(M), ks] = 0x3F80                     # 1.0
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512)).cuda()
+    info = E.enc_read_info(comp)
+    say("one-hot M=%d" % M)
+    y = run_fused(E, X, comp, info, N)
+    Wf = bf16_f64(W)
+    assert np.array_equal(y, Wf[ks]), "fused"
+    assert np.array_equal(run_dense(E, X, W), Wf[ks]), "dense"
+
+
+@pytest.mark.parametrize("B", [128, 256, 512, 1024, 4096])
+@pytest.mark.parametrize("M", [1, 5, 16, 33])
+def test_block_sizes_small(E, orc, B, M):
+    K, N = 520, 4096                                  # K not a multiple of the K ranges
+    W = synth.gaussian_bits((K, N), 0.02, 201, B)
+    X = synth.gemm_activations(M, K)
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), B)).cuda()
+    info = E.enc_read_info(comp)
+    Y, A = orc.gemm_f64(X, W)
+    say("B=%d M=%d" % (B, M))
+    assert_within(run_fused(E, X, comp, info, N), Y, A, "fused B=%d M=%d" % (B, M))
+    assert_within(run_dense(E, X, W), Y, A, "dense B=%d M=%d" % (B, M))
+
+
+def test_raw_weight(E, orc):
+    # exponents 1..64 and 129..190 in every block: width 8 everywhere -> RAW
+    K, N = 128, 1024
+    rng = np.random.default_rng(5)
+    exps = np.where(rng.random((K, N)) < 0.5, rng.integers(1, 65, (K, N)),
+                    rng.integers(129, 191, (K, N)))
+    sm = rng.integers(0, 256, (K, N))
+    W = (((sm & 0x80) << 8) | (exps << 7) | (sm & 0x7F)).astype(np.uint16)
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512)).cuda()
+    info = E.enc_read_info(comp)
+    assert info.flags == 1
+    for M in (2, 20):
+        X = synth.gemm_activations(M, K)
+        Y, A = orc.gemm_f64(X, W)
+        assert_within(run_fused(E, X, comp, info, N), Y, A, "raw M=%d" % M)
+
+
+def test_gpu_stream_and_workspace_reuse(E, orc):
+    # GPU-compressed W; the same workspace serves consecutive calls (counters
+    # are left at zero), results are deterministic, and a smaller M follows
+    K, N = 1024, 2048
+    W = synth.gaussian_bits((K, N), 0.02, 202, 0)
+    comp, info = E.enc_compress(dev(W), 512)
+    ws = E.gemm_workspace(64, K, N, 512)
+    ys = []
+    for M in (64, 64, 24, 2, 64):
+        X = synth.gemm_activations(M, K)
+        Y, A = orc.gemm_f64(X, W)
+        y = run_fused(E, X, comp, info, N, ws=ws)
+        assert_within(y, Y, A, "reuse M=%d" % M)
+        ys.append(y)
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[4])
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_full_size_all_outputs(E, orc, M):
+    K, N = 4096, 14336
+    W = synth.gemm_weight(K, N)
+    X = synth.gemm_activations(M, K)
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512)).cuda()
+    info = E.enc_read_info(comp)
+    say("full size M=%d" % M)
+    Y, A = orc.gemm_f64(X, W)
+    assert_within(run_fused(E, X, comp, info, N), Y, A, "fused full M=%d" % M)
+    assert_within(run_dense(E, X, W), Y, A, "dense full M=%d" % M)
+
+
+def test_full_size_m128_sampled(E, orc):
+    K, N, M = 4096, 14336, 128
+    W = synth.gemm_weight(K, N)
+    X = synth.gemm_activations(M, K)
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512)).cuda()
+    info = E.enc_read_info(comp)
+    rng = np.random.default_rng(128)
+    cols = np.unique(np.concatenate([rng.integers(0, N, 300), np.arange(0, 512),
+                                     np.arange(N - 128, N)])).astype(np.uint32)
+    say("full size M=128, %d sampled columns" % cols.size)
+    Y, A = orc.gemm_f64_cols(X, W, cols)
+    assert_within(run_fused(E, X, comp, info, N)[:, cols], Y, A, "fused M=128")
+    assert_within(run_dense(E, X, W)[:, cols], Y, A, "dense M=128")
