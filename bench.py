@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 METRIC = "decompress GB/s (BF16 out) + % of HBM roofline; compression ratio"
-DECODE_SRC = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc")
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "group_math.h", "enc_common.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_batch_set8b_pmc.json")
 
 
@@ -50,8 +51,11 @@ def parse():
     return p.parse_args()
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(n_launch_bytes):
@@ -61,7 +65,7 @@ def traffic_from_profile(n_launch_bytes):
         d = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
         return None
-    if d.get("decode_source_sha256_16") != source_hash(DECODE_SRC):
+    if d.get("decode_source_sha256_16") != source_hash(DECODE_SRCS):
         return None
     return d.get("hbm_bytes_per_launch")
 
