@@ -179,13 +179,13 @@ __device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t tile_i
     const float *p = a.partial + (uint64_t)y;
     float sum = 0.f;
     uint32_t k = 0;
-    for (; k + 8 <= a.ksplit; k += 8) {   // eight loads in flight, added in K order
-      float v[8];
+    for (; k + 16 <= a.ksplit; k += 16) {   // sixteen loads in flight, added in K order
+      float v[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 16; ++j)
         v[j] = __hip_atomic_load(p + (uint64_t)(k + j) * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum += v[j];
+      for (int j = 0; j < 16; ++j) sum += v[j];
     }
     for (; k < a.ksplit; ++k)
       sum += __hip_atomic_load(p + (uint64_t)k * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -201,7 +201,8 @@ template <int MM, bool DENSE>
 __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
   constexpr uint32_t RB = MM <= 4 ? 8 : 4;      // rows per batch; two batches in flight
   __shared__ float red[MM * kStrip];
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const uint32_t c = blockIdx.x, ks = blockIdx.y;
   const uint32_t N = a.N, K = a.K;
   const uint32_t rows_w = a.krows / 4;          // <= 64
@@ -293,6 +294,163 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// M < 16 and B >= 512: wave-uniform rows.
+//
+// A 512-column strip of a row lies inside one block when B >= 512, so the
+// width, base and block offset of every row a wave touches are uniform
+// across the wave: they live in SGPRs (v_readlane of a per-lane prologue
+// table), payload dwords are fetched with 32-bit offsets off the stream's
+// SGPR base, and the exponent/sign+mantissa byte planes turn into fp32 with
+// one v_perm per value (high byte = sign | e >> 1, next byte = (e & 1) << 7 |
+// mantissa, low bytes zero).
+// --------------------------------------------------------------------------
+constexpr uint32_t kRowsPerWaveU = 32;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Raw buffer descriptor over a whole stream (< 4 GiB): loads take a 32-bit
+// offset, and the hardware checks every dword against num_records = stream
+// size (out-of-range dwords read as 0, per dword), so a group's three code
+// dwords are one buffer_load_dwordx3 even at the very end of the stream.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t *s, uint64_t total) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(s), 0, (int)(uint32_t)total,
+                                           0x00020000);
+}
+
+template <int MM>
+__global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
+  constexpr uint32_t RW = kRowsPerWaveU;
+  constexpr uint32_t RB = MM <= 4 ? 8 : 4;       // rows per batch; two batches in flight
+  __shared__ float red[MM * kStrip];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const uint32_t c = blockIdx.x, ks = blockIdx.y;
+  const uint32_t N = a.N, K = a.K, log2b = a.log2b;
+  const uint32_t kw0 = ks * a.krows + wave * RW;
+  const uint32_t nrows = kw0 < K ? min(RW, K - kw0) : 0u;
+  const uint32_t col0 = c * kStrip;
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
+
+  // Prologue: lane l describes row kw0 + l (block offset, {base, width},
+  // first group of the strip inside its block) and holds X[:, kw0 + l].
+  uint32_t r_off = 0, r_meta = 0;
+  float xr[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) xr[m] = 0.f;
+  if (lane < nrows) {
+    const uint32_t kr = kw0 + lane;
+    const uint64_t e = (uint64_t)kr * N + col0;
+    uint64_t off, mw;
+    row_block<false>(a, e >> log2b, off, mw);
+    uint32_t w = (uint32_t)(mw >> 8) & 0xFFu;
+    if (w > 8) w = 0;   // corrupted stream: decode as width 0 (reads stay bounds-checked)
+    const uint32_t u0 = (uint32_t)((e & ((1ull << log2b) - 1)) >> 3);
+    r_off = (uint32_t)off;
+    r_meta = ((uint32_t)mw & 0xFFu) | (w << 8) | (u0 << 16);
+#pragma unroll
+    for (int m = 0; m < MM; ++m) xr[m] = bf_lo(a.x[(uint64_t)m * K + kr]);
+  }
+
+  float acc[MM][8];
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[m][q] = 0.f;
+
+  struct Batch {
+    u32x2 sm[RB];
+    u32x3 q[RB];
+  };
+  auto load_batch = [&](uint32_t r0, Batch &bt) {
+#pragma unroll
+    for (uint32_t j = 0; j < RB; ++j) {
+      const uint32_t r = r0 + j;
+      if (r < nrows) {
+        const uint32_t off = __builtin_amdgcn_readlane(r_off, r);
+        const uint32_t meta = __builtin_amdgcn_readlane(r_meta, r);
+        const uint32_t w = (meta >> 8) & 15u;
+        const uint32_t pb = off + ((meta >> 16) + lane) * w;
+        const uint32_t row_sm = kHeaderBytes + (kw0 + r) * N + col0;   // uniform
+        bt.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, row_sm, 0);
+        bt.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
+      }
+    }
+  };
+  auto compute_batch = [&](uint32_t r0, const Batch &bt) {
+#pragma unroll
+    for (uint32_t j = 0; j < RB; ++j) {
+      const uint32_t r = r0 + j;
+      if (r < nrows) {
+        const uint32_t off = __builtin_amdgcn_readlane(r_off, r);
+        const uint32_t meta = __builtin_amdgcn_readlane(r_meta, r);
+        const uint32_t w = (meta >> 8) & 15u;
+        const uint32_t base4 = (meta & 0xFFu) * 0x01010101u;
+        const uint32_t sh = ((off + ((meta >> 16) + lane) * w) & 3u) * 8;
+        const uint32_t lo = __builtin_amdgcn_alignbit(bt.q[j].y, bt.q[j].x, sh);
+        const uint32_t hi = __builtin_amdgcn_alignbit(bt.q[j].z, bt.q[j].y, sh);
+        const uint32_t mid = (w == 8) ? hi : __builtin_amdgcn_alignbit(hi, lo, 4 * w);
+        const uint32_t w2 = w + w, w3 = w2 + w;
+        uint32_t el = __builtin_amdgcn_ubfe(lo, 0, w);
+        el |= __builtin_amdgcn_ubfe(lo, w, w) << 8;
+        el |= __builtin_amdgcn_ubfe(lo, w2, w) << 16;
+        el |= __builtin_amdgcn_ubfe(lo, w3, w) << 24;
+        uint32_t eh = __builtin_amdgcn_ubfe(mid, 0, w);
+        eh |= __builtin_amdgcn_ubfe(mid, w, w) << 8;
+        eh |= __builtin_amdgcn_ubfe(mid, w2, w) << 16;
+        eh |= __builtin_amdgcn_ubfe(mid, w3, w) << 24;
+        el += base4;
+        eh += base4;
+        const uint32_t sml = bt.sm[j].x, smh = bt.sm[j].y;
+        const uint32_t hl = (sml & kH8) | ((el >> 1) & ~kH8);
+        const uint32_t ll = ((el << 7) & kH8) | (sml & ~kH8);
+        const uint32_t hh = (smh & kH8) | ((eh >> 1) & ~kH8);
+        const uint32_t lh = ((eh << 7) & kH8) | (smh & ~kH8);
+        // fp32 of value k: bytes [0, 0, L_k, H_k]
+        const float f[8] = {
+            __uint_as_float(__builtin_amdgcn_perm(hl, ll, 0x04000C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hl, ll, 0x05010C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hl, ll, 0x06020C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hl, ll, 0x07030C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hh, lh, 0x04000C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hh, lh, 0x05010C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hh, lh, 0x06020C0Cu)),
+            __uint_as_float(__builtin_amdgcn_perm(hh, lh, 0x07030C0Cu))};
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          const float xm = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(xr[m]), r));
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[m][q] = fmaf(xm, f[q], acc[m][q]);
+        }
+      }
+    }
+  };
+  Batch bA, bB;
+  if (nrows) load_batch(0, bA);
+  for (uint32_t r0 = 0; r0 < nrows; r0 += 2 * RB) {
+    if (r0 + RB < nrows) load_batch(r0 + RB, bB);
+    compute_batch(r0, bA);
+    if (r0 + 2 * RB < nrows) load_batch(r0 + 2 * RB, bA);
+    if (r0 + RB < nrows) compute_batch(r0 + RB, bB);
+  }
+  for (uint32_t w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t idx = m * kStrip + 8 * lane + q;
+          red[idx] = (w == 0 ? 0.f : red[idx]) + acc[m][q];
+        }
+    }
+    __syncthreads();
+  }
+  splitk_finish(
+      a, c, ks, MM * kStrip, [&](uint32_t i) { return red[i]; },
+      [&](uint32_t i) -> int64_t { return (int64_t)(i / kStrip) * N + (int64_t)col0 + (i % kStrip); });
+}
+
+// --------------------------------------------------------------------------
 // M >= 16: MFMA path.
 // --------------------------------------------------------------------------
 template <int MT, bool DENSE>
@@ -301,7 +459,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[kKStep * kWPitch];
   __shared__ __attribute__((aligned(16))) uint16_t xt[MT * kXPitch];
   __shared__ uint32_t row_off_lo[1024], row_off_hi[1024], row_meta[1024];
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const uint32_t nt = blockIdx.x, ks = blockIdx.y, mt = blockIdx.z;
   const uint32_t N = a.N, K = a.K, M = a.M;
   const uint32_t n0 = nt * kTileN, m0 = mt * MT;
@@ -445,6 +604,19 @@ hipError_t launch_valu(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
+  const dim3 grid(a.N / kStrip, a.ksplit);
+  switch (a.M) {
+#define CASE(m) \
+  case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(256), 0, s, a); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 uint32_t mfma_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 template <bool DENSE>
@@ -462,10 +634,20 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
-void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows) {
-  if (M < 16) {
-    *krows = kValuRows;
-    *ksplit = (K + kValuRows - 1) / kValuRows;
+// Which kernel serves a call: 0 = generic VALU (M < 16), 1 = uniform-row VALU
+// (M < 16, compressed, B >= 512, stream below 2 GiB: 32-bit buffer offsets),
+// 2 = MFMA (M >= 16).
+uint32_t gemm_kind(uint32_t M, bool dense, uint32_t log2b, uint64_t total) {
+  if (M >= 16) return 2;
+  return (!dense && log2b >= 9 && total < (1ull << 31)) ? 1 : 0;
+}
+
+void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit,
+                    uint32_t *krows) {
+  if (kind == 0 || kind == 1) {
+    const uint32_t rows = kind == 0 ? kValuRows : 4 * kRowsPerWaveU;
+    *krows = rows;
+    *ksplit = (K + rows - 1) / rows;
     return;
   }
   // enough workgroups to cover the CUs; at most 1024 rows per K range (the
@@ -484,22 +666,36 @@ void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *k
   *ksplit = (K + rows - 1) / rows;
 }
 
+void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows) {
+  gemm_plan_kind(M >= 16 ? 2 : 0, M, K, N, ksplit, krows);
+}
+
+static uint64_t counter_slots(uint32_t M, uint32_t N) {
+  return M < 16 ? N / kStrip : (uint64_t)(N / kTileN) * ((M + 127) / 16 + 1);
+}
+
 uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
-  uint32_t ks, kr;
-  gemm_plan(M, K, N, &ks, &kr);
-  const uint64_t tiles = M < 16 ? N / kStrip : (uint64_t)(N / kTileN) * ((M + 127) / 16 + 1);
-  const uint64_t counters = align_up(4 * tiles, 256);
-  const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
-  return counters + partial;
+  // enough for whichever kernel the call selects
+  uint64_t most = 0;
+  for (uint32_t kind = 0; kind < 3; ++kind) {
+    if ((kind == 2) != (M >= 16)) continue;
+    uint32_t ks, kr;
+    gemm_plan_kind(kind, M, K, N, &ks, &kr);
+    const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
+    if (partial > most) most = partial;
+  }
+  return align_up(4 * counter_slots(M, N), 256) + most;
 }
 
 hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
   GemmArgs a = a_in;
-  const uint32_t tiles = a.M < 16 ? a.N / kStrip : (a.N / kTileN) * ((a.M + 127) / 16 + 1);
-  a.partial = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(a.counters) +
-                                        align_up(4ull * tiles, 256));
   const bool dense = a.wstream == nullptr;
-  if (a.M < 16) return dense ? launch_valu<true>(a, s) : launch_valu<false>(a, s);
+  const uint32_t kind = gemm_kind(a.M, dense, a.log2b, a.total);
+  gemm_plan_kind(kind, a.M, a.K, a.N, &a.ksplit, &a.krows);
+  a.partial = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(a.counters) +
+                                        align_up(4ull * counter_slots(a.M, a.N), 256));
+  if (kind == 1) return launch_rowu(a, s);
+  if (kind == 0) return dense ? launch_valu<true>(a, s) : launch_valu<false>(a, s);
   return dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
 }
 
