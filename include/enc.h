@@ -132,8 +132,8 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table,
 /* Decode every item of a prepared table with one kernel launch; asynchronous. */
 enc_status enc_decompress_batch(const void *d_table, int count, void *stream);
 
-/* Device workspace bytes for enc_decompress_gemm (split-K partial sums,
- * arrival counters, per-block offset index). */
+/* Device workspace bytes for enc_decompress_gemm / enc_gemm_dense: the
+ * split-K partial sums (fp32, one slice per K range). */
 uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size);
 
 /* Fused decompress-GEMM (ZipServ Abstract: decompress on the fly into the
@@ -141,12 +141,13 @@ uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t b
  *   Y[M,N] (fp32, overwritten) = X[M,K] (BF16 row-major) * W[K,N]
  * where W is the row-major BF16 matrix compressed in d_wcomp (n_elems = K*N).
  * Requirements: K*N == n_elems, N % 512 == 0 and N % block_size == 0,
- * 1 <= M <= 4096, else ENC_ERR_SHAPE / ENC_ERR_UNSUPPORTED. A RAW stream is
- * multiplied directly from its verbatim values. The workspace must be at
- * least enc_gemm_workspace_bytes(M, K, N, block_size) bytes and must be
- * zero-filled before its first use; calls leave it zero-filled again, so it
- * can be reused by later calls on the same stream (not by concurrent calls).
- * Accumulation is fp32; the result is deterministic. */
+ * K % 8 == 0, 1 <= M <= 4096, else ENC_ERR_SHAPE / ENC_ERR_UNSUPPORTED. A RAW
+ * stream is multiplied directly from its verbatim values. The workspace must
+ * be at least enc_gemm_workspace_bytes(M, K, N, block_size) bytes; its
+ * contents need no initialisation. When the K dimension is split, a second
+ * kernel on the same stream adds the fp32 partial slices in K order, so the
+ * result is deterministic; calls sharing one workspace must not overlap.
+ * Accumulation is fp32. Asynchronous; allocates nothing. */
 enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
                                const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
                                uint64_t ws_bytes, void *stream);

@@ -402,8 +402,7 @@ static enc_status gemm_common(const uint16_t *d_x, uint32_t M, uint32_t K, uint3
   a->K = K;
   a->N = N;
   gemm_plan(M, K, N, &a->ksplit, &a->krows);
-  a->counters = static_cast<uint32_t *>(d_ws);
-  a->partial = reinterpret_cast<float *>(static_cast<uint8_t *>(d_ws) + kSectionAlign * 64);
+  a->partial = static_cast<float *>(d_ws);
   return ENC_OK;
 }
 

@@ -93,8 +93,7 @@ struct GemmArgs {
   const uint8_t *wstream;  // compressed W stream (nullptr for dense)
   const uint16_t *wdense;  // dense W [K, N] bf16 (RAW stream data or dense GEMM)
   float *y;                // Y [M, N] fp32
-  float *partial;          // [ksplit, M, N] split-K partial sums
-  uint32_t *counters;      // per output tile arrival counters (zero between calls)
+  float *partial;          // [ksplit, M, N] split-K partial sums (workspace)
   uint32_t M, K, N;
   uint32_t log2b;
   uint64_t nb;

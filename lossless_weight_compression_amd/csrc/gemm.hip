@@ -131,67 +131,65 @@ __device__ __forceinline__ uint4 decode_raw(const GroupRaw &r) {
   return join_group(lo, hi, w, base4, r.sml, r.smh);
 }
 
-// Split-K epilogue shared by both kernels: the workgroup's fp32 tile
-// `vals(i)` for i in [0, count) maps to Y element ymap(i) (-1 = none). With
-// one K range it writes Y. Otherwise, in one launch:
-//  1. the partial slice is written with agent-scope stores (global_store sc1:
-//     written through this XCD's L2 to the device-coherent level);
-//  2. s_waitcnt vmcnt(0) waits until every one of those stores is
-//     acknowledged, then the workgroup barrier;
-//  3. one agent-scope atomic add counts the workgroup in;
-//  4. the workgroup that sees the count reach ksplit - 1 reads all slices with
-//     agent-scope loads (global_load sc1, never served by a stale line of its
-//     own L2), adds them in K order -- deterministic -- writes Y and resets
-//     the counter for the next call.
-// No __threadfence(): on gfx950 an agent-scope release fence writes back the
-// whole XCD L2 (buffer_wbl2), which measured as the dominant cost of this
-// kernel when every workgroup issued one. Nothing here relies on L2
-// write-back: the only cross-workgroup data is written through.
-template <class Vals, class YMap>
-__device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t tile_id, uint32_t ks,
-                                              uint32_t count, Vals vals, YMap ymap) {
-  __shared__ uint32_t s_last;
-  const uint32_t tid = threadIdx.x;
-  if (a.ksplit == 1) {
-    for (uint32_t i = tid; i < count; i += blockDim.x) {
-      const int64_t y = ymap(i);
-      if (y >= 0) a.y[y] = vals(i);
-    }
-    return;
-  }
-  const uint64_t MN = (uint64_t)a.M * a.N;
-  for (uint32_t i = tid; i < count; i += blockDim.x) {
-    const int64_t y = ymap(i);
-    if (y >= 0)
-      __hip_atomic_store(a.partial + (uint64_t)ks * MN + (uint64_t)y, vals(i), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0)
-    s_last = (__hip_atomic_fetch_add(&a.counters[tile_id], 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) == a.ksplit - 1) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  for (uint32_t i = tid; i < count; i += blockDim.x) {
-    const int64_t y = ymap(i);
-    if (y < 0) continue;
-    const float *p = a.partial + (uint64_t)y;
-    float sum = 0.f;
+// Split-K epilogue shared by all kernels. for_each(fn) calls fn(y_index,
+// value) for every value this thread holds (y_index < 0: no output); it is
+// unrolled by the caller, so accumulator registers are never indexed
+// dynamically. With one K range the values go to Y; otherwise to this
+// range's slice of the partial buffer, which k_splitk_reduce (the next
+// launch on the stream) adds up in K order -- deterministic, and every CU
+// takes part in the reduction. (Letting the last workgroup of a tile add
+// the slices needs no second launch, but that one workgroup then streams
+// all slices of its tile alone: up to 512 KB through one CU.)
+template <class ForEach>
+__device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t ks, ForEach for_each) {
+  float *dst = a.ksplit == 1 ? a.y : a.partial + (uint64_t)ks * a.M * a.N;
+  for_each([&](int64_t y, float v) {
+    if (y >= 0) dst[y] = v;
+  });
+}
+
+// Y[i] = sum over K ranges of partial[k][i], k ascending; four outputs per
+// thread per iteration, the slices' loads in flight together.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ partial,
+                                                       float *__restrict__ y, uint64_t mn,
+                                                       uint32_t ksplit) {
+  const uint64_t n4 = mn / 4;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (uint64_t)gridDim.x * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     uint32_t k = 0;
-    for (; k + 16 <= a.ksplit; k += 16) {   // sixteen loads in flight, added in K order
-      float v[16];
+    for (; k + 8 <= ksplit; k += 8) {
+      float4 v[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        v[j] = __hip_atomic_load(p + (uint64_t)(k + j) * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const float4 *>(partial + (uint64_t)(k + j) * mn)[i];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sum += v[j];
+      for (int j = 0; j < 8; ++j) {
+        acc.x += v[j].x;
+        acc.y += v[j].y;
+        acc.z += v[j].z;
+        acc.w += v[j].w;
+      }
     }
-    for (; k < a.ksplit; ++k)
-      sum += __hip_atomic_load(p + (uint64_t)k * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.y[y] = sum;
+    for (; k < ksplit; ++k) {
+      const float4 v = reinterpret_cast<const float4 *>(partial + (uint64_t)k * mn)[i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    reinterpret_cast<float4 *>(y)[i] = acc;
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The VALU kernels' strip result sits in LDS (red[m * 512 + col]).
+template <int MM>
+__device__ __forceinline__ void strip_finish(const GemmArgs &a, uint32_t c, uint32_t ks,
+                                             const float *red) {
+  const uint64_t col0 = (uint64_t)c * kStrip;
+  splitk_finish(a, ks, [&](auto fn) {
+    for (uint32_t i = threadIdx.x; i < MM * kStrip; i += blockDim.x)
+      fn((int64_t)(i / kStrip) * a.N + (int64_t)col0 + (i % kStrip), red[i]);
+  });
 }
 
 // --------------------------------------------------------------------------
@@ -288,9 +286,7 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
     }
     __syncthreads();
   }
-  splitk_finish(
-      a, c, ks, MM * kStrip, [&](uint32_t i) { return red[i]; },
-      [&](uint32_t i) -> int64_t { return (int64_t)(i / kStrip) * N + (int64_t)col0 + (i % kStrip); });
+  strip_finish<MM>(a, c, ks, red);
 }
 
 // --------------------------------------------------------------------------
@@ -321,7 +317,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t *s, 
 template <int MM>
 __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
   constexpr uint32_t RW = kRowsPerWaveU;
-  constexpr uint32_t RB = MM <= 4 ? 8 : 4;       // rows per batch; two batches in flight
+  constexpr uint32_t RB = 4;                      // rows per batch; two batches in flight
   __shared__ float red[MM * kStrip];
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -362,19 +358,20 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
     u32x2 sm[RB];
     u32x3 q[RB];
   };
+  // Loads are issued unconditionally from a clamped row (see k_gemm_mfmau):
+  // loads under branches would make the next batch's prefetch block the
+  // current batch's decode.
   auto load_batch = [&](uint32_t r0, Batch &bt) {
 #pragma unroll
     for (uint32_t j = 0; j < RB; ++j) {
-      const uint32_t r = r0 + j;
-      if (r < nrows) {
-        const uint32_t off = __builtin_amdgcn_readlane(r_off, r);
-        const uint32_t meta = __builtin_amdgcn_readlane(r_meta, r);
-        const uint32_t w = (meta >> 8) & 15u;
-        const uint32_t pb = off + ((meta >> 16) + lane) * w;
-        const uint32_t row_sm = kHeaderBytes + (kw0 + r) * N + col0;   // uniform
-        bt.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, row_sm, 0);
-        bt.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
-      }
+      const uint32_t r = min(r0 + j, nrows - 1);
+      const uint32_t off = __builtin_amdgcn_readlane(r_off, r);
+      const uint32_t meta = __builtin_amdgcn_readlane(r_meta, r);
+      const uint32_t w = (meta >> 8) & 15u;
+      const uint32_t pb = off + ((meta >> 16) + lane) * w;
+      const uint32_t row_sm = kHeaderBytes + (kw0 + r) * N + col0;   // uniform
+      bt.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, row_sm, 0);
+      bt.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
     }
   };
   auto compute_batch = [&](uint32_t r0, const Batch &bt) {
@@ -384,21 +381,19 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
       if (r < nrows) {
         const uint32_t off = __builtin_amdgcn_readlane(r_off, r);
         const uint32_t meta = __builtin_amdgcn_readlane(r_meta, r);
-        const uint32_t w = (meta >> 8) & 15u;
+        const uint32_t w = (meta >> 8) & 15u;           // wave-uniform
         const uint32_t base4 = (meta & 0xFFu) * 0x01010101u;
-        const uint32_t sh = ((off + ((meta >> 16) + lane) * w) & 3u) * 8;
-        const uint32_t lo = __builtin_amdgcn_alignbit(bt.q[j].y, bt.q[j].x, sh);
-        const uint32_t hi = __builtin_amdgcn_alignbit(bt.q[j].z, bt.q[j].y, sh);
-        const uint32_t mid = (w == 8) ? hi : __builtin_amdgcn_alignbit(hi, lo, 4 * w);
-        const uint32_t w2 = w + w, w3 = w2 + w;
-        uint32_t el = __builtin_amdgcn_ubfe(lo, 0, w);
-        el |= __builtin_amdgcn_ubfe(lo, w, w) << 8;
-        el |= __builtin_amdgcn_ubfe(lo, w2, w) << 16;
-        el |= __builtin_amdgcn_ubfe(lo, w3, w) << 24;
-        uint32_t eh = __builtin_amdgcn_ubfe(mid, 0, w);
-        eh |= __builtin_amdgcn_ubfe(mid, w, w) << 8;
-        eh |= __builtin_amdgcn_ubfe(mid, w2, w) << 16;
-        eh |= __builtin_amdgcn_ubfe(mid, w3, w) << 24;
+        uint32_t el, eh;
+        if (w == 4) {
+          // block payloads start on 16-byte boundaries, so a 4-byte group
+          // is dword-aligned: its codes are exactly q.x
+          codes_to_bytes_w4(bt.q[j].x, el, eh);
+        } else {
+          const uint32_t sh = ((off + ((meta >> 16) + lane) * w) & 3u) * 8;
+          const uint32_t lo = __builtin_amdgcn_alignbit(bt.q[j].y, bt.q[j].x, sh);
+          const uint32_t hi = __builtin_amdgcn_alignbit(bt.q[j].z, bt.q[j].y, sh);
+          codes_to_bytes(lo, hi, w, el, eh);
+        }
         el += base4;
         eh += base4;
         const uint32_t sml = bt.sm[j].x, smh = bt.sm[j].y;
@@ -445,9 +440,7 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
     }
     __syncthreads();
   }
-  splitk_finish(
-      a, c, ks, MM * kStrip, [&](uint32_t i) { return red[i]; },
-      [&](uint32_t i) -> int64_t { return (int64_t)(i / kStrip) * N + (int64_t)col0 + (i % kStrip); });
+  strip_finish<MM>(a, c, ks, red);
 }
 
 // --------------------------------------------------------------------------
@@ -560,34 +553,208 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
     __syncthreads();
   }
 
-  // results: lane holds D[4 (lane >> 4) + j][lane & 15] of each 16x16 subtile;
-  // stage through LDS (reuse the X tile area is too small: use a flat float view
-  // of registers instead) -> write directly with the split-K epilogue.
-  const uint32_t tile_id = mt * (N / kTileN) + nt;
-  splitk_finish(
-      a, tile_id, ks, MT * kTileN,
-      [&](uint32_t i) -> float {
-        // i enumerates this thread's own values only (see ymap)
-        const uint32_t idx = i / 256;            // 0 .. MSUB*2*4-1
-        const uint32_t t = idx / 8, s = (idx / 4) & 1, j = idx & 3;
-        float v = 0.f;
+  // lane holds D[4 (lane >> 4) + j][lane & 15] of each 16x16 subtile
+  splitk_finish(a, ks, [&](auto fn) {
 #pragma unroll
-        for (int tt = 0; tt < MSUB; ++tt)
+    for (int t = 0; t < MSUB; ++t)
 #pragma unroll
-          for (int ss = 0; ss < 2; ++ss)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              if ((uint32_t)tt == t && (uint32_t)ss == s && (uint32_t)jj == j) v = acc[tt][ss][jj];
-        return v;
-      },
-      [&](uint32_t i) -> int64_t {
-        const uint32_t idx = i / 256;
-        const uint32_t t = idx / 8, s = (idx / 4) & 1, j = idx & 3;
-        const uint32_t m = m0 + 16 * t + 4 * (lane >> 4) + j;
-        const uint32_t n = n0 + 32 * wave + 16 * s + (lane & 15);
-        if (m >= M) return -1;
-        return (int64_t)m * N + n;
-      });
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t m = m0 + 16 * t + 4 * (lane >> 4) + j;
+          const uint32_t n = n0 + 32 * wave + 16 * s2 + (lane & 15);
+          fn(m < M ? (int64_t)m * N + n : (int64_t)-1, acc[t][s2][j]);
+        }
+  });
+}
+
+// --------------------------------------------------------------------------
+// M >= 16 and B >= 512 (or dense W): MFMA on wave-uniform rows.
+//
+// Output tile MT x 512 (one strip) per workgroup of WAVES waves, split over
+// K ranges. Per K step of 32 rows, wave w decodes rows [w*RPW, w*RPW + RPW)
+// of the step over the full 512 columns (lane: 8 columns; width, base and
+// block offset wave-uniform as in k_gemm_rowu), two rows at a time, and
+// writes k-pair dwords (W[k][n] | W[k+1][n] << 16) into an LDS tile of
+// 16 k-pairs x 516 dwords. The 4-dword pad makes the MFMA B-fragment reads
+// (4 x ds_read_b32: k-pairs 4*(lane/16)+p, column lane%16) hit distinct banks
+// for 32- and 64-bank LDS alike. Two tiles alternate, so one barrier per step
+// separates a step's decode from its MFMAs; the next step's compressed bytes
+// and X fragments are loaded before the current step is decoded.
+// v_mfma_f32_16x16x32_bf16: A fragment = 8 consecutive k of one X row (one
+// 16-byte load), D = 4 rows x 1 column per lane.
+// --------------------------------------------------------------------------
+constexpr uint32_t kPitchU = 516;
+
+// Workgroup barrier for LDS hand-off only. __syncthreads() also fences
+// global memory, so the compiler waits for every outstanding global load
+// (vmcnt 0) first -- including the next K step's prefetched loads, which
+// would serialise each step on a full memory round trip. Here only this
+// wave's LDS operations are waited for; the "memory" clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// M tile of k_gemm_mfmau: 128 rows would not fit the accumulators and the
+// double-buffered loads in 256 registers, so larger M uses several 64-row tiles.
+uint32_t mfmau_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
+
+template <int MT, int WAVES, bool DENSE>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
+  constexpr uint32_t RPW = 32 / WAVES;          // rows decoded per wave per step
+  constexpr uint32_t NSUB = 32 / WAVES;         // 16-column subtiles per wave
+  constexpr uint32_t MSUB = MT / 16;
+  constexpr uint32_t NTHR = WAVES * 64;
+  static_assert(RPW % 2 == 0, "rows are decoded in pairs");
+  __shared__ __attribute__((aligned(16))) uint32_t tile[2][16 * kPitchU];
+  __shared__ uint32_t tbl_off[1024], tbl_meta[1024];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const uint32_t c = blockIdx.x, ks = blockIdx.y, mt = blockIdx.z;
+  const uint32_t N = a.N, K = a.K, M = a.M, log2b = a.log2b;
+  const uint32_t k0 = ks * a.krows;
+  const uint32_t k1 = min(k0 + a.krows, K);
+  const uint32_t nsteps = (k1 - k0 + 31) / 32;
+  const uint32_t col0 = c * kStrip, m0 = mt * MT;
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
+
+  if (!DENSE) {
+    for (uint32_t r = tid; r < k1 - k0; r += NTHR) {
+      const uint64_t e = (uint64_t)(k0 + r) * N + col0;
+      uint64_t off, mw;
+      row_block<false>(a, e >> log2b, off, mw);
+      uint32_t w = (uint32_t)(mw >> 8) & 0xFFu;
+      if (w > 8) w = 0;   // corrupted stream: decode as width 0
+      tbl_off[r] = (uint32_t)off;
+      tbl_meta[r] = ((uint32_t)mw & 0xFFu) | (w << 8) |
+                    ((uint32_t)((e & ((1ull << log2b) - 1)) >> 3) << 16);
+    }
+    __syncthreads();
+  }
+
+  struct Step {
+    u32x2 sm[RPW];
+    u32x3 q[RPW];
+    uint4 dv[RPW];
+    uint4 x[MSUB];
+  };
+  // Every load is issued unconditionally, from a clamped (always valid) row
+  // or X element; out-of-range data is discarded after the load. Loads under
+  // branches would make the compiler wait for all outstanding loads (vmcnt 0)
+  // before the decode, i.e. also for the next step's prefetch.
+  auto load_step = [&](uint32_t st, Step &S) {
+    const uint32_t kb = k0 + 32 * st;
+#pragma unroll
+    for (uint32_t j = 0; j < RPW; ++j) {
+      const uint32_t kr = min(kb + wave * RPW + j, k1 - 1);
+      if (DENSE) {
+        S.dv[j] = *reinterpret_cast<const uint4 *>(a.wdense + (uint64_t)kr * N + col0 + 8 * lane);
+      } else {
+        const uint32_t off = __builtin_amdgcn_readfirstlane(tbl_off[kr - k0]);
+        const uint32_t meta = __builtin_amdgcn_readfirstlane(tbl_meta[kr - k0]);
+        const uint32_t w = (meta >> 8) & 15u;
+        const uint32_t pb = off + ((meta >> 16) + lane) * w;
+        S.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, kHeaderBytes + kr * N + col0, 0);
+        S.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
+      }
+    }
+    const uint32_t kx = kb + 8 * (lane >> 4);
+#pragma unroll
+    for (uint32_t mi = 0; mi < MSUB; ++mi) {
+      const uint32_t m = m0 + 16 * mi + (lane & 15);
+      const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K +
+                                                       min(kx, k1 - 8));
+      const bool in = m < M && kx < k1;
+      S.x[mi] = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
+    }
+  };
+  auto decode_row = [&](uint32_t st, const Step &S, uint32_t j) -> uint4 {
+    const uint32_t kr = k0 + 32 * st + wave * RPW + j;   // uniform
+    if (kr >= k1) return make_uint4(0, 0, 0, 0);
+    if (DENSE) return S.dv[j];
+    const uint32_t off = __builtin_amdgcn_readfirstlane(tbl_off[kr - k0]);
+    const uint32_t meta = __builtin_amdgcn_readfirstlane(tbl_meta[kr - k0]);
+    const uint32_t w = (meta >> 8) & 15u;           // wave-uniform
+    uint32_t el, eh;
+    if (w == 4) {
+      codes_to_bytes_w4(S.q[j].x, el, eh);          // dword-aligned, see k_gemm_rowu
+    } else {
+      const uint32_t sh = ((off + ((meta >> 16) + lane) * w) & 3u) * 8;
+      const uint32_t lo = __builtin_amdgcn_alignbit(S.q[j].y, S.q[j].x, sh);
+      const uint32_t hi = __builtin_amdgcn_alignbit(S.q[j].z, S.q[j].y, sh);
+      codes_to_bytes(lo, hi, w, el, eh);
+    }
+    return bytes_to_bf16(el, eh, (meta & 0xFFu) * 0x01010101u, S.sm[j].x, S.sm[j].y);
+  };
+  auto decode_step = [&](uint32_t st, const Step &S, uint32_t buf) {
+#pragma unroll
+    for (uint32_t j = 0; j < RPW; j += 2) {
+      const uint4 ra = decode_row(st, S, j), rb = decode_row(st, S, j + 1);
+      uint4 lo4, hi4;   // k-pairs of columns 0..3 and 4..7 of this lane
+      lo4.x = __builtin_amdgcn_perm(rb.x, ra.x, 0x05040100u);
+      lo4.y = __builtin_amdgcn_perm(rb.x, ra.x, 0x07060302u);
+      lo4.z = __builtin_amdgcn_perm(rb.y, ra.y, 0x05040100u);
+      lo4.w = __builtin_amdgcn_perm(rb.y, ra.y, 0x07060302u);
+      hi4.x = __builtin_amdgcn_perm(rb.z, ra.z, 0x05040100u);
+      hi4.y = __builtin_amdgcn_perm(rb.z, ra.z, 0x07060302u);
+      hi4.z = __builtin_amdgcn_perm(rb.w, ra.w, 0x05040100u);
+      hi4.w = __builtin_amdgcn_perm(rb.w, ra.w, 0x07060302u);
+      uint32_t *dst = &tile[buf][(wave * RPW + j) / 2 * kPitchU + 8 * lane];
+      *reinterpret_cast<uint4 *>(dst) = lo4;
+      *reinterpret_cast<uint4 *>(dst + 4) = hi4;
+    }
+  };
+  f32x4 acc[MSUB][NSUB];
+#pragma unroll
+  for (uint32_t mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+    for (uint32_t ns = 0; ns < NSUB; ++ns) acc[mi][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mfma_step = [&](uint32_t buf, const Step &S) {
+    const uint32_t kq = 4 * (lane >> 4);
+#pragma unroll
+    for (uint32_t ns = 0; ns < NSUB; ++ns) {
+      const uint32_t n = wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
+      uint4 bw;
+      bw.x = tile[buf][(kq + 0) * kPitchU + n];
+      bw.y = tile[buf][(kq + 1) * kPitchU + n];
+      bw.z = tile[buf][(kq + 2) * kPitchU + n];
+      bw.w = tile[buf][(kq + 3) * kPitchU + n];
+      const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+      for (uint32_t mi = 0; mi < MSUB; ++mi)
+        acc[mi][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, S.x[mi]), b,
+                                                               acc[mi][ns], 0, 0, 0);
+    }
+  };
+
+  Step SA, SB;
+  if (nsteps) load_step(0, SA);
+  for (uint32_t st = 0; st < nsteps; st += 2) {
+    if (st + 1 < nsteps) load_step(st + 1, SB);
+    decode_step(st, SA, 0);
+    lds_barrier();
+    mfma_step(0, SA);
+    if (st + 1 < nsteps) {
+      if (st + 2 < nsteps) load_step(st + 2, SA);
+      decode_step(st + 1, SB, 1);
+      lds_barrier();
+      mfma_step(1, SB);
+    }
+  }
+
+  splitk_finish(a, ks, [&](auto fn) {
+#pragma unroll
+    for (uint32_t mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+      for (uint32_t ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j) {
+          const uint32_t m = m0 + 16 * mi + 4 * (lane >> 4) + j;
+          const uint32_t n = col0 + wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
+          fn(m < M ? (int64_t)m * N + n : (int64_t)-1, acc[mi][ns][j]);
+        }
+  });
 }
 
 template <bool DENSE>
@@ -617,6 +784,18 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool DENSE>
+hipError_t launch_mfmau(const GemmArgs &a, hipStream_t s) {
+  const uint32_t MT = mfmau_tile_m(a.M);
+  const dim3 grid(a.N / kStrip, a.ksplit, (a.M + MT - 1) / MT);
+  switch (MT) {
+    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, 4, DENSE>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, 4, DENSE>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfmau<64, 8, DENSE>), grid, dim3(512), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 uint32_t mfma_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 template <bool DENSE>
@@ -636,11 +815,14 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
 
 // Which kernel serves a call: 0 = generic VALU (M < 16), 1 = uniform-row VALU
 // (M < 16, compressed, B >= 512, stream below 2 GiB: 32-bit buffer offsets),
-// 2 = MFMA (M >= 16).
+// 2 = generic MFMA (M >= 16, B < 512), 3 = uniform-row MFMA (M >= 16, dense
+// W or B >= 512).
 uint32_t gemm_kind(uint32_t M, bool dense, uint32_t log2b, uint64_t total) {
-  if (M >= 16) return 2;
-  return (!dense && log2b >= 9 && total < (1ull << 31)) ? 1 : 0;
+  const bool uniform = dense || (log2b >= 9 && total < (1ull << 31));
+  if (M >= 16) return uniform ? 3 : 2;
+  return (!dense && uniform) ? 1 : 0;
 }
+
 
 void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit,
                     uint32_t *krows) {
@@ -652,16 +834,26 @@ void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t 
   }
   // enough workgroups to cover the CUs; at most 1024 rows per K range (the
   // per-row block offsets are kept in LDS), at least 64
-  const uint32_t MT = mfma_tile_m(M);
-  const uint64_t tiles = (uint64_t)(N / kTileN) * ((M + MT - 1) / MT);
-  const uint64_t target = M <= 32 ? 512 : 256;
-  uint64_t ks = (target + tiles - 1) / tiles;
+  const uint32_t MT = kind == 3 ? mfmau_tile_m(M) : mfma_tile_m(M);
+  const uint32_t ncol = kind == 3 ? kStrip : kTileN;
+  const uint64_t tiles = (uint64_t)(N / ncol) * ((M + MT - 1) / MT);
+  uint64_t ks;
+  if (kind == 3) {
+    // Resident k_gemm_mfmau workgroups: ~74 KB of LDS allows two per CU;
+    // the 8-wave 64-row variant needs ~170 registers per lane, one per CU.
+    // Fill the slots in one round: a partial second round doubles the time.
+    const uint64_t slots = MT == 64 ? 256 : 512;
+    ks = tiles >= slots ? 1 : slots / tiles;
+  } else {
+    const uint64_t target = M <= 32 ? 512 : 256;
+    ks = (target + tiles - 1) / tiles;
+  }
   const uint64_t ks_min = (K + 1023) / 1024, ks_max = (K + 63) / 64;
   if (ks < ks_min) ks = ks_min;
   if (ks > ks_max) ks = ks_max;
   if (ks < 1) ks = 1;
   uint32_t rows = (uint32_t)((K + ks - 1) / ks);
-  rows = (rows + kKStep - 1) / kKStep * kKStep;
+  rows = (rows + kKStep - 1) / kKStep * kKStep;   // never increases the range count
   *krows = rows;
   *ksplit = (K + rows - 1) / rows;
 }
@@ -670,21 +862,17 @@ void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *k
   gemm_plan_kind(M >= 16 ? 2 : 0, M, K, N, ksplit, krows);
 }
 
-static uint64_t counter_slots(uint32_t M, uint32_t N) {
-  return M < 16 ? N / kStrip : (uint64_t)(N / kTileN) * ((M + 127) / 16 + 1);
-}
-
 uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
-  // enough for whichever kernel the call selects
-  uint64_t most = 0;
-  for (uint32_t kind = 0; kind < 3; ++kind) {
-    if ((kind == 2) != (M >= 16)) continue;
+  // the split-K partial slices of whichever kernel the call selects
+  uint64_t most = 256;
+  for (uint32_t kind = 0; kind < 4; ++kind) {
+    if ((kind >= 2) != (M >= 16)) continue;
     uint32_t ks, kr;
     gemm_plan_kind(kind, M, K, N, &ks, &kr);
     const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
     if (partial > most) most = partial;
   }
-  return align_up(4 * counter_slots(M, N), 256) + most;
+  return most;
 }
 
 hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
@@ -692,11 +880,22 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
   const bool dense = a.wstream == nullptr;
   const uint32_t kind = gemm_kind(a.M, dense, a.log2b, a.total);
   gemm_plan_kind(kind, a.M, a.K, a.N, &a.ksplit, &a.krows);
-  a.partial = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(a.counters) +
-                                        align_up(4ull * counter_slots(a.M, a.N), 256));
-  if (kind == 1) return launch_rowu(a, s);
-  if (kind == 0) return dense ? launch_valu<true>(a, s) : launch_valu<false>(a, s);
-  return dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
+  hipError_t e;
+  if (kind == 1)
+    e = launch_rowu(a, s);
+  else if (kind == 0)
+    e = dense ? launch_valu<true>(a, s) : launch_valu<false>(a, s);
+  else if (kind == 3)
+    e = dense ? launch_mfmau<true>(a, s) : launch_mfmau<false>(a, s);
+  else
+    e = dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const uint64_t mn = (uint64_t)a.M * a.N;
+  uint64_t blocks = (mn / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((uint32_t)blocks), dim3(256), 0, s, a.partial, a.y, mn,
+                     a.ksplit);
+  return hipGetLastError();
 }
 
 }  // namespace enc

@@ -201,9 +201,9 @@ def enc_gemm_workspace_bytes(M, K, N, block_size=512):
 
 
 def gemm_workspace(M, K, N, block_size=512, device="cuda"):
-    """A zero-filled workspace for the GEMM entry points (zero on first use)."""
+    """A workspace for the GEMM entry points (contents need no initialisation)."""
     import torch
-    return torch.zeros(max(enc_gemm_workspace_bytes(M, K, N, block_size), 16), dtype=torch.uint8,
+    return torch.empty(max(enc_gemm_workspace_bytes(M, K, N, block_size), 16), dtype=torch.uint8,
                        device=device)
 
 
