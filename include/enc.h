@@ -33,7 +33,7 @@
  *   RAW streams (flags bit 0): header, then the n input values verbatim at
  *   raw_off = 256; chosen when the coded stream would not be smaller.
  *   A stream is valid only if every decoded exponent base + code is <= 255
- *   (always true for streams this library or the reference encoder wrote).
+ *   (always true for a stream written from BF16 input by these rules).
  *
  * Conventions for every entry point:
  *  - d_ pointers are device (HBM) pointers, h_ pointers are host pointers.
@@ -87,7 +87,8 @@ uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size);
  * kernel, the scan of segment sizes and the pack kernel on `stream`; then
  * synchronises `stream` once to read back the stream size (the only blocking
  * point of the library), and fills *h_info. The bytes written are exactly
- * those of the reference encoder for the same input. out_capacity must be
+ * the ones the format above prescribes (the stream is unique for a given
+ * input and block size). out_capacity must be
  * at least the final stream size (enc_compress_bound(n) always suffices). */
 enc_status enc_compress(const uint16_t *d_in, uint64_t n_elems, uint32_t block_size, void *d_out,
                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream,
