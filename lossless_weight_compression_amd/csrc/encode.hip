@@ -16,8 +16,8 @@
 //                   bits are zero) and written out with 16-byte stores; the
 //                   sign+mantissa plane is written directly;
 //  4. k_enc_finish  header, meta and segment-offset sections, section padding.
-// The bytes are exactly those of the format definition, so streams match the
-// reference encoder byte for byte.
+// The bytes are exactly those the format definition prescribes (the stream
+// is unique for a given input and block size).
 #include "enc_common.h"
 
 namespace enc {
