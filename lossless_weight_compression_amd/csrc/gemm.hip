@@ -148,36 +148,26 @@ __device__ __forceinline__ void splitk_finish(const GemmArgs &a, uint32_t ks, Fo
   });
 }
 
-// Y[i] = sum over K ranges of partial[k][i], k ascending; four outputs per
-// thread per iteration, the slices' loads in flight together.
+// Y[i] = sum over K ranges of partial[k][i], k ascending. One output per
+// thread and CH (>= ksplit when ksplit <= 32) slices' loads in flight at
+// once: the reduction is a few MB at most, so it is latency-bound and wants
+// one round trip, not a chain.
+template <uint32_t CH>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ partial,
                                                        float *__restrict__ y, uint64_t mn,
                                                        uint32_t ksplit) {
-  const uint64_t n4 = mn / 4;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn;
        i += (uint64_t)gridDim.x * blockDim.x) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    uint32_t k = 0;
-    for (; k + 8 <= ksplit; k += 8) {
-      float4 v[8];
+    float sum = 0.f;
+    for (uint32_t k = 0; k < ksplit; k += CH) {
+      float v[CH];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const float4 *>(partial + (uint64_t)(k + j) * mn)[i];
+      for (uint32_t j = 0; j < CH; ++j)   // unconditional (clamped) loads, masked after
+        v[j] = partial[(uint64_t)min(k + j, ksplit - 1) * mn + i];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc.x += v[j].x;
-        acc.y += v[j].y;
-        acc.z += v[j].z;
-        acc.w += v[j].w;
-      }
+      for (uint32_t j = 0; j < CH; ++j) sum += k + j < ksplit ? v[j] : 0.f;
     }
-    for (; k < ksplit; ++k) {
-      const float4 v = reinterpret_cast<const float4 *>(partial + (uint64_t)k * mn)[i];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
-    reinterpret_cast<float4 *>(y)[i] = acc;
+    y[i] = sum;
   }
 }
 
@@ -891,10 +881,17 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
     e = dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
   if (e != hipSuccess || a.ksplit == 1) return e;
   const uint64_t mn = (uint64_t)a.M * a.N;
-  uint64_t blocks = (mn / 4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_splitk_reduce, dim3((uint32_t)blocks), dim3(256), 0, s, a.partial, a.y, mn,
-                     a.ksplit);
+  uint64_t blocks = (mn + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  const dim3 g((uint32_t)blocks), t(256);
+  if (a.ksplit <= 4)
+    hipLaunchKernelGGL(k_splitk_reduce<4>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  else if (a.ksplit <= 8)
+    hipLaunchKernelGGL(k_splitk_reduce<8>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  else if (a.ksplit <= 16)
+    hipLaunchKernelGGL(k_splitk_reduce<16>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<32>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
   return hipGetLastError();
 }
 
