@@ -47,6 +47,10 @@
  *  - Every entry point checks its arguments on the host before launching
  *    anything; failures return a negative enc_status and set a thread-local
  *    message readable with enc_last_error(). Nothing is launched on failure.
+ *  - With the environment variable ENC_DEBUG_SYNC set (to anything but "" or
+ *    "0"), the asynchronous entry points synchronise their stream after
+ *    launching (except while it is being captured into a graph), so a kernel
+ *    fault is returned as ENC_ERR_HIP by the call that caused it.
  */
 #ifndef ENC_H
 #define ENC_H
@@ -158,6 +162,34 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
  * with. Same workspace rules, with block_size 512. */
 enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
                           uint32_t N, float *d_y, void *d_ws, uint64_t ws_bytes, void *stream);
+
+/* Deep check of a stream's device data (the header is checked on the host
+ * by enc_parse_header / enc_read_info). In this order of precedence:
+ *   ENC_CHECK_WIDTH    some block width is above 8;
+ *   ENC_CHECK_OFFSETS  a stored segment offset differs from the exclusive
+ *                      prefix sum of the padded block payload sizes, or
+ *                      payload_bytes differs from their total (ENEC
+ *                      Abstract: block offsets come from a prefix scan);
+ *   ENC_CHECK_EXPONENT some base + code exceeds 255 (the transform subtracts
+ *                      the block minimum, so a valid code never does).
+ * index = the first failing block (width, exponent) or the first wrong stored
+ * offset (offsets; index n_segments stands for payload_bytes). A RAW stream
+ * has no device structure and always passes. d_ws: device workspace of at
+ * least enc_validate_workspace_bytes() bytes, 16-byte aligned. Synchronous
+ * on `stream` (so it cannot be captured in a graph). Returns ENC_OK, or
+ * ENC_ERR_BAD_STREAM with *h_check (may be NULL) naming the failure.
+ * Decoding never reads outside a stream, valid or not; this check says
+ * whether its output is meaningful. */
+enum { ENC_CHECK_OK = 0, ENC_CHECK_WIDTH = 1, ENC_CHECK_OFFSETS = 2, ENC_CHECK_EXPONENT = 3 };
+typedef struct enc_check {
+  uint32_t kind;     /* ENC_CHECK_* */
+  uint32_t reserved; /* 0 */
+  uint64_t index;    /* first failing block or stored offset */
+} enc_check;
+
+uint64_t enc_validate_workspace_bytes(void);
+enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, uint64_t ws_bytes,
+                        void *stream, enc_check *h_check);
 
 /* Static text for a status code. */
 const char *enc_status_string(enc_status s);

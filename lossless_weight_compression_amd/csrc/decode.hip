@@ -102,13 +102,16 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
   }
   const uint32_t incl = wave_incl_scan(P, lane);
   pk |= incl - P;   // exclusive offset < 2^18
-  uint64_t seg_payload =
-      d.payload_off + *reinterpret_cast<const uint64_t *>(s + d.segoff_off + 8 * seg);
+  const uint64_t seg_rel = *reinterpret_cast<const uint64_t *>(s + d.segoff_off + 8 * seg);
+  uint64_t seg_payload = d.payload_off + seg_rel;
   // Guard against corrupted streams (checked once per wave, not per group):
   // a width above 8 or a segment whose payload runs past the stream end
-  // decodes as width 0, so no lane ever reads outside [0, total).
+  // decodes as width 0, so no lane ever reads outside [0, total). The test
+  // is written without sums that could wrap (payload_off <= total holds for
+  // every header the host accepts).
   const uint32_t seg_bytes = __shfl(incl, 63, 64);
-  if (__any((pk >> 20 & 15u) > 8) || seg_payload + seg_bytes > d.total) {
+  const uint64_t room = d.total - d.payload_off;
+  if (__any((pk >> 20 & 15u) > 8) || seg_rel > room || seg_bytes > room - seg_rel) {
     pk = 0;
     seg_payload = d.payload_off;
   }

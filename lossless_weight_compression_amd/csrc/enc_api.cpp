@@ -10,6 +10,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -34,6 +35,30 @@ enc_status hip_fail(hipError_t e, const char *what) {
 }
 
 void clear_err() { g_err[0] = 0; }
+
+// ENC_DEBUG_SYNC set to anything but "" or "0": every asynchronous entry
+// point synchronises its stream after its launches (unless the stream is
+// being captured into a graph), so a fault inside a kernel is reported by
+// the call that launched it. Read on every call, so it can be toggled.
+bool debug_sync() {
+  const char *v = getenv("ENC_DEBUG_SYNC");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+enc_status launched(hipError_t e, hipStream_t s, const char *what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (debug_sync()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_fail(e, "capture status query");
+    if (cs == hipStreamCaptureStatusNone) {
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess)
+        return fail(ENC_ERR_HIP, "%s, found by ENC_DEBUG_SYNC: %s", what, hipGetErrorString(e));
+    }
+  }
+  return ENC_OK;
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -186,8 +211,10 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
   if (n == 0) {
     if (out_capacity < raw_total) return fail(ENC_ERR_CAPACITY, "output capacity below 256");
     const enc_info i = raw_info(0, block_size);
-    hipError_t e = launch_encode_raw(d_in, static_cast<uint8_t *>(d_out), 0, header_of(i), s);
-    if (e != hipSuccess) return hip_fail(e, "raw header launch");
+    const enc_status st = launched(launch_encode_raw(d_in, static_cast<uint8_t *>(d_out), 0,
+                                                     header_of(i), s),
+                                   s, "raw header launch");
+    if (st != ENC_OK) return st;
     *h_info = i;
     return ENC_OK;
   }
@@ -229,8 +256,9 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
       return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
                   (unsigned long long)out_capacity, (unsigned long long)raw_total);
     i = raw_info(n, block_size);
-    e = launch_encode_raw(d_in, a.out, n, header_of(i), s);
-    if (e != hipSuccess) return hip_fail(e, "raw copy launch");
+    const enc_status st = launched(launch_encode_raw(d_in, a.out, n, header_of(i), s), s,
+                                   "raw copy launch");
+    if (st != ENC_OK) return st;
   } else {
     if (out_capacity < coded_total)
       return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
@@ -252,8 +280,9 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
     i.total_bytes = coded_total;
     e = launch_encode_pack(a, s);
     if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
-    e = launch_encode_finish(a, header_of(i), s);
-    if (e != hipSuccess) return hip_fail(e, "finish kernel launch");
+    const enc_status st = launched(launch_encode_finish(a, header_of(i), s), s,
+                                   "finish kernel launch");
+    if (st != ENC_OK) return st;
   }
   *h_info = i;
   return ENC_OK;
@@ -316,9 +345,8 @@ enc_status enc_decompress(const void *d_comp, const enc_info *h_info, uint16_t *
   if (!aligned16(d_comp) || !aligned16(d_out))
     return fail(ENC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   if (out_elems == 0) return ENC_OK;
-  const hipError_t e = launch_decode(desc_of(d_comp, *h_info, d_out), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return ENC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_decode(desc_of(d_comp, *h_info, d_out), s), s, "decode launch");
 }
 
 uint64_t enc_batch_table_bytes(int count) { return count < 0 ? 0 : batch_bytes(count); }
@@ -373,9 +401,8 @@ enc_status enc_decompress_batch(const void *d_table, int count, void *stream) {
   if (count < 0) return fail(ENC_ERR_INVALID_ARG, "negative count");
   if (!d_table || !aligned16(d_table)) return fail(ENC_ERR_INVALID_ARG, "d_table NULL or unaligned");
   if (count == 0) return ENC_OK;
-  const hipError_t e = launch_decode_batch(d_table, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "batch decode launch");
-  return ENC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_decode_batch(d_table, s), s, "batch decode launch");
 }
 
 uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size) {
@@ -434,9 +461,8 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
     a.payload_off = h_winfo->payload_off;
     a.total = h_winfo->total_bytes;
   }
-  const hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "GEMM launch");
-  return ENC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_gemm(a, s), s, "GEMM launch");
 }
 
 enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
@@ -447,8 +473,58 @@ enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uin
   const enc_status st = gemm_common(d_x, M, K, N, d_y, d_ws, ws_bytes, &a);
   if (st != ENC_OK) return st;
   a.wdense = d_w;
-  const hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_gemm(a, s), s, "GEMM launch");
+}
+
+uint64_t enc_validate_workspace_bytes(void) { return 256; }
+
+enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, uint64_t ws_bytes,
+                        void *stream, enc_check *h_check) {
+  clear_err();
+  enc_status st = check_info(h_info);
+  if (st != ENC_OK) return st;
+  if (!d_comp || !aligned16(d_comp)) return fail(ENC_ERR_INVALID_ARG, "d_comp NULL or unaligned");
+  if (h_check) memset(h_check, 0, sizeof *h_check);
+  if (h_info->flags == 1) return ENC_OK;   // RAW: the header is the whole structure
+  if (!d_ws || !aligned16(d_ws) || ws_bytes < enc_validate_workspace_bytes())
+    return fail(ENC_ERR_CAPACITY, "validation workspace of %llu bytes needed",
+                (unsigned long long)enc_validate_workspace_bytes());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ValidateArgs a;
+  memset(&a, 0, sizeof a);
+  a.stream = static_cast<const uint8_t *>(d_comp);
+  a.result = static_cast<unsigned long long *>(d_ws);
+  a.n = h_info->n_elems;
+  a.nb = h_info->n_blocks;
+  a.nseg = h_info->n_segments;
+  a.meta_off = h_info->meta_off;
+  a.segoff_off = h_info->segoff_off;
+  a.payload_off = h_info->payload_off;
+  a.payload_bytes = h_info->payload_bytes;
+  a.log2b = (uint32_t)log2_block(h_info->block_size);
+  hipError_t e = hipMemsetAsync(d_ws, 0xFF, 3 * sizeof(unsigned long long), s);
+  if (e != hipSuccess) return hip_fail(e, "result initialisation");
+  e = launch_validate(a, s);
+  if (e != hipSuccess) return hip_fail(e, "validation launch");
+  unsigned long long r[3];
+  e = hipMemcpyAsync(r, d_ws, sizeof r, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "result read-back");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  static const char *const what[3] = {"block %llu has a width above 8",
+                                      "stored segment offset %llu is not the prefix sum of the "
+                                      "block sizes (index n_segments = payload_bytes)",
+                                      "block %llu decodes an exponent above 255"};
+  for (int k = 0; k < 3; ++k) {
+    if (r[k] != ~0ull) {
+      if (h_check) {
+        h_check->kind = (uint32_t)(k + 1);
+        h_check->index = r[k];
+      }
+      return fail(ENC_ERR_BAD_STREAM, what[k], r[k]);
+    }
+  }
   return ENC_OK;
 }
 

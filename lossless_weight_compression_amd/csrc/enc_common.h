@@ -87,6 +87,16 @@ hipError_t launch_encode_finish(const EncodeArgs &a, const HeaderImage &h, hipSt
 hipError_t launch_encode_raw(const uint16_t *in, uint8_t *out, uint64_t n, const HeaderImage &h,
                              hipStream_t s);
 
+// ---- deep stream check ------------------------------------------------------
+struct ValidateArgs {
+  const uint8_t *stream;
+  unsigned long long *result;   // [3]: first failing block / offset per kind, ~0 = none
+  uint64_t n, nb, nseg;
+  uint64_t meta_off, segoff_off, payload_off, payload_bytes;
+  uint32_t log2b;
+};
+hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
+
 // ---- fused decompress-GEMM ------------------------------------------------
 struct GemmArgs {
   const uint16_t *x;       // X [M, K] bf16

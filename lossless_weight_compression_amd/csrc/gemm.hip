@@ -109,8 +109,9 @@ __device__ __forceinline__ GroupRaw load_group(const GemmArgs &a, uint64_t e, ui
   }
   uint32_t w = meta >> 8;
   // corrupted stream guard: a width above 8, or a block running past the
-  // stream end, decodes as width 0 (wrong values, but no stray reads)
-  if (w > 8 || blk_off + extra + ((uint64_t)w << (log2b - 3)) > a.total) w = 0;
+  // stream end, decodes as width 0 (wrong values, but no stray reads); no
+  // sum here can wrap, whatever the stored segment offset
+  if (w > 8 || blk_off > a.total || extra + ((uint64_t)w << (log2b - 3)) > a.total - blk_off) w = 0;
   const uint64_t pb = blk_off + extra + (uint64_t)u * w;
   const uint64_t sm_addr = kHeaderBytes + e + 8 * (uint64_t)g;
   const uint2 sm = *reinterpret_cast<const uint2 *>(s + sm_addr);

@@ -39,6 +39,18 @@ class EncInfo(ctypes.Structure):
         return "EncInfo(%s)" % ", ".join("%s=%s" % kv for kv in self.as_dict().items())
 
 
+CHECK_NAMES = {0: "ENC_CHECK_OK", 1: "ENC_CHECK_WIDTH", 2: "ENC_CHECK_OFFSETS",
+               3: "ENC_CHECK_EXPONENT"}
+
+
+class EncCheck(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("index", ctypes.c_uint64)]
+
+    def __repr__(self):
+        return "EncCheck(%s, index=%d)" % (CHECK_NAMES.get(self.kind, "?"), self.index)
+
+
 class EncItem(ctypes.Structure):
     _fields_ = [("d_comp", ctypes.c_void_p), ("d_out", ctypes.c_void_p), ("info", EncInfo)]
 
@@ -63,6 +75,8 @@ SIGNATURES = {
     "enc_gemm_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
     "enc_decompress_gemm": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP, _U64, _VP]),
     "enc_gemm_dense": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
+    "enc_validate_workspace_bytes": (_U64, []),
+    "enc_validate": (_ST, [_VP, _INFO_P, _VP, _U64, _VP, ctypes.POINTER(EncCheck)]),
     "enc_status_string": (ctypes.c_char_p, [_ST]),
     "enc_last_error": (ctypes.c_char_p, []),
 }
@@ -237,6 +251,23 @@ def enc_gemm_dense(x, w, y=None, ws=None, stream=None):
     _check(lib().enc_gemm_dense(_ptr(x), M, K, _ptr(w), N, _ptr(y), _ptr(ws), ws.numel(),
                                 _stream(stream)))
     return y
+
+
+def enc_validate_workspace_bytes():
+    return int(lib().enc_validate_workspace_bytes())
+
+
+def enc_validate(comp, info, ws=None, stream=None):
+    """Deep check of a device stream. Returns an EncCheck (kind 0 = valid);
+    ENC_ERR_BAD_STREAM is reported through it, other failures raise."""
+    if ws is None:
+        ws = _empty_u8(enc_validate_workspace_bytes(), comp.device)
+    chk = EncCheck()
+    st = lib().enc_validate(_ptr(comp), ctypes.byref(info), _ptr(ws), ws.numel(), _stream(stream),
+                            ctypes.byref(chk))
+    if st != ENC_OK and not (st == -4 and chk.kind != 0):
+        _check(st)
+    return chk
 
 
 def enc_status_string(status):

@@ -139,3 +139,37 @@ def decode(s):
             out.append(join((base + d) & 0xFF, s[sm_off + i * B + t]))
         pos += _align(-(-L * w // 8), 16)
     return out
+
+
+def validate(s):
+    """(kind, index) of the first failing deep condition of a coded stream
+    with a consistent header, restated by walking the blocks in order:
+    1 = a width above 8 (index: block), 2 = a stored segment offset that is
+    not the running total of padded payload sizes, or a payload_bytes field
+    that is not the grand total (index: segment, or nseg for payload_bytes),
+    3 = some base + code above 255 (index: block). (0, 0) = valid."""
+    flags, B = _get(s, 8, 4), _get(s, 12, 4)
+    if flags & 1:
+        return 0, 0
+    n, nb, nseg = _get(s, 24, 8), _get(s, 32, 8), _get(s, 40, 8)
+    meta_off, segoff_off = _get(s, 56, 8), _get(s, 64, 8)
+    payload_off, payload_bytes = _get(s, 72, 8), _get(s, 80, 8)
+    widths = [s[meta_off + 2 * i + 1] for i in range(nb)]
+    for i, w in enumerate(widths):
+        if w > 8:
+            return 1, i
+    sizes = [_align(-(-min(B, n - i * B) * w // 8), 16) for i, w in enumerate(widths)]
+    expected = [sum(sizes[:SEG * k]) for k in range(nseg)] + [sum(sizes)]
+    stored = [_get(s, segoff_off + 8 * k, 8) for k in range(nseg)] + [payload_bytes]
+    for k in range(nseg + 1):
+        if stored[k] != expected[k]:
+            return 2, k
+    pos = payload_off
+    for i in range(nb):
+        L, base, w = min(B, n - i * B), s[meta_off + 2 * i], widths[i]
+        for t in range(L):
+            d = sum(((s[pos + (t * w + b) // 8] >> ((t * w + b) % 8)) & 1) << b for b in range(w))
+            if base + d > 255:
+                return 3, i
+        pos += sizes[i]
+    return 0, 0

@@ -301,7 +301,7 @@ typedef struct {
   uint64_t n, nb, nseg, sm_off, meta_off, segoff_off, payload_off, payload_bytes, raw_off, total;
 } orc_header;
 
-static int parse_header(const uint8_t *s, uint64_t bytes, orc_header *h) {
+static int parse_header_fields(const uint8_t *s, uint64_t bytes, orc_header *h) {
   if (s == NULL || bytes < ORC_HEADER_BYTES) return ORC_E_STREAM;
   if (s[0] != 'E' || s[1] != 'N' || s[2] != 'C' || s[3] != 'B') return ORC_E_STREAM;
   if (get_le(s + 4, 2) != ORC_VERSION || get_le(s + 6, 2) != ORC_DTYPE_BF16) return ORC_E_STREAM;
@@ -335,17 +335,43 @@ static int parse_header(const uint8_t *s, uint64_t bytes, orc_header *h) {
       h->segoff_off != L.segoff_off || h->payload_off != L.payload_off || h->raw_off != 0 ||
       h->total != h->payload_off + h->payload_bytes)
     return ORC_E_STREAM;
-  /* widths and offsets must agree with the meta section */
+  return ORC_OK;
+}
+
+/* The two structural conditions on the data sections of a coded stream with
+ * a consistent header: every width is at most 8 (kind 1, index = first such
+ * block), and each stored segment offset equals the sum of the padded
+ * payload sizes of all earlier blocks, with payload_bytes equal to the sum
+ * over all blocks (kind 2, index = first wrong stored offset; index nseg
+ * stands for payload_bytes). Returns 0 when both hold. */
+static int check_widths_offsets(const uint8_t *s, const orc_header *h, uint64_t *index) {
+  for (uint64_t i = 0; i < h->nb; i++) {
+    if (s[h->meta_off + 2 * i + 1] > 8) {
+      *index = i;
+      return 1;
+    }
+  }
   uint64_t running = 0;
   for (uint64_t i = 0; i < h->nb; i++) {
-    unsigned w = s[h->meta_off + 2 * i + 1];
-    if (w > 8) return ORC_E_STREAM;
-    if (i % ORC_SEG_BLOCKS == 0 && get_le(s + h->segoff_off + 8 * (i / ORC_SEG_BLOCKS), 8) != running)
-      return ORC_E_STREAM;
-    running += orc_block_payload_bytes(w, block_len(h->n, h->B, i));
+    if (i % ORC_SEG_BLOCKS == 0 &&
+        get_le(s + h->segoff_off + 8 * (i / ORC_SEG_BLOCKS), 8) != running) {
+      *index = i / ORC_SEG_BLOCKS;
+      return 2;
+    }
+    running += orc_block_payload_bytes(s[h->meta_off + 2 * i + 1], block_len(h->n, h->B, i));
   }
-  if (running != h->payload_bytes) return ORC_E_STREAM;
-  return ORC_OK;
+  if (running != h->payload_bytes) {
+    *index = h->nseg;
+    return 2;
+  }
+  return 0;
+}
+
+static int parse_header(const uint8_t *s, uint64_t bytes, orc_header *h) {
+  int st = parse_header_fields(s, bytes, h);
+  if (st != ORC_OK || h->flags == ORC_FLAG_RAW) return st;
+  uint64_t index;
+  return check_widths_offsets(s, h, &index) == 0 ? ORC_OK : ORC_E_STREAM;
 }
 
 /* Validates a stream; returns its element count or a negative status. */
@@ -416,6 +442,39 @@ int orc_decode_range(const uint8_t *s, uint64_t bytes, uint64_t first, uint64_t 
     }
   }
   return ORC_OK;
+}
+
+/* Deep validity of a stream whose header is consistent. Returns the kind of
+ * the first failing condition, in this order: 1 = a width above 8, 2 = a
+ * stored segment offset (or payload_bytes) that is not the prefix sum of the
+ * padded block sizes, 3 = an element whose base + code exceeds 255 (the
+ * transform subtracts the block minimum from exponent bytes, so a stream
+ * written from BF16 input never has one; ENEC Abstract: branch-free integer
+ * transformation). *index receives the first failing block (1, 3) or stored
+ * offset (2). 0 = valid (RAW streams always are). Negative = bad header. */
+int orc_validate(const uint8_t *s, uint64_t bytes, uint64_t *index) {
+  orc_header h;
+  *index = 0;
+  int st = parse_header_fields(s, bytes, &h);
+  if (st != ORC_OK) return st;
+  if (h.flags == ORC_FLAG_RAW) return 0;
+  int kind = check_widths_offsets(s, &h, index);
+  if (kind != 0) return kind;
+  for (uint64_t i = 0; i < h.nb; i++) {
+    uint64_t q = block_payload_start(s, &h, i);
+    unsigned base = s[h.meta_off + 2 * i];
+    unsigned w = s[h.meta_off + 2 * i + 1];
+    uint64_t len = block_len(h.n, h.B, i);
+    for (uint64_t t = 0; t < len; t++) {
+      unsigned d = 0;
+      for (unsigned b = 0; b < w; b++) d |= get_bit(s + q, t * w + b) << b;
+      if (base + d > 255) {
+        *index = i;
+        return 3;
+      }
+    }
+  }
+  return 0;
 }
 
 /* ---------------------------------------------------------------------------

@@ -62,6 +62,8 @@ def lib():
         L.orc_decode_range.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                        _u16p]
         L.orc_decode_range.restype = ctypes.c_int
+        L.orc_validate.argtypes = [_u8p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+        L.orc_validate.restype = ctypes.c_int
         L.orc_gemm_f64.argtypes = [_u16p, ctypes.c_uint32, ctypes.c_uint32, _u16p,
                                    ctypes.c_uint32, _f64p, _f64p]
         L.orc_gemm_f64.restype = None
@@ -163,6 +165,18 @@ def decode_range(s, first, count):
     if r != 0:
         raise OracleError("decode_range failed: %d" % r)
     return out[:count]
+
+
+def validate(s):
+    """(kind, index) of the first failing deep condition of a stream whose
+    header is consistent: 0 valid, 1 width above 8, 2 wrong stored segment
+    offset (index nseg = payload_bytes), 3 exponent above 255."""
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    idx = ctypes.c_uint64(0)
+    kind = lib().orc_validate(_ptr(s, _u8p), s.size, ctypes.byref(idx))
+    if kind < 0:
+        raise OracleError("bad header: %d" % kind)
+    return int(kind), int(idx.value)
 
 
 def gemm_f64(X, W):

@@ -352,6 +352,82 @@ def test_rejects_corrupted_streams(orc):
     assert orc.stream_elements(bad) < 0
 
 
+# ------------------------------------------------------------ deep check
+def _u64(s, off):
+    return int.from_bytes(bytes(s[off:off + 8]), "little")
+
+
+def test_validate_accepts_encoder_output(orc):
+    rng = np.random.default_rng(91)
+    top = _bits_from_exps(rng.integers(250, 256, 4096), rng.integers(0, 256, 4096))
+    cases = [(synth.tiny(), 512), (synth.tiny()[:3001], 8), (top, 16), (top, 512),
+             (synth.stress("mixture", 1 << 16), 128), (np.zeros(777, np.uint16), 64)]
+    for x, B in cases:
+        s = orc.encode(x, B)
+        assert orc.validate(s) == (0, 0), B
+        if x.size <= 5000:
+            assert brute.validate(bytes(s)) == (0, 0), B
+    raw = orc.encode(synth.random_bits(3000, 2), 512)
+    assert orc.validate(raw) == (0, 0)
+
+
+def _planted_stream(orc):
+    # B = 64 and 200 blocks (4 segments). Every block cycles through exponents
+    # 120, 121, 122 (base 120, width 2: 16 payload bytes, no padding) except
+    # block 7, which cycles through 253, 254, 255 (base 253, width 2). Every
+    # block's payload is 16 bytes, so block i's starts 16 i bytes into the
+    # payload section.
+    exps = 120 + np.arange(12800) % 3
+    exps[7 * 64:8 * 64] = 253 + np.arange(64) % 3
+    x = _bits_from_exps(exps, np.arange(12800) % 256)
+    s = orc.encode(x, 64)
+    assert s[8] == 0                                    # coded, not RAW
+    assert s[_u64(s, 56) + 2 * 7: _u64(s, 56) + 2 * 7 + 2].tolist() == [253, 2]
+    assert _u64(s, 80) == 200 * 16
+    return s
+
+
+def test_validate_planted_cases(orc):
+    s = _planted_stream(orc)
+    meta, seg, pay = _u64(s, 56), _u64(s, 64), _u64(s, 72)
+    assert orc.validate(s) == (0, 0)
+    b = s.copy(); b[meta + 2 * 5 + 1] = 9; b[meta + 2 * 2 + 1] = 200
+    assert orc.validate(b) == (1, 2)
+    b = s.copy(); b[seg + 8 * 3] += 16                  # segment 3 offset off by 16
+    assert orc.validate(b) == (2, 3)
+    b = s.copy(); b[seg] = 16                           # first offset must be 0
+    assert orc.validate(b) == (2, 0)
+    b = np.concatenate([s, np.zeros(16, np.uint8)])     # payload_bytes 16 too big
+    b[80:88] = np.frombuffer((200 * 16 + 16).to_bytes(8, "little"), np.uint8)
+    b[96:104] = np.frombuffer((s.size + 16).to_bytes(8, "little"), np.uint8)
+    assert orc.validate(b) == (2, 4)
+    # element 3 of block 7: code bits [6, 8) = bits 6, 7 of payload byte 0;
+    # code 3 on base 253 gives 256
+    b = s.copy(); b[pay + 7 * 16] |= 0b11000000
+    assert orc.validate(b) == (3, 7)
+    b = s.copy(); b[meta + 2 * 7] = 254                 # base 254 + code 2 = 256
+    assert orc.validate(b) == (3, 7)
+    b = s.copy(); b[meta + 2 * 7] = 250                 # smaller base: still in range
+    assert orc.validate(b) == (0, 0)
+    for v in (b, s):
+        assert brute.validate(bytes(v)) == orc.validate(v)
+
+
+@pytest.mark.parametrize("B", [24, 40, 64, 136])
+def test_validate_matches_brute_on_corruptions(orc, B):
+    import corruptions
+    x = synth.gaussian_bits((3, 1000), 0.02, 92, B)
+    s = orc.encode(x, B)
+    assert s[8] == 0                                    # coded, not RAW
+    seen = set()
+    for seed, kind in enumerate(corruptions.KINDS * 3):
+        b = corruptions.corrupt(s, kind, 1000 * B + seed)
+        got = orc.validate(b)
+        assert got == brute.validate(bytes(b)), (kind, seed)
+        seen.add(got[0])
+    assert seen >= {0, 1, 2, 3}
+
+
 # ----------------------------------------------------------------- GEMM
 def _bf16_to_f64(bits):
     return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
