@@ -153,6 +153,19 @@ def main():
     log("decode: %.3f ms/step (launch avg %.3f, min %.3f), %.1f GB/s out, %.1f GB/s HBM"
         % (step_ms, avg_launch_ms, min(launch_ms), value, achieved))
 
+    # ---- the same step as one launch per tensor (context, not the headline) ----
+    pt_ms = []
+    for _ in range(max(args.steps // 4, 2)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for (c, inf), o in zip(streams, outs):
+            enc.enc_decompress(c, inf, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pt_ms.append(e0.elapsed_time(e1))
+    per_tensor_ms = float(np.median(pt_ms))
+    log("per-tensor launches: %.3f ms/step" % per_tensor_ms)
+
     # ---- correctness of what was timed (outside the timed region) ------------
     for k, i in enumerate(idx):
         x = synth.set8b_tensor_gpu(i, device=dev).reshape(-1)
@@ -207,6 +220,7 @@ def main():
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "hbm_frac_of_copy": round(achieved / copy_gbs, 4),
         "encode_gbs": round((2 * n_total + comp_total) / (enc_ms * 1e-3) / 1e9, 1),
+        "per_tensor_launch_ms_per_step": round(per_tensor_ms, 4),
         "roofline": {
             "bound": "hbm",
             "kernel": "k_decode_batch",

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libenc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["decode.hip", "encode.hip", "gemm.hip", "validate.hip", "enc_api.cpp"]
+SOURCES = ["decode.hip", "encode.hip", "encode_onepass.hip", "gemm.hip", "validate.hip",
+           "enc_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -174,6 +174,91 @@ DecodeDesc desc_of(const void *d_comp, const enc_info &i, uint16_t *d_out) {
   return d;
 }
 
+enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t payload) {
+  enc_info i;
+  memset(&i, 0, sizeof i);
+  i.version = 1;
+  i.dtype = 1;
+  i.flags = 0;
+  i.block_size = block_size;
+  i.n_elems = n;
+  i.n_blocks = L.nb;
+  i.n_segments = L.nseg;
+  i.sm_off = L.sm_off;
+  i.meta_off = L.meta_off;
+  i.segoff_off = L.segoff_off;
+  i.payload_off = L.payload_off;
+  i.payload_bytes = payload;
+  i.raw_off = 0;
+  i.total_bytes = L.payload_off + payload;
+  return i;
+}
+
+// Polls of an unpublished tile before the single pass gives up (about 0.1 s;
+// never reached when workgroups are dispatched in order). ENC_LOOKBACK_SPINS
+// overrides it, which lets tests force the fallback path.
+uint32_t lookback_spin_limit() {
+  const char *v = getenv("ENC_LOOKBACK_SPINS");
+  if (v && v[0]) return (uint32_t)strtoul(v, nullptr, 10);
+  return 1u << 22;
+}
+
+// Single pass (reads the input once): used when the output can hold the
+// RAW size and the fixed sections fit below it, so no store of the pass can
+// land outside the buffer and the RAW fallback can simply overwrite it.
+// Returns ENC_ERR_HIP with *gave_up set if a look-back wait gave up; the
+// caller then runs the two-pass encoder, which rewrites every byte.
+enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_size, const Layout &L,
+                             uint8_t *d_out, uint64_t cap, uint8_t *d_ws, hipStream_t s,
+                             enc_info *h_info, bool *gave_up) {
+  *gave_up = false;
+  EncodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.in = d_in;
+  a.out = d_out;
+  a.n = n;
+  a.nb = L.nb;
+  a.nseg = L.nseg;
+  a.meta_off = L.meta_off;
+  a.segoff_off = L.segoff_off;
+  a.payload_off = L.payload_off;
+  a.log2b = (uint32_t)log2_block(block_size);
+  a.ntiles = onepass_tiles(n);
+  a.cap = cap;
+  const uint64_t status_bytes = align_up(8 * a.ntiles, kSectionAlign);
+  a.status = reinterpret_cast<uint64_t *>(d_ws);
+  a.ws_total = reinterpret_cast<uint64_t *>(d_ws + status_bytes);
+  a.error = reinterpret_cast<uint32_t *>(d_ws + status_bytes + 12);
+  a.spin_limit = lookback_spin_limit();
+  hipError_t e = hipMemsetAsync(d_ws, 0, status_bytes + 16, s);
+  if (e != hipSuccess) return hip_fail(e, "look-back state initialisation");
+  e = launch_encode_onepass(a, s);
+  if (e != hipSuccess) return hip_fail(e, "single-pass kernel launch");
+  uint64_t back[2] = {0, 0};   // payload bytes; (unused) | error << 32
+  e = hipMemcpyAsync(back, a.ws_total, sizeof back, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "size read-back");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  if (back[1] >> 32) {
+    *gave_up = true;
+    return fail(ENC_ERR_HIP, "single-pass encoder: a look-back wait gave up");
+  }
+  const uint64_t payload = back[0];
+  const uint64_t raw_total = kHeaderBytes + 2 * n;
+  enc_info i;
+  enc_status st;
+  if (L.payload_off + payload >= raw_total) {
+    i = raw_info(n, block_size);
+    st = launched(launch_encode_raw(d_in, d_out, n, header_of(i), s), s, "raw copy launch");
+  } else {
+    i = coded_info(n, block_size, L, payload);
+    st = launched(launch_encode_pads(a, header_of(i), s), s, "header kernel launch");
+  }
+  if (st != ENC_OK) return st;
+  *h_info = i;
+  return ENC_OK;
+}
+
 uint64_t batch_bytes(int count) {
   return align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
                       8 * ((uint64_t)count + 1),
@@ -189,7 +274,10 @@ uint64_t enc_compress_bound(uint64_t n_elems) { return kHeaderBytes + 2 * n_elem
 uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size) {
   if (log2_block(block_size) < 0) return 0;
   const Layout L = layout_of(n_elems, block_size);
-  return align_up(2 * L.nb, kSectionAlign) + align_up(8 * L.nseg, kSectionAlign) + kSectionAlign;
+  const uint64_t two_pass =
+      align_up(2 * L.nb, kSectionAlign) + align_up(8 * L.nseg, kSectionAlign) + kSectionAlign;
+  const uint64_t one_pass = align_up(8 * onepass_tiles(n_elems), kSectionAlign) + kSectionAlign;
+  return two_pass > one_pass ? two_pass : one_pass;
 }
 
 enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, void *d_out,
@@ -223,6 +311,14 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
     return fail(ENC_ERR_CAPACITY, "workspace of %llu bytes needed", (unsigned long long)need_ws);
 
   const Layout L = layout_of(n, block_size);
+  if (out_capacity >= raw_total && L.payload_off <= raw_total) {
+    bool gave_up = false;
+    const enc_status st = compress_one_pass(d_in, n, block_size, L, static_cast<uint8_t *>(d_out),
+                                            out_capacity, static_cast<uint8_t *>(d_ws), s, h_info,
+                                            &gave_up);
+    if (!gave_up) return st;
+    clear_err();   // fall through to the two-pass encoder
+  }
   EncodeArgs a;
   memset(&a, 0, sizeof a);
   a.in = d_in;
@@ -263,21 +359,7 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
     if (out_capacity < coded_total)
       return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
                   (unsigned long long)out_capacity, (unsigned long long)coded_total);
-    memset(&i, 0, sizeof i);
-    i.version = 1;
-    i.dtype = 1;
-    i.flags = 0;
-    i.block_size = block_size;
-    i.n_elems = n;
-    i.n_blocks = L.nb;
-    i.n_segments = L.nseg;
-    i.sm_off = L.sm_off;
-    i.meta_off = L.meta_off;
-    i.segoff_off = L.segoff_off;
-    i.payload_off = L.payload_off;
-    i.payload_bytes = payload;
-    i.raw_off = 0;
-    i.total_bytes = coded_total;
+    i = coded_info(n, block_size, L, payload);
     e = launch_encode_pack(a, s);
     if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
     const enc_status st = launched(launch_encode_finish(a, header_of(i), s), s,

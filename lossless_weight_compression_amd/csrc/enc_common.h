@@ -62,6 +62,11 @@ constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"
 
 inline uint64_t tiles_for(uint64_t n) { return (n + kTileElems - 1) / kTileElems; }
 
+// The single-pass encoder handles kOnePassSub consecutive tiles per
+// workgroup and runs one look-back per workgroup.
+constexpr uint32_t kOnePassSub = 4;
+inline uint64_t onepass_tiles(uint64_t n) { return (tiles_for(n) + kOnePassSub - 1) / kOnePassSub; }
+
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_decode(const DecodeDesc &d, hipStream_t s);
 hipError_t launch_decode_batch(const void *table, hipStream_t s);
@@ -75,8 +80,15 @@ struct EncodeArgs {
   uint64_t n, nb, nseg;
   uint64_t meta_off, segoff_off, payload_off;
   uint32_t log2b;
+  // single pass only
+  uint64_t *status;      // one word per tile: flag (bits 63..62) | payload bytes
+  uint32_t *error;       // nonzero: a look-back wait gave up
+  uint32_t spin_limit;   // polls of a not-yet-published tile before giving up
+  uint64_t cap;          // output capacity: payload stores beyond it are dropped
+  uint64_t ntiles;
 };
 hipError_t launch_encode_params(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_encode_onepass(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_encode_scan(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_encode_pack(const EncodeArgs &a, hipStream_t s);
 
@@ -84,6 +96,7 @@ struct HeaderImage {
   uint8_t bytes[256];
 };
 hipError_t launch_encode_finish(const EncodeArgs &a, const HeaderImage &h, hipStream_t s);
+hipError_t launch_encode_pads(const EncodeArgs &a, const HeaderImage &h, hipStream_t s);
 hipError_t launch_encode_raw(const uint16_t *in, uint8_t *out, uint64_t n, const HeaderImage &h,
                              hipStream_t s);
 

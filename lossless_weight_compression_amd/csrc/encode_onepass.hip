@@ -1,0 +1,377 @@
+// encode_onepass.hip -- single-pass gfx950 encoder: reads the input once.
+//
+// "ENEC: A Lossless AI Model Compression Method Enabling Fast Inference on
+// Ascend NPUs", Abstract: block widths, bit-packing and a branch-free
+// transform per block, with a dependency-decoupled scan for the prefix sums
+// of block sizes. The scan across tiles here is a decoupled look-back: every
+// tile publishes its payload total as soon as it knows it, and a tile finds
+// its own offset by walking back over its predecessors' published totals
+// until it meets one that already carries a full prefix.
+//
+// One workgroup per tile of kOnePassSub x 1024 groups (4 x 8192 values:
+// whole blocks; tile = workgroup index). One look-back per 32768 values: a
+// published prefix can only advance about one 64-tile window per memory
+// round trip, and with 8192-value tiles that, not HBM, set the pace.
+// Workgroups are dispatched in index order, so a workgroup only ever waits
+// for tiles whose workgroups are already resident or finished: the lowest
+// unfinished one always proceeds. (A shared atomic ticket would not need that
+// ordering, but every workgroup would then update one address, which was
+// slower still.) Should a wait ever give up anyway, the host discards the
+// result and runs the two-pass encoder.
+// For each 8192-value sub-tile, in turn (the next one's loads in flight):
+//  1. per-block exponent min/max: lanes of one block reduce with packed
+//     16-bit max over shuffles, then one LDS atomic per block and wave;
+//  2. wave 0: base, width, padded payload size and offset (inside the
+//     workgroup's payload) of each block; writes the block metas;
+//  3. all lanes: sign+mantissa bytes to the stream, codes into a zeroed LDS
+//     image of the workgroup's payload (so pad bits are zero).
+// Per group the work is byte-parallel, as in the decoder: v_perm splits the
+// exponent and sign+mantissa bytes of 4 values at once, min/max use packed
+// 16-bit integer ops, and 4 codes pack with one bit-field extract each.
+// Then wave 0 publishes the workgroup's payload total, looks back for its
+// offset, publishes the prefix, stores the offsets of the segments that
+// start in this tile (and, in the last tile, the stream's payload size), and
+// the LDS image goes out with 16-byte stores.
+// Status words hold flag and value together and are read and written with
+// agent-scope relaxed atomics, so no fence is needed; every wait is bounded
+// (on give-up the kernel flags an error and the host falls back).
+#include "enc_common.h"
+
+namespace enc {
+namespace {
+
+constexpr uint64_t kFlagAgg = 1ull << 62;    // value = this tile's payload bytes
+constexpr uint64_t kFlagPre = 2ull << 62;    // value = payload bytes of tiles 0..t
+constexpr uint64_t kValMask = (1ull << 62) - 1;
+constexpr uint32_t kPayBytes = kOnePassSub * kTileGroups * 8 + 16;   // a tile's payload, at most
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pmax16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
+#pragma unroll
+  for (uint32_t d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+#pragma unroll
+  for (uint32_t d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__device__ __forceinline__ void publish(uint64_t *status, uint64_t tile, uint64_t word) {
+  __hip_atomic_store(status + tile, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of the payload totals of tiles [0, tile), by the whole wave. Lane l
+// reads tile top - l; the window is usable once every tile from the top down
+// to the nearest full prefix has published (a position below tile 0 counts
+// as a full prefix of 0); otherwise the wave sleeps briefly and reads it
+// again.
+__device__ uint64_t look_back(uint64_t *status, uint64_t tile, uint32_t lane, uint32_t *error,
+                              uint32_t spin_limit) {
+  uint64_t excl = 0;
+  int64_t top = (int64_t)tile - 1;
+  uint32_t spins = 0;
+  while (top >= 0) {
+    const int64_t idx = top - (int64_t)lane;
+    uint64_t v = kFlagPre;
+    if (idx >= 0)
+      v = __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t flag = v >> 62;
+    const uint64_t pre = __ballot(flag == 2);
+    const uint64_t none = __ballot(flag == 0);
+    const uint64_t need = pre ? ((pre & (~pre + 1)) << 1) - 1 : ~0ull;   // lanes up to the first prefix
+    if (none & need) {
+      if (++spins > spin_limit) {
+        if (lane == 0) atomicOr(error, 1u);
+        return 0;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    excl += wave_sum64(((need >> lane) & 1) ? (v & kValMask) : 0);
+    if (pre) break;
+    top -= 64;
+  }
+  return excl;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Barrier that waits for LDS traffic only: __syncthreads() would also wait
+// for every outstanding global load and store (on this part one counter
+// covers both), which would drain the next sub-tile's prefetch.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Raw buffer descriptor over [base, base + bytes): the hardware drops stores
+// and zero-fills loads of dwords that do not lie wholly inside, so every lane
+// issues its loads and stores unconditionally (a load or store under a branch
+// would make the compiler wait for all outstanding memory operations).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void *base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                           (int)(uint32_t)(bytes < 0xFFFFFFF0ull ? bytes : 0xFFFFFFF0ull),
+                                           0x00020000);
+}
+
+// Loads the 4 groups of this lane in sub-tile `sub` of the workgroup's tile;
+// offsets are relative to the tile start. A group cut short by the end of
+// the input is completed with copies of its first value (x_last: the input's
+// last value, needed when n is odd because its dword straddles the end), so
+// exponent min / max need no masking; the bytes it would add to the stream
+// are masked off when packing.
+__device__ __forceinline__ void load_sub(__amdgpu_buffer_rsrc_t in_rs, uint64_t left, uint32_t sub,
+                                         uint32_t tid, uint32_t x_last,
+                                         uint4 (&g)[kGroupsPerThread],
+                                         uint32_t (&valid)[kGroupsPerThread]) {
+#pragma unroll
+  for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+    const uint32_t e0 = (sub * kTileGroups + it * kThreads + tid) * 8;   // from the tile start
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(in_rs, 2 * e0, 0, 0);
+    g[it] = make_uint4(v.x, v.y, v.z, v.w);
+    valid[it] = e0 < left ? (left - e0 < 8 ? (uint32_t)(left - e0) : 8u) : 0u;
+  }
+  (void)x_last;
+}
+
+// The end-of-input fix-up described above (no memory access).
+__device__ __forceinline__ void complete_group(uint4 &g, uint32_t valid, uint32_t x_last) {
+  uint32_t x[8] = {g.x & 0xFFFFu, g.x >> 16, g.y & 0xFFFFu, g.y >> 16,
+                   g.z & 0xFFFFu, g.z >> 16, g.w & 0xFFFFu, g.w >> 16};
+  if (valid & 1) x[valid - 1] = x_last;   // n odd: the last value's dword read as 0
+#pragma unroll
+  for (uint32_t k = 1; k < 8; ++k)
+    if (k >= valid) x[k] = x[0];
+  g = make_uint4(x[0] | x[1] << 16, x[2] | x[3] << 16, x[4] | x[5] << 16, x[6] | x[7] << 16);
+}
+
+// Exponent bytes of a group's 8 values (el: values 0..3, eh: 4..7). A BF16
+// value shifted left by one carries its exponent in its high byte.
+__device__ __forceinline__ void exp_bytes(const uint4 &g, uint32_t &el, uint32_t &eh) {
+  el = __builtin_amdgcn_perm(g.y << 1, g.x << 1, 0x07050301u);
+  eh = __builtin_amdgcn_perm(g.w << 1, g.z << 1, 0x07050301u);
+}
+
+// Sign+mantissa bytes (sign in bit 7, mantissa in bits 6..0) of 4 values.
+__device__ __forceinline__ uint32_t sm_bytes(uint32_t x01, uint32_t x23) {
+  const uint32_t lo = __builtin_amdgcn_perm(x23, x01, 0x06040200u);   // low byte of each value
+  const uint32_t hi = __builtin_amdgcn_perm(x23, x01, 0x07050301u);   // high byte of each value
+  return (hi & 0x80808080u) | (lo & 0x7F7F7F7Fu);
+}
+
+// ((255 - min) << 16) | max over the 8 exponent bytes, with packed 16-bit
+// min / max (no packed-float instructions involved).
+__device__ __forceinline__ uint32_t minmax_key(uint32_t el, uint32_t eh) {
+  const u16x2 a = __builtin_bit_cast(u16x2, el & 0x00FF00FFu);
+  const u16x2 b = __builtin_bit_cast(u16x2, (el >> 8) & 0x00FF00FFu);
+  const u16x2 c = __builtin_bit_cast(u16x2, eh & 0x00FF00FFu);
+  const u16x2 d = __builtin_bit_cast(u16x2, (eh >> 8) & 0x00FF00FFu);
+  const u16x2 mn = __builtin_elementwise_min(__builtin_elementwise_min(a, b),
+                                             __builtin_elementwise_min(c, d));
+  const u16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                             __builtin_elementwise_max(c, d));
+  const uint32_t lo = mn.x < mn.y ? mn.x : mn.y, hi = mx.x > mx.y ? mx.x : mx.y;
+  return ((255u - lo) << 16) | hi;
+}
+
+// Four code bytes (each < 2^w) packed LSB first at width w: 4w bits.
+__device__ __forceinline__ uint32_t pack4(uint32_t d, uint32_t w) {
+  return __builtin_amdgcn_ubfe(d, 0, 8) | (__builtin_amdgcn_ubfe(d, 8, 8) << w) |
+         (__builtin_amdgcn_ubfe(d, 16, 8) << (2 * w)) | ((d >> 24) << (3 * w));
+}
+
+__global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
+  __shared__ uint32_t pay[kPayBytes / 4];
+  __shared__ uint32_t smin[64], smax[64], sblk[64], s_suboff[kOnePassSub];
+  __shared__ uint64_t s_excl;
+  __shared__ uint32_t s_run;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t tile = blockIdx.x;
+  const uint32_t log2b = a.log2b, log2gpb = log2b - 3;
+  const uint32_t bps = (uint32_t)(kTileElems >> log2b);            // blocks per sub-tile
+  const uint64_t n = a.n;
+  const uint64_t start = tile * kOnePassSub * kTileElems;         // first value of the tile
+  const uint64_t left = n - start;                                 // values from the tile start on
+  const uint32_t nsub = (uint32_t)((left < kOnePassSub * kTileElems ? left : kOnePassSub * kTileElems) +
+                                   kTileElems - 1) / kTileElems;
+  const uint64_t span_vals = left < kOnePassSub * kTileElems ? left : kOnePassSub * kTileElems;
+  const uint32_t span = (1u << log2gpb) < 64 ? (1u << log2gpb) : 64u;   // lanes of one block
+  const __amdgpu_buffer_rsrc_t in_rs = range_rsrc(a.in + start, 2 * span_vals);
+  // sign+mantissa plane of the tile, up to the 8-value boundary (the plane's
+  // padding is zero, and so are the masked bytes of a short last group)
+  const __amdgpu_buffer_rsrc_t sm_rs = range_rsrc(a.out + kHeaderBytes + start, align_up(span_vals, 8));
+  const uint32_t x_last = a.in[n - 1];
+
+  if (tid < 64) {
+    smin[tid] = 255;
+    smax[tid] = 0;
+  }
+  if (tid == 0) s_run = 0;
+  for (uint32_t i = tid; i < kPayBytes / 4; i += kThreads) pay[i] = 0;
+
+  uint4 g[kGroupsPerThread], gn[kGroupsPerThread];
+  uint32_t valid[kGroupsPerThread], vn[kGroupsPerThread];
+  load_sub(in_rs, left, 0, tid, x_last, g, valid);
+#pragma unroll 1
+  for (uint32_t sub = 0; sub < nsub; ++sub) {
+    const uint64_t st = tile * kOnePassSub + sub;                  // global sub-tile index
+    const uint64_t blk0 = st * bps;
+    load_sub(in_rs, left, sub + 1 < nsub ? sub + 1 : sub, tid, x_last, gn, vn);   // next, in flight
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it)
+      if (valid[it] - 1 < 7) complete_group(g[it], valid[it], x_last);   // 1 <= valid < 8
+    lds_barrier();   // previous sub-tile packed (sblk free), min/max reset
+
+    // per-block min / max exponent
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+      uint32_t el, eh;
+      exp_bytes(g[it], el, eh);
+      uint32_t key = valid[it] ? minmax_key(el, eh) : 0u;   // 0: no valid value here
+      for (uint32_t d = 1; d < span; d <<= 1) key = pmax16(key, __shfl_xor(key, d, 64));
+      const uint32_t q = it * kThreads + tid;
+      if ((lane & (span - 1)) == 0 && key != 0) {
+        atomicMin(&smin[q >> log2gpb], 255u - (key >> 16));
+        atomicMax(&smax[q >> log2gpb], key & 0xFFFFu);
+      }
+    }
+    lds_barrier();
+
+    // block parameters, metas, offsets inside the workgroup's payload
+    if (wave == 0) {
+      const uint64_t blk = blk0 + lane;
+      uint32_t P = 0, base = 0, w = 0;
+      if (lane < bps && blk < a.nb) {
+        base = smin[lane];
+        const uint32_t r = smax[lane] - base;
+        w = r ? 32u - __clz(r) : 0u;
+        const uint32_t L = (blk + 1 == a.nb) ? (uint32_t)(n - ((a.nb - 1) << log2b)) : (1u << log2b);
+        P = (((w * L + 7) >> 3) + 15) & ~15u;
+      }
+      // metas of this sub-tile, two per dword store. The range is rounded up
+      // to whole dwords (a lone last meta's neighbour is a zero pad byte pair
+      // of the meta section); pairs past it are dropped.
+      const __amdgpu_buffer_rsrc_t meta_rs = range_rsrc(
+          a.out + a.meta_off + 2 * blk0, align_up(2 * (a.nb - blk0 < bps ? a.nb - blk0 : bps), 4));
+      const uint32_t mw = base | (w << 8);
+      const uint32_t pair = mw | (__shfl_down(mw, 1, 64) << 16);
+      if (!(lane & 1)) __builtin_amdgcn_raw_buffer_store_b32(pair, meta_rs, 2 * lane, 0, 0);
+      smin[lane] = 255;
+      smax[lane] = 0;
+      const uint32_t run = s_run;
+      const uint32_t incl = wave_incl_scan(P, lane);
+      const uint32_t sub_total = __shfl(incl, 63, 64);
+      sblk[lane] = base | (w << 8) | ((run + incl - P) << 16);
+      if (lane == 0) {
+        s_suboff[sub] = run;
+        s_run = run + sub_total;
+      }
+    }
+    lds_barrier();
+
+    // sign+mantissa plane and the payload image. A group's codes are w bytes
+    // at byte `pos` of the image; they are OR-ed into the (at most three)
+    // dwords they touch, with LDS atomics since neighbouring groups share
+    // dwords.
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+      const uint32_t q = it * kThreads + tid;
+      const uint32_t info = sblk[q >> log2gpb];
+      const uint32_t w = (info >> 8) & 0xFFu, base4 = (info & 0xFFu) * 0x01010101u;
+      uint32_t el, eh;
+      exp_bytes(g[it], el, eh);
+      uint32_t s0 = sm_bytes(g[it].x, g[it].y), s1 = sm_bytes(g[it].z, g[it].w);
+      const uint32_t c0 = pack4(el - base4, w), c1 = pack4(eh - base4, w);   // bytes: no borrows
+      uint32_t lo = w == 8 ? c0 : c0 | (c1 << (4 * w));
+      uint32_t hi = w == 8 ? c1 : (w > 4 ? c1 >> (32 - 4 * w) : 0u);
+      const uint32_t v = valid[it];
+      if (v < 8) {   // zero what lies past the end of the input (all of it if v == 0)
+        const uint32_t bits = v * w;
+        s0 &= v >= 4 ? ~0u : (1u << (8 * v)) - 1;
+        s1 &= v <= 4 ? 0u : (1u << (8 * (v - 4))) - 1;
+        lo &= bits >= 32 ? ~0u : (1u << bits) - 1;
+        hi &= bits <= 32 ? 0u : (1u << (bits - 32)) - 1;
+      }
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){s0, s1}, sm_rs, 8 * (sub * kTileGroups + q), 0, 0);
+      const uint32_t pos = (info >> 16) + (q & ((1u << log2gpb) - 1)) * w;
+      const uint32_t sh = (pos & 3) * 8, d0 = pos >> 2;
+      const uint32_t w0 = lo << sh;
+      const uint32_t w1 = sh ? (lo >> (32 - sh)) | (hi << sh) : hi;
+      const uint32_t w2 = sh ? hi >> (32 - sh) : 0u;
+      if (w0) atomicOr(&pay[d0], w0);
+      if (w1) atomicOr(&pay[d0 + 1], w1);
+      if (w2) atomicOr(&pay[d0 + 2], w2);
+    }
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+      g[it] = gn[it];
+      valid[it] = vn[it];
+    }
+  }
+  lds_barrier();
+
+  // the workgroup's payload offset
+  if (wave == 0) {
+    const uint32_t agg = s_run;
+    if (lane == 0) publish(a.status, tile, (tile == 0 ? kFlagPre : kFlagAgg) | agg);
+    const uint64_t excl = look_back(a.status, tile, lane, a.error, a.spin_limit);
+    if (lane == 0) {
+      if (tile > 0) publish(a.status, tile, kFlagPre | (excl + agg));
+      if (tile + 1 == a.ntiles) *a.ws_total = excl + agg;
+      s_excl = excl;
+    }
+    if (lane < nsub && (((tile * kOnePassSub + lane) * bps) & 63) == 0)   // segment starts
+      *reinterpret_cast<uint64_t *>(a.out + a.segoff_off +
+                                    8 * (((tile * kOnePassSub + lane) * bps) >> 6)) = excl + s_suboff[lane];
+  }
+  lds_barrier();
+
+  // payload out
+  const uint64_t dst = a.payload_off + s_excl;
+  const __amdgpu_buffer_rsrc_t pay_rs = range_rsrc(a.out + dst, a.cap > dst ? a.cap - dst : 0);
+  for (uint32_t i = tid; i < s_run / 16; i += kThreads) {
+    const uint4 d = reinterpret_cast<const uint4 *>(pay)[i];
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){d.x, d.y, d.z, d.w}, pay_rs, 16 * i, 0, 0);
+  }
+}
+
+// Header and the zero padding of the sm, meta and segment-offset sections of
+// a stream the single pass wrote.
+__global__ __launch_bounds__(kThreads) void k_enc_pads(EncodeArgs a, HeaderImage h) {
+  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  if (tid < 64) reinterpret_cast<uint32_t *>(a.out)[tid] = reinterpret_cast<const uint32_t *>(h.bytes)[tid];
+  const uint64_t sm_from = kHeaderBytes + align_up(a.n, 8), sm_to = a.meta_off;
+  const uint64_t meta_from = a.meta_off + 2 * a.nb, meta_to = a.segoff_off;
+  const uint64_t seg_from = a.segoff_off + 8 * a.nseg, seg_to = a.payload_off;
+  const uint64_t l0 = sm_to - sm_from, l1 = meta_to - meta_from, l2 = seg_to - seg_from;
+  for (uint64_t i = tid; i < l0 + l1 + l2; i += stride) {
+    const uint64_t at = i < l0 ? sm_from + i : i < l0 + l1 ? meta_from + (i - l0) : seg_from + (i - l0 - l1);
+    a.out[at] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode_onepass(const EncodeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_enc_onepass, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_pads(const EncodeArgs &a, const HeaderImage &h, hipStream_t s) {
+  hipLaunchKernelGGL(k_enc_pads, dim3(4), dim3(kThreads), 0, s, a, h);
+  return hipGetLastError();
+}
+
+}  // namespace enc

@@ -184,6 +184,50 @@ def test_batch_mixed_items(E, orc):
         assert np.array_equal(host_u16(out), x.reshape(-1))
 
 
+# ------------------------------------------- single pass and two passes
+@pytest.mark.parametrize("B", [128, 512, 4096])
+def test_one_pass_and_two_pass_streams_agree(E, orc, B):
+    """An output buffer of the RAW size selects the single-pass encoder (one
+    read of the input, decoupled look-back across tiles); a buffer of exactly
+    the final size selects the two-pass encoder. Both must write the oracle's
+    bytes, for coded and RAW results, many tiles and ragged tails."""
+    cases = [synth.gaussian_bits((777, 1111), 0.02, 95, B),          # 105 tiles, ragged
+             synth.stress("laplace", (1024, 4100)),
+             synth.random_bits(70_001, 6),                             # RAW
+             synth.tiny()[:8192 * 3 + 5]]
+    for k, x in enumerate(cases):
+        x = np.ascontiguousarray(x).reshape(-1)
+        say("one/two pass", k, "n=%d B=%d" % (x.size, B))
+        ref = orc.encode(x, B)
+        xd = dev(x)
+        big = torch.full((E.enc_compress_bound(x.size),), 0xA5, dtype=torch.uint8, device="cuda")
+        c1, i1 = E.enc_compress(xd, B, out=big)
+        exact = torch.full((ref.size,), 0x5A, dtype=torch.uint8, device="cuda")
+        c2, i2 = E.enc_compress(xd, B, out=exact)
+        torch.cuda.synchronize()
+        assert i1.total_bytes == i2.total_bytes == ref.size
+        assert np.array_equal(host_u8(c1), ref), k
+        assert np.array_equal(host_u8(c2), ref), k
+
+
+def test_look_back_give_up_falls_back_to_two_passes(E, orc):
+    """With the look-back allowed no second poll (ENC_LOOKBACK_SPINS=0), a
+    tile that finds a predecessor unpublished gives up at once; the call must
+    still return the oracle's stream (through the two-pass encoder)."""
+    import os
+    x = synth.gaussian_bits((2048, 4096), 0.02, 96, 0)     # 1024 tiles
+    ref = orc.encode(x.reshape(-1), 512)
+    os.environ["ENC_LOOKBACK_SPINS"] = "0"
+    try:
+        say("look-back spin limit 0")
+        for _ in range(3):
+            comp, info = E.enc_compress(dev(x), 512)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_u8(comp), ref)
+    finally:
+        os.environ.pop("ENC_LOOKBACK_SPINS", None)
+
+
 # ------------------------------------------------------------------ errors
 def test_capacity_error_leaves_output_untouched(E):
     x = dev(synth.tiny())
