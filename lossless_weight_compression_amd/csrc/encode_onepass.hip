@@ -8,10 +8,10 @@
 // its own offset by walking back over its predecessors' published totals
 // until it meets one that already carries a full prefix.
 //
-// One workgroup per tile of kOnePassSub x 1024 groups (4 x 8192 values:
-// whole blocks; tile = workgroup index). One look-back per 32768 values: a
-// published prefix can only advance about one 64-tile window per memory
-// round trip, and with 8192-value tiles that, not HBM, set the pace.
+// One workgroup per tile of SUB x 1024 groups (SUB x 8192 values: whole
+// blocks; tile = workgroup index). A published prefix can only advance about
+// one 64-tile window per memory round trip, so large inputs take SUB = 4 (one
+// look-back per 32768 values); small ones take fewer, to fill the device.
 // Workgroups are dispatched in index order, so a workgroup only ever waits
 // for tiles whose workgroups are already resident or finished: the lowest
 // unfinished one always proceeds. (A shared atomic ticket would not need that
@@ -43,7 +43,6 @@ namespace {
 constexpr uint64_t kFlagAgg = 1ull << 62;    // value = this tile's payload bytes
 constexpr uint64_t kFlagPre = 2ull << 62;    // value = payload bytes of tiles 0..t
 constexpr uint64_t kValMask = (1ull << 62) - 1;
-constexpr uint32_t kPayBytes = kOnePassSub * kTileGroups * 8 + 16;   // a tile's payload, at most
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -191,9 +190,11 @@ __device__ __forceinline__ uint32_t pack4(uint32_t d, uint32_t w) {
          (__builtin_amdgcn_ubfe(d, 16, 8) << (2 * w)) | ((d >> 24) << (3 * w));
 }
 
+template <uint32_t SUB>
 __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
+  constexpr uint32_t kPayBytes = SUB * kTileGroups * 8 + 16;   // a tile's payload, at most
   __shared__ uint32_t pay[kPayBytes / 4];
-  __shared__ uint32_t smin[64], smax[64], sblk[64], s_suboff[kOnePassSub];
+  __shared__ uint32_t smin[64], smax[64], sblk[64], s_suboff[SUB];
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_run;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -201,11 +202,11 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
   const uint32_t log2b = a.log2b, log2gpb = log2b - 3;
   const uint32_t bps = (uint32_t)(kTileElems >> log2b);            // blocks per sub-tile
   const uint64_t n = a.n;
-  const uint64_t start = tile * kOnePassSub * kTileElems;         // first value of the tile
+  const uint64_t start = tile * SUB * kTileElems;         // first value of the tile
   const uint64_t left = n - start;                                 // values from the tile start on
-  const uint32_t nsub = (uint32_t)((left < kOnePassSub * kTileElems ? left : kOnePassSub * kTileElems) +
+  const uint32_t nsub = (uint32_t)((left < SUB * kTileElems ? left : SUB * kTileElems) +
                                    kTileElems - 1) / kTileElems;
-  const uint64_t span_vals = left < kOnePassSub * kTileElems ? left : kOnePassSub * kTileElems;
+  const uint64_t span_vals = left < SUB * kTileElems ? left : SUB * kTileElems;
   const uint32_t span = (1u << log2gpb) < 64 ? (1u << log2gpb) : 64u;   // lanes of one block
   const __amdgpu_buffer_rsrc_t in_rs = range_rsrc(a.in + start, 2 * span_vals);
   // sign+mantissa plane of the tile, up to the 8-value boundary (the plane's
@@ -225,9 +226,11 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
   load_sub(in_rs, left, 0, tid, x_last, g, valid);
 #pragma unroll 1
   for (uint32_t sub = 0; sub < nsub; ++sub) {
-    const uint64_t st = tile * kOnePassSub + sub;                  // global sub-tile index
+    const uint64_t st = tile * SUB + sub;                  // global sub-tile index
     const uint64_t blk0 = st * bps;
-    load_sub(in_rs, left, sub + 1 < nsub ? sub + 1 : sub, tid, x_last, gn, vn);   // next, in flight
+    // next sub-tile, in flight (past the tile's last one every dword is out of
+    // the descriptor's range: zeros, and no memory access)
+    load_sub(in_rs, left, sub + 1, tid, x_last, gn, vn);
 #pragma unroll
     for (uint32_t it = 0; it < kGroupsPerThread; ++it)
       if (valid[it] - 1 < 7) complete_group(g[it], valid[it], x_last);   // 1 <= valid < 8
@@ -331,9 +334,9 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
       if (tile + 1 == a.ntiles) *a.ws_total = excl + agg;
       s_excl = excl;
     }
-    if (lane < nsub && (((tile * kOnePassSub + lane) * bps) & 63) == 0)   // segment starts
+    if (lane < nsub && (((tile * SUB + lane) * bps) & 63) == 0)   // segment starts
       *reinterpret_cast<uint64_t *>(a.out + a.segoff_off +
-                                    8 * (((tile * kOnePassSub + lane) * bps) >> 6)) = excl + s_suboff[lane];
+                                    8 * (((tile * SUB + lane) * bps) >> 6)) = excl + s_suboff[lane];
   }
   lds_barrier();
 
@@ -365,7 +368,11 @@ __global__ __launch_bounds__(kThreads) void k_enc_pads(EncodeArgs a, HeaderImage
 }  // namespace
 
 hipError_t launch_encode_onepass(const EncodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_enc_onepass, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a);
+  switch (onepass_sub(a.n)) {
+    case 1: hipLaunchKernelGGL(k_enc_onepass<1>, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_enc_onepass<2>, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_enc_onepass<4>, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

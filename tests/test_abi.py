@@ -47,9 +47,10 @@ def test_sizes(L):
     assert enc.enc_compress_bound(1000) == 2256
     # meta A(2*nb) + seg A(8*nseg) + one 256-byte slot
     assert enc.enc_compress_workspace_bytes(1 << 20, 512) == 4096 + 256 + 256
-    # B = 4096: meta A(512) + seg A(32) + slot; the single pass (one status
-    # word per 32768 values + slot = 512) needs less
-    assert enc.enc_compress_workspace_bytes(1 << 20, 4096) == 512 + 256 + 256
+    # B = 4096: meta A(512) + seg A(32) + slot = 1024 for two passes; the single
+    # pass on an input this small uses one status word per 8192 values:
+    # A(8 * 128) + slot = 1280
+    assert enc.enc_compress_workspace_bytes(1 << 20, 4096) == 1024 + 256
     assert enc.enc_compress_workspace_bytes(1 << 20, 24) == 0
     assert enc.enc_batch_table_bytes(0) % 256 == 0
     assert enc.enc_batch_table_bytes(226) >= 64 + 226 * 80 + 227 * 8
