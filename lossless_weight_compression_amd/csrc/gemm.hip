@@ -591,7 +591,7 @@ __device__ __forceinline__ void lds_barrier() {
 // double-buffered loads in 256 registers, so larger M uses several 64-row tiles.
 uint32_t mfmau_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
 
-template <int MT, int WAVES, bool DENSE>
+template <int MT, int WAVES, bool DENSE, int NB>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   constexpr uint32_t RPW = 32 / WAVES;          // rows decoded per wave per step
   constexpr uint32_t NSUB = 32 / WAVES;         // 16-column subtiles per wave
@@ -634,8 +634,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   // or X element; out-of-range data is discarded after the load. Loads under
   // branches would make the compiler wait for all outstanding loads (vmcnt 0)
   // before the decode, i.e. also for the next step's prefetch.
+  // st >= nsteps (ring slots past the end): the stream loads get an offset
+  // past the descriptor's range (zeros, no memory access), the others a
+  // clamped row.
   auto load_step = [&](uint32_t st, Step &S) {
-    const uint32_t kb = k0 + 32 * st;
+    const uint32_t kb = k0 + 32 * min(st, nsteps - 1);
+    const uint32_t dead = st < nsteps ? 0u : 0x80000000u;
 #pragma unroll
     for (uint32_t j = 0; j < RPW; ++j) {
       const uint32_t kr = min(kb + wave * RPW + j, k1 - 1);
@@ -646,8 +650,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
         const uint32_t meta = __builtin_amdgcn_readfirstlane(tbl_meta[kr - k0]);
         const uint32_t w = (meta >> 8) & 15u;
         const uint32_t pb = off + ((meta >> 16) + lane) * w;
-        S.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, kHeaderBytes + kr * N + col0, 0);
-        S.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
+        S.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (8 * lane) | dead, kHeaderBytes + kr * N + col0, 0);
+        S.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
       }
     }
     const uint32_t kx = kb + 8 * (lane >> 4);
@@ -719,18 +723,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
     }
   };
 
-  Step SA, SB;
-  if (nsteps) load_step(0, SA);
-  for (uint32_t st = 0; st < nsteps; st += 2) {
-    if (st + 1 < nsteps) load_step(st + 1, SB);
-    decode_step(st, SA, 0);
-    lds_barrier();
-    mfma_step(0, SA);
-    if (st + 1 < nsteps) {
-      if (st + 2 < nsteps) load_step(st + 2, SA);
-      decode_step(st + 1, SB, 1);
-      lds_barrier();
-      mfma_step(1, SB);
+  // NB step buffers in a ring: step s + NB - 1 is loaded while step s is
+  // decoded and multiplied. Loads are issued unconditionally (see load_step
+  // for slots past the last step), so the number of loads in flight is the
+  // same on every path and the compiler waits for exactly the step it needs.
+  Step S[NB];
+#pragma unroll
+  for (uint32_t p = 0; p + 1 < NB; ++p) load_step(p, S[p]);
+  for (uint32_t st = 0; st < nsteps; st += NB) {
+#pragma unroll
+    for (uint32_t j = 0; j < NB; ++j) {
+      load_step(st + j + NB - 1, S[(j + NB - 1) % NB]);
+      if (st + j < nsteps) {
+        decode_step(st + j, S[j], (st + j) & 1);
+        lds_barrier();
+        mfma_step((st + j) & 1, S[j]);
+      }
     }
   }
 
@@ -775,14 +783,18 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Step buffers per M tile size (ring depth of the prefetch). Measured at
+// M = 16 / 32 / 128: two beat three (register pressure).
+constexpr int kNB16 = 2, kNB32 = 2, kNB64 = 2;
+
 template <bool DENSE>
 hipError_t launch_mfmau(const GemmArgs &a, hipStream_t s) {
   const uint32_t MT = mfmau_tile_m(a.M);
   const dim3 grid(a.N / kStrip, a.ksplit, (a.M + MT - 1) / MT);
   switch (MT) {
-    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, 4, DENSE>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, 4, DENSE>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfmau<64, 8, DENSE>), grid, dim3(512), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, 4, DENSE, kNB16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, 4, DENSE, kNB32>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfmau<64, 8, DENSE, kNB64>), grid, dim3(512), 0, s, a); break;
   }
   return hipGetLastError();
 }
