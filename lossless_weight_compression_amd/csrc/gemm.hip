@@ -349,20 +349,22 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
     u32x2 sm[RB];
     u32x3 q[RB];
   };
-  // Loads are issued unconditionally from a clamped row (see k_gemm_mfmau):
-  // loads under branches would make the next batch's prefetch block the
-  // current batch's decode.
+  // Loads are issued on every path (see k_gemm_mfmau): loads under branches
+  // make the compiler wait for all outstanding loads, the next batch's
+  // prefetch included. Rows past the last one load from past the
+  // descriptor's range (zeros, no memory access).
   auto load_batch = [&](uint32_t r0, Batch &bt) {
 #pragma unroll
     for (uint32_t j = 0; j < RB; ++j) {
       const uint32_t r = min(r0 + j, nrows - 1);
+      const uint32_t dead = r0 + j < nrows ? 0u : 0x80000000u;
       const uint32_t off = __builtin_amdgcn_readlane(r_off, r);
       const uint32_t meta = __builtin_amdgcn_readlane(r_meta, r);
       const uint32_t w = (meta >> 8) & 15u;
       const uint32_t pb = off + ((meta >> 16) + lane) * w;
       const uint32_t row_sm = kHeaderBytes + (kw0 + r) * N + col0;   // uniform
-      bt.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, row_sm, 0);
-      bt.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
+      bt.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (8 * lane) | dead, row_sm, 0);
+      bt.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
     }
   };
   auto compute_batch = [&](uint32_t r0, const Batch &bt) {
@@ -412,12 +414,12 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
     }
   };
   Batch bA, bB;
-  if (nrows) load_batch(0, bA);
+  load_batch(0, bA);
   for (uint32_t r0 = 0; r0 < nrows; r0 += 2 * RB) {
-    if (r0 + RB < nrows) load_batch(r0 + RB, bB);
+    load_batch(r0 + RB, bB);
     compute_batch(r0, bA);
-    if (r0 + 2 * RB < nrows) load_batch(r0 + 2 * RB, bA);
-    if (r0 + RB < nrows) compute_batch(r0 + RB, bB);
+    load_batch(r0 + 2 * RB, bA);
+    compute_batch(r0 + RB, bB);   // rows past nrows are skipped inside
   }
   for (uint32_t w = 0; w < 4; ++w) {
     if (wave == w) {
