@@ -12,25 +12,30 @@
 // blocks of that segment. Every block of W is full (N % B == 0), so a block's
 // payload is w * B / 8 bytes.
 //
-//  * M < 16  (k_gemm_valu): HBM-bound streaming. A wave owns a 512-column
-//    strip (lane: 8 columns) and a run of 64 rows; a prologue finds every
-//    row's block offset, meta word and X[:, row] with independent loads (one
-//    row per lane), then rows are broadcast with v_readlane and decoded in
-//    registers, two batches of rows in flight, with M x 8 fp32 FMAs per row.
-//    The four waves of a workgroup reduce in LDS in a fixed order.
-//  * M >= 16 (k_gemm_mfma): a 128-column x 32-row W tile is decoded into LDS
-//    as BF16 per K step (two groups per thread), the X tile is staged in LDS,
-//    and v_mfma_f32_16x16x32_bf16 accumulates in fp32; the next step's
-//    compressed bytes are loaded while the current step's MFMAs run.
-//  * split K: workgroups over K ranges write fp32 partial tiles; the last
-//    workgroup to finish a tile (atomic arrival counter) adds the partials in
-//    K order, writes Y and resets the counter -- one launch, deterministic.
+// Small M (below kMfmaMinM = 5) runs on VALU FMAs, larger M on MFMA; above
+// that crossover the MFMA kernels' cost hardly depends on M (measured on a
+// 4096 x 14336 W: M = 4 31.5 us on VALU vs 33.1 on MFMA, M = 5 33.7 vs 33.4,
+// M = 15 68.3 vs 36.1).
+//  * k_gemm_rowu (small M, B >= 512): a wave owns a 512-column strip and 32
+//    rows; every row's width, base and block offset are wave-uniform, so
+//    codes come in with one buffer load per lane and row and the byte planes
+//    turn into fp32 with v_perm; M x 8 fp32 FMAs per row.
+//  * k_gemm_mfmau (larger M, B >= 512, or dense W): wave-uniform rows are
+//    decoded into k-pair dwords in an LDS tile, B fragments of
+//    v_mfma_f32_16x16x32_bf16 are read from it, A fragments are X rows.
+//  * k_gemm_valu / k_gemm_mfma: the same two schemes for B < 512, where a
+//    512-column run spans several blocks and each lane finds its own block.
+//  * split K: workgroups over K ranges write fp32 partial slices, and
+//    k_splitk_reduce, launched next on the same stream, adds them in K order
+//    (deterministic).
 #include "enc_common.h"
 #include "group_math.h"
 
 namespace enc {
 namespace {
 
+constexpr uint32_t kMfmaMinM = 5;              // smallest M routed to the MFMA kernels
+static_assert(kMfmaMinM == 5, "the VALU launchers instantiate M = 1..4");
 constexpr uint32_t kStrip = 512;               // VALU path: columns per workgroup
 constexpr uint32_t kValuRowsPerWave = 64;
 constexpr uint32_t kValuRows = 4 * kValuRowsPerWave;
@@ -184,7 +189,7 @@ __device__ __forceinline__ void strip_finish(const GemmArgs &a, uint32_t c, uint
 }
 
 // --------------------------------------------------------------------------
-// M < 16: VALU FMA path.
+// M < kMfmaMinM: VALU FMA path.
 // --------------------------------------------------------------------------
 template <int MM, bool DENSE>
 __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// M < 16 and B >= 512: wave-uniform rows.
+// M < kMfmaMinM and B >= 512: wave-uniform rows.
 //
 // A 512-column strip of a row lies inside one block when B >= 512, so the
 // width, base and block offset of every row a wave touches are uniform
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// M >= 16: MFMA path.
+// M >= kMfmaMinM: MFMA path.
 // --------------------------------------------------------------------------
 template <int MT, bool DENSE>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
@@ -562,7 +567,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// M >= 16 and B >= 512 (or dense W): MFMA on wave-uniform rows.
+// M >= kMfmaMinM and B >= 512 (or dense W): MFMA on wave-uniform rows.
 //
 // Output tile MT x 512 (one strip) per workgroup of WAVES waves, split over
 // K ranges. Per K step of 32 rows, wave w decodes rows [w*RPW, w*RPW + RPW)
@@ -764,8 +769,7 @@ hipError_t launch_valu(const GemmArgs &a, hipStream_t s) {
   switch (a.M) {
 #define CASE(m) \
   case m: hipLaunchKernelGGL((k_gemm_valu<m, DENSE>), grid, dim3(256), 0, s, a); break;
-    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
-    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15)
+    CASE(1) CASE(2) CASE(3) CASE(4)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
@@ -777,8 +781,7 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
   switch (a.M) {
 #define CASE(m) \
   case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(256), 0, s, a); break;
-    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
-    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15)
+    CASE(1) CASE(2) CASE(3) CASE(4)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
@@ -818,13 +821,14 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// Which kernel serves a call: 0 = generic VALU (M < 16), 1 = uniform-row VALU
-// (M < 16, compressed, B >= 512, stream below 2 GiB: 32-bit buffer offsets),
-// 2 = generic MFMA (M >= 16, B < 512), 3 = uniform-row MFMA (M >= 16, dense
-// W or B >= 512).
+// Which kernel serves a call: 0 = generic VALU (M < kMfmaMinM), 1 =
+// uniform-row VALU (M < kMfmaMinM, compressed, B >= 512, stream below 2 GiB:
+// 32-bit buffer offsets), 2 = generic MFMA (M >= kMfmaMinM, B < 512), 3 =
+// uniform-row MFMA (M >= kMfmaMinM, dense W or B >= 512).
+
 uint32_t gemm_kind(uint32_t M, bool dense, uint32_t log2b, uint64_t total) {
   const bool uniform = dense || (log2b >= 9 && total < (1ull << 31));
-  if (M >= 16) return uniform ? 3 : 2;
+  if (M >= kMfmaMinM) return uniform ? 3 : 2;
   return (!dense && uniform) ? 1 : 0;
 }
 
@@ -864,14 +868,14 @@ void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t 
 }
 
 void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows) {
-  gemm_plan_kind(M >= 16 ? 2 : 0, M, K, N, ksplit, krows);
+  gemm_plan_kind(M >= kMfmaMinM ? 2 : 0, M, K, N, ksplit, krows);
 }
 
 uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
   // the split-K partial slices of whichever kernel the call selects
   uint64_t most = 256;
   for (uint32_t kind = 0; kind < 4; ++kind) {
-    if ((kind >= 2) != (M >= 16)) continue;
+    if ((kind >= 2) != (M >= kMfmaMinM)) continue;
     uint32_t ks, kr;
     gemm_plan_kind(kind, M, K, N, &ks, &kr);
     const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
