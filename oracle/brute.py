@@ -39,12 +39,15 @@ def join(exp, sm):
     return sum(b << k for k, b in enumerate(bits))
 
 
-def width_by_search(codes):
-    """Smallest w in 0..8 with every code < 2**w."""
-    for w in range(9):
+def width_by_search(codes, allowed=range(9)):
+    """Smallest w of `allowed` (ascending) with every code < 2**w."""
+    for w in allowed:
         if all(c < (1 << w) for c in codes):
             return w
     raise ValueError("code above 255")
+
+
+POW2_WIDTHS = (0, 1, 2, 4, 8)
 
 
 def _le(v, nbytes):
@@ -61,8 +64,9 @@ def _header(flags, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
     return h + [0] * (HEADER - len(h))
 
 
-def encode(xs, B):
-    """Stream bytes for the BF16 patterns xs (list of ints) at block size B."""
+def encode(xs, B, pow2=False):
+    """Stream bytes for the BF16 patterns xs (list of ints) at block size B;
+    pow2: widths restricted to POW2_WIDTHS (stream flag 2)."""
     n = len(xs)
     raw = _header(1, B, n, 0, 0, 0, 0, 0, 0, 0, HEADER, HEADER + 2 * n)
     for x in xs:
@@ -77,7 +81,7 @@ def encode(xs, B):
         exps = [split(v)[0] for v in blk]
         base = min(exps)
         codes = [e - base for e in exps]
-        w = width_by_search(codes)
+        w = width_by_search(codes, POW2_WIDTHS if pow2 else range(9))
         bitlist = []
         for c in codes:                      # LSB first, consecutive fields
             bitlist += [(c >> b) & 1 for b in range(w)]
@@ -98,7 +102,7 @@ def encode(xs, B):
     total = payload_off + payload_bytes
     if total >= HEADER + 2 * n:
         return bytes(raw)
-    out = _header(0, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
+    out = _header(2 if pow2 else 0, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
                   payload_bytes, 0, total)
     out += [split(v)[1] for v in xs]
     out += [0] * (meta_off - len(out))
@@ -144,7 +148,8 @@ def decode(s):
 def validate(s):
     """(kind, index) of the first failing deep condition of a coded stream
     with a consistent header, restated by walking the blocks in order:
-    1 = a width above 8 (index: block), 2 = a stored segment offset that is
+    1 = a width above 8, or not a power of two in a stream flagged 2 (index:
+    block), 2 = a stored segment offset that is
     not the running total of padded payload sizes, or a payload_bytes field
     that is not the grand total (index: segment, or nseg for payload_bytes),
     3 = some base + code above 255 (index: block). (0, 0) = valid."""
@@ -155,8 +160,9 @@ def validate(s):
     meta_off, segoff_off = _get(s, 56, 8), _get(s, 64, 8)
     payload_off, payload_bytes = _get(s, 72, 8), _get(s, 80, 8)
     widths = [s[meta_off + 2 * i + 1] for i in range(nb)]
+    allowed = POW2_WIDTHS if flags == 2 else range(9)
     for i, w in enumerate(widths):
-        if w > 8:
+        if w not in allowed:
             return 1, i
     sizes = [_align(-(-min(B, n - i * B) * w // 8), 16) for i, w in enumerate(widths)]
     expected = [sum(sizes[:SEG * k]) for k in range(nseg)] + [sum(sizes)]

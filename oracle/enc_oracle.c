@@ -48,6 +48,8 @@
 #define ORC_VERSION 1u
 #define ORC_DTYPE_BF16 1u
 #define ORC_FLAG_RAW 1u
+#define ORC_FLAG_POW2 2u   /* coded stream whose widths are powers of two */
+#define ORC_OPT_POW2 1u    /* encoder option: round widths up to 0, 1, 2, 4 or 8 */
 
 /* status codes returned by the oracle (negative = failure) */
 #define ORC_OK 0
@@ -98,6 +100,24 @@ unsigned orc_bit_width(unsigned r) {
   return w;
 }
 
+/* The width variant that keeps only powers of two ("bit-width quantization"
+ * with "hierarchical halving bit-packing", ENEC Abstract, read as: the width
+ * of a block is rounded up to the next of 0, 1, 2, 4, 8, so that a byte holds
+ * exactly 8, 4, 2 or 1 codes). Found by doubling from 1. */
+unsigned orc_pow2_width(unsigned r) {
+  unsigned w = orc_bit_width(r);
+  if (w == 0) return 0;
+  unsigned p = 1;
+  while (p < w) p *= 2;
+  return p;
+}
+
+static int width_allowed(unsigned w, uint32_t flags) {
+  if (w > 8) return 0;
+  if ((flags & ORC_FLAG_POW2) && w != 0 && w != 1 && w != 2 && w != 4 && w != 8) return 0;
+  return 1;
+}
+
 /* ---------------------------------------------------------------------------
  * Layout of a non-RAW stream for n elements and block size B.
  * ------------------------------------------------------------------------- */
@@ -141,8 +161,8 @@ static int block_size_ok(uint32_t B) { return B >= 8 && B <= 4096 && B % 8 == 0;
  * quantization" read as the minimal width of the transformed values).
  * Writes base[nb], width[nb]. Returns nb, or a negative status.
  * ------------------------------------------------------------------------- */
-int64_t orc_block_params(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *base,
-                         uint8_t *width) {
+int64_t orc_block_params_opts(const uint16_t *x, uint64_t n, uint32_t B, uint32_t opts,
+                              uint8_t *base, uint8_t *width) {
   if (!block_size_ok(B)) return ORC_E_ARG;
   uint64_t nb = (n + B - 1) / B;
   for (uint64_t i = 0; i < nb; i++) {
@@ -154,15 +174,20 @@ int64_t orc_block_params(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *bas
       if (e > hi) hi = e;
     }
     base[i] = (uint8_t)lo;
-    width[i] = (uint8_t)orc_bit_width(hi - lo);
+    width[i] = (uint8_t)((opts & ORC_OPT_POW2) ? orc_pow2_width(hi - lo) : orc_bit_width(hi - lo));
   }
   return (int64_t)nb;
+}
+
+int64_t orc_block_params(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *base,
+                         uint8_t *width) {
+  return orc_block_params_opts(x, n, B, 0, base, width);
 }
 
 /* Size in bytes of the stream that orc_encode writes for x (RAW fallback
  * included). Closed form of the layout: header + aligned sections + sum of
  * padded block payloads; RAW when that is not smaller than header + 2n. */
-int64_t orc_stream_size(const uint16_t *x, uint64_t n, uint32_t B) {
+int64_t orc_stream_size_opts(const uint16_t *x, uint64_t n, uint32_t B, uint32_t opts) {
   if (!block_size_ok(B)) return ORC_E_ARG;
   uint64_t raw_total = ORC_HEADER_BYTES + 2 * n;
   if (n == 0) return (int64_t)raw_total;
@@ -173,13 +198,17 @@ int64_t orc_stream_size(const uint16_t *x, uint64_t n, uint32_t B) {
     free(w);
     return ORC_E_NOMEM;
   }
-  orc_block_params(x, n, B, base, w);
+  orc_block_params_opts(x, n, B, opts, base, w);
   uint64_t payload = 0;
   for (uint64_t i = 0; i < L.nb; i++) payload += orc_block_payload_bytes(w[i], block_len(n, B, i));
   free(base);
   free(w);
   uint64_t total = L.payload_off + payload;
   return (int64_t)(total >= raw_total ? raw_total : total);
+}
+
+int64_t orc_stream_size(const uint16_t *x, uint64_t n, uint32_t B) {
+  return orc_stream_size_opts(x, n, B, 0);
 }
 
 static void write_header(uint8_t *h, uint32_t flags, uint32_t B, uint64_t n, uint64_t nb,
@@ -225,10 +254,12 @@ static unsigned get_bit(const uint8_t *q, uint64_t k) { return (q[k >> 3] >> (k 
  *  5. pack each block's codes at its fixed width, LSB first;
  *  6. fall back to a verbatim (RAW) stream when that is not larger.
  * ------------------------------------------------------------------------- */
-int64_t orc_encode(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *out, uint64_t cap) {
+int64_t orc_encode_opts(const uint16_t *x, uint64_t n, uint32_t B, uint32_t opts, uint8_t *out,
+                        uint64_t cap) {
   if (!block_size_ok(B)) return ORC_E_ARG;
   if (n > 0 && x == NULL) return ORC_E_ARG;
-  int64_t size = orc_stream_size(x, n, B);
+  if (opts & ~ORC_OPT_POW2) return ORC_E_ARG;
+  int64_t size = orc_stream_size_opts(x, n, B, opts);
   if (size < 0) return size;
   if ((uint64_t)size > cap) return ORC_E_CAPACITY;
   uint64_t raw_total = ORC_HEADER_BYTES + 2 * n;
@@ -250,7 +281,7 @@ int64_t orc_encode(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *out, uint
     free(psize);
     return ORC_E_NOMEM;
   }
-  orc_block_params(x, n, B, base, w);
+  orc_block_params_opts(x, n, B, opts, base, w);
   for (uint64_t i = 0; i < L.nb; i++) psize[i] = orc_block_payload_bytes(w[i], block_len(n, B, i));
 
   memset(out, 0, (size_t)size);
@@ -285,12 +316,17 @@ int64_t orc_encode(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *out, uint
     pos += psize[i];
   }
 
-  write_header(out, 0, B, n, L.nb, L.nseg, L.sm_off, L.meta_off, L.segoff_off, L.payload_off,
-               payload_bytes, 0, L.payload_off + payload_bytes);
+  write_header(out, (opts & ORC_OPT_POW2) ? ORC_FLAG_POW2 : 0, B, n, L.nb, L.nseg, L.sm_off,
+               L.meta_off, L.segoff_off, L.payload_off, payload_bytes, 0,
+               L.payload_off + payload_bytes);
   free(base);
   free(w);
   free(psize);
   return size;
+}
+
+int64_t orc_encode(const uint16_t *x, uint64_t n, uint32_t B, uint8_t *out, uint64_t cap) {
+  return orc_encode_opts(x, n, B, 0, out, cap);
 }
 
 /* ---------------------------------------------------------------------------
@@ -329,7 +365,7 @@ static int parse_header_fields(const uint8_t *s, uint64_t bytes, orc_header *h) 
       return ORC_E_STREAM;
     return ORC_OK;
   }
-  if (h->flags != 0 || h->n == 0) return ORC_E_STREAM;
+  if ((h->flags != 0 && h->flags != ORC_FLAG_POW2) || h->n == 0) return ORC_E_STREAM;
   orc_layout L = layout_of(h->n, h->B);
   if (h->nb != L.nb || h->nseg != L.nseg || h->sm_off != L.sm_off || h->meta_off != L.meta_off ||
       h->segoff_off != L.segoff_off || h->payload_off != L.payload_off || h->raw_off != 0 ||
@@ -339,14 +375,15 @@ static int parse_header_fields(const uint8_t *s, uint64_t bytes, orc_header *h) 
 }
 
 /* The two structural conditions on the data sections of a coded stream with
- * a consistent header: every width is at most 8 (kind 1, index = first such
- * block), and each stored segment offset equals the sum of the padded
+ * a consistent header: every width is at most 8, and a power of two in a
+ * stream flagged so (kind 1, index = first other block), and each stored
+ * segment offset equals the sum of the padded
  * payload sizes of all earlier blocks, with payload_bytes equal to the sum
  * over all blocks (kind 2, index = first wrong stored offset; index nseg
  * stands for payload_bytes). Returns 0 when both hold. */
 static int check_widths_offsets(const uint8_t *s, const orc_header *h, uint64_t *index) {
   for (uint64_t i = 0; i < h->nb; i++) {
-    if (s[h->meta_off + 2 * i + 1] > 8) {
+    if (!width_allowed(s[h->meta_off + 2 * i + 1], h->flags)) {
       *index = i;
       return 1;
     }

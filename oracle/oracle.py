@@ -55,6 +55,16 @@ def lib():
         L.orc_stream_size.restype = ctypes.c_int64
         L.orc_encode.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32, _u8p, ctypes.c_uint64]
         L.orc_encode.restype = ctypes.c_int64
+        L.orc_encode_opts.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, _u8p,
+                                      ctypes.c_uint64]
+        L.orc_encode_opts.restype = ctypes.c_int64
+        L.orc_stream_size_opts.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32]
+        L.orc_stream_size_opts.restype = ctypes.c_int64
+        L.orc_pow2_width.argtypes = [ctypes.c_uint]
+        L.orc_pow2_width.restype = ctypes.c_uint
+        L.orc_block_params_opts.argtypes = [_u16p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                            _u8p, _u8p]
+        L.orc_block_params_opts.restype = ctypes.c_int64
         L.orc_stream_elements.argtypes = [_u8p, ctypes.c_uint64]
         L.orc_stream_elements.restype = ctypes.c_int64
         L.orc_decode.argtypes = [_u8p, ctypes.c_uint64, _u16p, ctypes.c_uint64]
@@ -109,32 +119,38 @@ def block_payload_bytes(w, L):
     return lib().orc_block_payload_bytes(int(w), int(L))
 
 
-def block_params(x, B):
+def pow2_width(r):
+    return lib().orc_pow2_width(int(r))
+
+
+def block_params(x, B, pow2=False):
     """(base[nb], width[nb]) as uint8 arrays."""
     x = _u16(x)
     nb = -(-x.size // B)
     base = np.zeros(max(nb, 1), np.uint8)
     w = np.zeros(max(nb, 1), np.uint8)
-    r = lib().orc_block_params(_ptr(x, _u16p), x.size, B, _ptr(base, _u8p), _ptr(w, _u8p))
+    r = lib().orc_block_params_opts(_ptr(x, _u16p), x.size, B, 1 if pow2 else 0, _ptr(base, _u8p),
+                                    _ptr(w, _u8p))
     if r < 0:
         raise OracleError("block_params failed: %d" % r)
     return base[:nb], w[:nb]
 
 
-def stream_size(x, B):
+def stream_size(x, B, pow2=False):
     x = _u16(x)
-    r = lib().orc_stream_size(_ptr(x, _u16p), x.size, B)
+    r = lib().orc_stream_size_opts(_ptr(x, _u16p), x.size, B, 1 if pow2 else 0)
     if r < 0:
         raise OracleError("stream_size failed: %d" % r)
     return int(r)
 
 
-def encode(x, B):
-    """Stream bytes (np.uint8 array) for the BF16 patterns x at block size B."""
+def encode(x, B, pow2=False):
+    """Stream bytes (np.uint8 array) for the BF16 patterns x at block size B;
+    pow2: widths rounded up to 0, 1, 2, 4 or 8 (stream flag 2)."""
     x = _u16(x)
-    size = stream_size(x, B)
+    size = stream_size(x, B, pow2)
     out = np.empty(size, np.uint8)
-    r = lib().orc_encode(_ptr(x, _u16p), x.size, B, _ptr(out, _u8p), out.size)
+    r = lib().orc_encode_opts(_ptr(x, _u16p), x.size, B, 1 if pow2 else 0, _ptr(out, _u8p), out.size)
     if r < 0:
         raise OracleError("encode failed: %d" % r)
     assert r == size

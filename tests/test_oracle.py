@@ -510,3 +510,88 @@ def test_raw_tie_goes_raw(orc):
     s = orc.encode(below, 512)
     assert s.size == 2816 + 64 * 23 and int.from_bytes(bytes(s[8:12]), "little") == 0
     assert np.array_equal(orc.decode(s), below)
+
+
+# ------------------------------------------------- power-of-two width variant
+def test_pow2_width_rule_exhaustive(orc):
+    # smallest of 0, 1, 2, 4, 8 bits that holds r, three ways: the oracle's
+    # doubling, a search over the allowed set, and 2 ** ceil(log2(bitlen))
+    for r in range(256):
+        bl = int(r).bit_length()
+        closed = 0 if r == 0 else 1 << (bl - 1).bit_length()
+        assert orc.pow2_width(r) == brute.width_by_search([r], brute.POW2_WIDTHS) == closed, r
+        assert orc.pow2_width(r) >= orc.bit_width(r)
+
+
+def test_pow2_hand_block(orc):
+    # blocks of 64 values with exponents 120..125 repeated: base 120, codes
+    # t mod 6, max 5 -> minimal width 3, power-of-two width 4. At width 4
+    # code t is nibble t of the block payload: byte k = d[2k] | d[2k+1] << 4,
+    # 32 bytes (a multiple of 16: no padding). 100 such blocks keep the
+    # stream below the RAW size.
+    codes = [t % 6 for t in range(64)]
+    n = 64 * 100
+    x = _bits_from_exps([120 + codes[t % 64] for t in range(n)], np.arange(n) * 7 % 256)
+    base, w = orc.block_params(x, 64)
+    assert (int(base[0]), int(w[0])) == (120, 3)
+    base, w = orc.block_params(x, 64, pow2=True)
+    assert (int(base[0]), int(w[0])) == (120, 4)
+    s = orc.encode(x, 64, pow2=True)
+    assert int.from_bytes(bytes(s[8:12]), "little") == 2                  # flag: powers of two
+    pay = int.from_bytes(bytes(s[72:80]), "little")
+    want = [codes[2 * k] | codes[2 * k + 1] << 4 for k in range(32)]
+    assert s[pay:pay + 32].tolist() == want
+    assert int.from_bytes(bytes(s[80:88]), "little") == 100 * 32
+    assert np.array_equal(orc.decode(s), x)
+    assert orc.validate(s) == (0, 0)
+
+
+@pytest.mark.parametrize("B,n", [(24, 200 * 24 + 5), (8, 4096 + 3), (40, 64 * 40 * 2 + 17),
+                                 (64, 3000)])
+def test_pow2_brute_force(orc, B, n):
+    rng = np.random.default_rng([12, B, n])
+    exps = np.full(n, 118, np.int64)
+    hot = rng.random(n) < 0.03
+    exps[hot] += rng.integers(0, 40, int(hot.sum()))        # widths 1..6 before rounding
+    x = _bits_from_exps(exps, rng.integers(0, 256, n))
+    s = orc.encode(x, B, pow2=True)
+    assert int.from_bytes(bytes(s[8:12]), "little") == 2
+    assert bytes(s) == brute.encode([int(v) for v in x], B, pow2=True)
+    assert np.array_equal(orc.decode(s), x)
+    _, w = orc.block_params(x, B, pow2=True)
+    assert set(np.unique(w)) <= {0, 1, 2, 4, 8}
+
+
+@pytest.mark.parametrize("kind", ["laplace", "mixture", "uniform16"])
+def test_pow2_sizes_and_round_trip(orc, kind):
+    x = synth.stress(kind, (64, 2048))
+    for B in (256, 512):
+        s2, s = orc.encode(x, B, pow2=True), orc.encode(x, B)
+        assert np.array_equal(orc.decode(s2), x.reshape(-1))
+        assert s2.size >= s.size                          # widths only grow
+        _, w = orc.block_params(x, B, pow2=True)
+        _, wmin = orc.block_params(x, B)
+        nb = w.size
+        L = [min(B, x.size - i * B) for i in range(nb)]
+        pay = sum(-(-(-(-int(wi) * li // 8)) // 16) * 16 for wi, li in zip(w, L))
+        a = lambda v: -(-v // 256) * 256
+        closed = 256 + a(x.size) + a(2 * nb) + a(8 * (-(-nb // 64))) + pay
+        raw = 256 + 2 * x.size
+        assert s2.size == (raw if closed >= raw else closed)
+        flags = int.from_bytes(bytes(s2[8:12]), "little")
+        assert flags == (1 if closed >= raw else 2)
+        assert np.all(w >= wmin)
+
+
+def test_pow2_validate(orc):
+    x = synth.gaussian_bits((4, 1000), 0.02, 97, 0)
+    s = orc.encode(x, 64, pow2=True)
+    assert orc.validate(s) == (0, 0)
+    meta = int.from_bytes(bytes(s[56:64]), "little")
+    ws = s[meta + 1: meta + 2 * 40: 2]
+    i = int(np.flatnonzero(ws == 4)[0])
+    b = s.copy(); b[meta + 2 * i + 1] = 3                 # 3 is not a power of two
+    assert orc.validate(b)[0] == 1 and orc.validate(b)[1] <= i
+    assert brute.validate(bytes(b)) == orc.validate(b)
+    c = orc.encode(x, 64)                                  # the same width is fine unflagged
+    assert orc.validate(c) == (0, 0)
