@@ -46,6 +46,8 @@ def parse():
                    help="decoder layers in the set (32 = the full 8B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-pow2", action="store_true",
+                   help="skip the power-of-two-width variant of the decode step")
     p.add_argument("--cpu-sample-tensors", type=int, default=21,
                    help="first tensors of the set the CPU oracle decodes (bounded sample)")
     return p.parse_args()
@@ -166,6 +168,42 @@ def main():
     per_tensor_ms = float(np.median(pt_ms))
     log("per-tensor launches: %.3f ms/step" % per_tensor_ms)
 
+    # ---- variant: power-of-two widths (stream flag 2), same tensors ---------
+    pow2 = None
+    if not args.no_pow2:
+        p2_streams, p2_total = [], 0
+        for i in idx:
+            x = synth.set8b_tensor_gpu(i, device=dev)
+            c, inf = enc.enc_compress(x, B, pow2_widths=True)
+            p2_streams.append((c.clone(), inf))
+            p2_total += inf.total_bytes
+            del x, c
+        p2_read = sum((2 * inf.n_elems if inf.flags == 1 else
+                       inf.n_elems + 2 * inf.n_blocks + 8 * inf.n_segments + inf.payload_bytes)
+                      for _, inf in p2_streams)
+        p2_table = enc.enc_batch_prepare([(c, inf, o) for (c, inf), o in zip(p2_streams, outs)])
+        for _ in range(args.warmup):
+            enc.enc_decompress_batch(p2_table, count)
+        ms = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            enc.enc_decompress_batch(p2_table, count)
+            e1.record(stream)
+            ms.append((e0, e1))
+        torch.cuda.synchronize()
+        p2_ms = float(np.mean([a.elapsed_time(b) for a, b in ms]))
+        pow2 = {
+            "compression_ratio": round(2 * n_total / p2_total, 5),
+            "decode_ms_per_step": round(p2_ms, 4),
+            "bf16_out_gbs": round(out_bytes / (p2_ms * 1e-3) / 1e9, 1),
+            "hbm_gbs": round((p2_read + out_bytes) / (p2_ms * 1e-3) / 1e9, 1),
+        }
+        log("power-of-two widths: ratio %.4f, decode %.3f ms/step"
+            % (pow2["compression_ratio"], p2_ms))
+        del p2_streams, p2_table
+        torch.cuda.empty_cache()
+
     # ---- correctness of what was timed (outside the timed region) ------------
     for k, i in enumerate(idx):
         x = synth.set8b_tensor_gpu(i, device=dev).reshape(-1)
@@ -234,6 +272,9 @@ def main():
         },
     }
 
+    if pow2 is not None:
+        result["pow2_widths"] = pow2
+
     if not args.no_gemm:
         result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream)
 
@@ -270,7 +311,7 @@ def _graph_time_us(fn, torch, calls=8, replays=20):
 
 def bench_gemm(enc, synth, torch, np, dev, stream):
     """Y = X W with W 4096x14336 compressed (B=512) vs the same GEMM on the
-    uncompressed W, M in {1, 16, 128}. Four rotating weight copies keep the
+    uncompressed W, M from 1 to 256. Four rotating weight copies keep the
     working set above the 256 MB last-level cache; times are GPU time per
     call from HIP-graph replays, and every replayed result is checked
     bit-exactly against an eager call (the fused path is deterministic)."""
@@ -282,7 +323,7 @@ def bench_gemm(enc, synth, torch, np, dev, stream):
     out = {"shape": "X[M,4096] x W[4096,14336], W compressed at B=512",
            "timing": "GPU time per call, HIP-graph replay of 8 calls x 20",
            "w_bytes_compressed": comps[0][1].total_bytes, "w_bytes_dense": 2 * K * N}
-    for M in (1, 16, 128):
+    for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):
         X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
         Xb = X.view(torch.bfloat16)
         Ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(copies)]

@@ -18,7 +18,8 @@
  *
  * Stream format (little-endian; all pad bytes zero):
  *   [0, 256)            header: "ENCB", u16 version=1, u16 dtype=1 (BF16),
- *                       u32 flags (bit 0 = RAW), u32 block_size, u32 64,
+ *                       u32 flags (0 = coded, 1 = RAW, 2 = coded with
+ *                       power-of-two widths), u32 block_size, u32 64,
  *                       u32 0, then u64 n_elems, n_blocks, n_segments, sm_off,
  *                       meta_off, segoff_off, payload_off, payload_bytes,
  *                       raw_off, total_bytes; bytes 104..255 zero.
@@ -30,8 +31,12 @@
  *   payload_off         per block, ceil(width * len / 8) bytes rounded up to
  *                       16: the codes exponent - base, width bits each, packed
  *                       LSB first in element order.
- *   RAW streams (flags bit 0): header, then the n input values verbatim at
+ *   RAW streams (flags 1): header, then the n input values verbatim at
  *   raw_off = 256; chosen when the coded stream would not be smaller.
+ *   Flags 2: the widths were rounded up to 0, 1, 2, 4 or 8 (ENEC Abstract:
+ *   bit-width quantization with hierarchical halving bit-packing, read as
+ *   power-of-two widths, so a byte holds exactly 8, 4, 2 or 1 codes); the
+ *   layout is otherwise identical and every entry point reads such streams.
  *   A stream is valid only if every decoded exponent base + code is <= 255
  *   (always true for a stream written from BF16 input by these rules).
  *
@@ -97,6 +102,15 @@ uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size);
 enc_status enc_compress(const uint16_t *d_in, uint64_t n_elems, uint32_t block_size, void *d_out,
                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream,
                         enc_info *h_info);
+
+/* enc_compress with options (bitwise or; 0 = enc_compress):
+ *   ENC_OPT_POW2_WIDTHS  round every block width up to 0, 1, 2, 4 or 8 and
+ *                        write flags 2 (if the result is RAW, flags 1).
+ * Unknown option bits: ENC_ERR_INVALID_ARG. */
+enum { ENC_OPT_POW2_WIDTHS = 1 };
+enc_status enc_compress_ex(const uint16_t *d_in, uint64_t n_elems, uint32_t block_size,
+                           uint32_t options, void *d_out, uint64_t out_capacity, void *d_ws,
+                           uint64_t ws_bytes, void *stream, enc_info *h_info);
 
 /* Parse and check a stream header held in host memory (header_bytes >= 256)
  * for a stream of comp_bytes bytes. Checks magic, version, dtype, flags,
@@ -165,7 +179,8 @@ enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uin
 
 /* Deep check of a stream's device data (the header is checked on the host
  * by enc_parse_header / enc_read_info). In this order of precedence:
- *   ENC_CHECK_WIDTH    some block width is above 8;
+ *   ENC_CHECK_WIDTH    some block width is above 8 (or, in a flags-2
+ *                      stream, not a power of two);
  *   ENC_CHECK_OFFSETS  a stored segment offset differs from the exclusive
  *                      prefix sum of the padded block payload sizes, or
  *                      payload_bytes differs from their total (ENEC

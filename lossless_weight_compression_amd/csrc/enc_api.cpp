@@ -138,7 +138,7 @@ enc_status check_info(const enc_info *i) {
       return fail(ENC_ERR_BAD_STREAM, "inconsistent RAW header");
     return ENC_OK;
   }
-  if (i->flags != 0) return fail(ENC_ERR_BAD_STREAM, "unknown flags 0x%x", i->flags);
+  if (i->flags != 0 && i->flags != 2) return fail(ENC_ERR_BAD_STREAM, "unknown flags 0x%x", i->flags);
   if (log2_block(i->block_size) < 0)
     return fail(ENC_ERR_UNSUPPORTED, "block size %u (library supports 128..4096, powers of two)",
                 i->block_size);
@@ -174,12 +174,13 @@ DecodeDesc desc_of(const void *d_comp, const enc_info &i, uint16_t *d_out) {
   return d;
 }
 
-enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t payload) {
+enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t payload,
+                    uint32_t pow2) {
   enc_info i;
   memset(&i, 0, sizeof i);
   i.version = 1;
   i.dtype = 1;
-  i.flags = 0;
+  i.flags = pow2 ? 2 : 0;
   i.block_size = block_size;
   i.n_elems = n;
   i.n_blocks = L.nb;
@@ -208,12 +209,13 @@ uint32_t lookback_spin_limit() {
 // land outside the buffer and the RAW fallback can simply overwrite it.
 // Returns ENC_ERR_HIP with *gave_up set if a look-back wait gave up; the
 // caller then runs the two-pass encoder, which rewrites every byte.
-enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_size, const Layout &L,
-                             uint8_t *d_out, uint64_t cap, uint8_t *d_ws, hipStream_t s,
-                             enc_info *h_info, bool *gave_up) {
+enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_size, uint32_t pow2,
+                             const Layout &L, uint8_t *d_out, uint64_t cap, uint8_t *d_ws,
+                             hipStream_t s, enc_info *h_info, bool *gave_up) {
   *gave_up = false;
   EncodeArgs a;
   memset(&a, 0, sizeof a);
+  a.pow2 = pow2;
   a.in = d_in;
   a.out = d_out;
   a.n = n;
@@ -251,7 +253,7 @@ enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_si
     i = raw_info(n, block_size);
     st = launched(launch_encode_raw(d_in, d_out, n, header_of(i), s), s, "raw copy launch");
   } else {
-    i = coded_info(n, block_size, L, payload);
+    i = coded_info(n, block_size, L, payload, a.pow2);
     st = launched(launch_encode_pads(a, header_of(i), s), s, "header kernel launch");
   }
   if (st != ENC_OK) return st;
@@ -283,7 +285,16 @@ uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size) {
 enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, void *d_out,
                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream,
                         enc_info *h_info) {
+  return enc_compress_ex(d_in, n, block_size, 0, d_out, out_capacity, d_ws, ws_bytes, stream, h_info);
+}
+
+enc_status enc_compress_ex(const uint16_t *d_in, uint64_t n, uint32_t block_size, uint32_t options,
+                           void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
+                           void *stream, enc_info *h_info) {
   clear_err();
+  if (options & ~(uint32_t)ENC_OPT_POW2_WIDTHS)
+    return fail(ENC_ERR_INVALID_ARG, "unknown options 0x%x", options);
+  const uint32_t pow2 = (options & ENC_OPT_POW2_WIDTHS) ? 1u : 0u;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!h_info) return fail(ENC_ERR_INVALID_ARG, "h_info is NULL");
   if (!d_out) return fail(ENC_ERR_INVALID_ARG, "d_out is NULL");
@@ -313,9 +324,9 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
   const Layout L = layout_of(n, block_size);
   if (out_capacity >= raw_total && L.payload_off <= raw_total) {
     bool gave_up = false;
-    const enc_status st = compress_one_pass(d_in, n, block_size, L, static_cast<uint8_t *>(d_out),
-                                            out_capacity, static_cast<uint8_t *>(d_ws), s, h_info,
-                                            &gave_up);
+    const enc_status st = compress_one_pass(d_in, n, block_size, pow2, L,
+                                            static_cast<uint8_t *>(d_out), out_capacity,
+                                            static_cast<uint8_t *>(d_ws), s, h_info, &gave_up);
     if (!gave_up) return st;
     clear_err();   // fall through to the two-pass encoder
   }
@@ -334,6 +345,7 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
   a.segoff_off = L.segoff_off;
   a.payload_off = L.payload_off;
   a.log2b = (uint32_t)lb;
+  a.pow2 = pow2;
 
   hipError_t e = launch_encode_params(a, s);
   if (e != hipSuccess) return hip_fail(e, "width kernel launch");
@@ -359,7 +371,7 @@ enc_status enc_compress(const uint16_t *d_in, uint64_t n, uint32_t block_size, v
     if (out_capacity < coded_total)
       return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
                   (unsigned long long)out_capacity, (unsigned long long)coded_total);
-    i = coded_info(n, block_size, L, payload);
+    i = coded_info(n, block_size, L, payload, a.pow2);
     e = launch_encode_pack(a, s);
     if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
     const enc_status st = launched(launch_encode_finish(a, header_of(i), s), s,
@@ -525,7 +537,7 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
   if ((uint64_t)K * N != h_winfo->n_elems)
     return fail(ENC_ERR_SHAPE, "K*N=%llu but the stream holds %llu elements",
                 (unsigned long long)K * N, (unsigned long long)h_winfo->n_elems);
-  if (h_winfo->flags == 0 && N % h_winfo->block_size)
+  if (h_winfo->flags != 1 && N % h_winfo->block_size)
     return fail(ENC_ERR_UNSUPPORTED, "N=%u not a multiple of the block size %u", N,
                 h_winfo->block_size);
   GemmArgs a;
@@ -585,6 +597,7 @@ enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, 
   a.payload_off = h_info->payload_off;
   a.payload_bytes = h_info->payload_bytes;
   a.log2b = (uint32_t)log2_block(h_info->block_size);
+  a.pow2 = h_info->flags == 2;
   hipError_t e = hipMemsetAsync(d_ws, 0xFF, 3 * sizeof(unsigned long long), s);
   if (e != hipSuccess) return hip_fail(e, "result initialisation");
   e = launch_validate(a, s);
@@ -594,7 +607,8 @@ enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, 
   if (e != hipSuccess) return hip_fail(e, "result read-back");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "stream synchronize");
-  static const char *const what[3] = {"block %llu has a width above 8",
+  static const char *const what[3] = {"block %llu has a width above 8 (or not a power of two "
+                                      "in a stream that declares power-of-two widths)",
                                       "stored segment offset %llu is not the prefix sum of the "
                                       "block sizes (index n_segments = payload_bytes)",
                                       "block %llu decodes an exponent above 255"};

@@ -32,6 +32,16 @@ constexpr uint32_t kMinLog2B = 7, kMaxLog2B = 12;
 
 __host__ __device__ inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+// Block width of a code range r: the bits of r, or, for streams with
+// power-of-two widths, the next of 0, 1, 2, 4, 8 ("ENEC: A Lossless AI Model
+// Compression Method Enabling Fast Inference on Ascend NPUs", Abstract:
+// bit-width quantization).
+__host__ __device__ inline uint32_t block_width(uint32_t r, uint32_t pow2) {
+  uint32_t w = 0;
+  while (r >> w) ++w;
+  return pow2 ? (w <= 2 ? w : (w <= 4 ? 4u : 8u)) : w;
+}
+
 // One stream to decode (by value for a single call, in the batch table for
 // batched calls). 80 bytes.
 struct DecodeDesc {
@@ -83,6 +93,7 @@ struct EncodeArgs {
   uint64_t n, nb, nseg;
   uint64_t meta_off, segoff_off, payload_off;
   uint32_t log2b;
+  uint32_t pow2;         // 1: widths rounded up to 0, 1, 2, 4 or 8
   // single pass only
   uint64_t *status;      // one word per tile: flag (bits 63..62) | payload bytes
   uint32_t *error;       // nonzero: a look-back wait gave up
@@ -110,6 +121,7 @@ struct ValidateArgs {
   uint64_t n, nb, nseg;
   uint64_t meta_off, segoff_off, payload_off, payload_bytes;
   uint32_t log2b;
+  uint32_t pow2;         // 1: the stream declares power-of-two widths
 };
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_params(EncodeArgs a) {
     if (blk < a.nb) {
       const uint32_t base = smin[tid];
       const uint32_t r = smax[tid] - base;
-      const uint32_t w = r ? 32u - __clz(r) : 0u;
+      const uint32_t w = block_width(r, a.pow2);
       const uint32_t L = (blk + 1 == a.nb) ? (uint32_t)(a.n - ((a.nb - 1) << a.log2b)) : (1u << a.log2b);
       P = (((w * L + 7) >> 3) + 15) & ~15u;
       *reinterpret_cast<uint16_t *>(a.ws_meta + 2 * blk) = (uint16_t)(base | (w << 8));

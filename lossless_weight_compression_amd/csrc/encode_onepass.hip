@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
       if (lane < bps && blk < a.nb) {
         base = smin[lane];
         const uint32_t r = smax[lane] - base;
-        w = r ? 32u - __clz(r) : 0u;
+        w = block_width(r, a.pow2);
         const uint32_t L = (blk + 1 == a.nb) ? (uint32_t)(n - ((a.nb - 1) << log2b)) : (1u << log2b);
         P = (((w * L + 7) >> 3) + 15) & ~15u;
       }

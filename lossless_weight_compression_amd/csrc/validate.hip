@@ -1,6 +1,7 @@
 // validate.hip -- deep check of a coded stream on the device.
 //
-// A coded stream is usable only if (1) every block width is at most 8,
+// A coded stream is usable only if (1) every block width is at most 8 (and
+// a power of two in a stream that declares power-of-two widths),
 // (2) the stored segment offsets are the exclusive prefix sums of the padded
 // block payload sizes (and payload_bytes is their total), and (3) every
 // decoded exponent base + code fits in a byte. Condition (2) is what lets a
@@ -11,7 +12,7 @@
 // block minimum (same Abstract). The header itself is checked on the host.
 //
 // One wave per segment, lane j = block 64s + j:
-//  * width:   w_j > 8;
+//  * width:   w_j > 8, or not a power of two in a flag-2 stream;
 //  * offsets: stored[s+1] - stored[s] must equal the wave's sum of padded
 //             sizes (stored[nseg] means payload_bytes) and stored[0] must be
 //             0. If stored[0..k) are right and stored[k] is not, the first
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(kThreads) void k_validate(ValidateArgs a) {
       L = (blk + 1 == a.nb) ? (uint32_t)(a.n - ((a.nb - 1) << a.log2b)) : (1u << a.log2b);
       P = (((w * L + 7) >> 3) + 15) & ~15u;   // w <= 255: fits easily in 32 bits
     }
-    if (valid && w > 8) atomicMin(&a.result[0], (unsigned long long)blk);
+    if (valid && (w > 8 || (a.pow2 && (w & (w - 1)))))
+      atomicMin(&a.result[0], (unsigned long long)blk);
 
     const uint32_t incl = wave_incl_scan(P, lane);
     const uint32_t seg_sum = __shfl(incl, 63, 64);

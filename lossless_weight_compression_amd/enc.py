@@ -66,6 +66,7 @@ SIGNATURES = {
     "enc_compress_bound": (_U64, [_U64]),
     "enc_compress_workspace_bytes": (_U64, [_U64, _U32]),
     "enc_compress": (_ST, [_VP, _U64, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
+    "enc_compress_ex": (_ST, [_VP, _U64, _U32, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
     "enc_parse_header": (_ST, [_VP, _U64, _U64, _INFO_P]),
     "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
     "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
@@ -142,9 +143,13 @@ def enc_compress_workspace_bytes(n_elems, block_size):
     return int(lib().enc_compress_workspace_bytes(n_elems, block_size))
 
 
-def enc_compress(x, block_size=512, out=None, ws=None, stream=None):
+ENC_OPT_POW2_WIDTHS = 1
+
+
+def enc_compress(x, block_size=512, out=None, ws=None, stream=None, pow2_widths=False):
     """Compress the BF16 tensor x. Returns (stream bytes as a uint8 CUDA tensor
-    sliced to the stream size, EncInfo)."""
+    sliced to the stream size, EncInfo). pow2_widths: enc_compress_ex with
+    ENC_OPT_POW2_WIDTHS."""
     x = _bits(x)
     n = x.numel()
     if out is None:
@@ -152,8 +157,13 @@ def enc_compress(x, block_size=512, out=None, ws=None, stream=None):
     if ws is None:
         ws = _empty_u8(enc_compress_workspace_bytes(n, block_size), x.device)
     info = EncInfo()
-    _check(lib().enc_compress(_ptr(x), n, block_size, _ptr(out), out.numel(), _ptr(ws), ws.numel(),
-                              _stream(stream), ctypes.byref(info)))
+    if pow2_widths:
+        _check(lib().enc_compress_ex(_ptr(x), n, block_size, ENC_OPT_POW2_WIDTHS, _ptr(out),
+                                     out.numel(), _ptr(ws), ws.numel(), _stream(stream),
+                                     ctypes.byref(info)))
+    else:
+        _check(lib().enc_compress(_ptr(x), n, block_size, _ptr(out), out.numel(), _ptr(ws),
+                                  ws.numel(), _stream(stream), ctypes.byref(info)))
     return out[:info.total_bytes], info
 
 

@@ -68,6 +68,9 @@ def test_parse_oracle_headers(L, orc, B):
     assert (info.n_elems, info.n_blocks, info.n_segments) == (n, nb, -(-nb // 64))
     assert info.total_bytes == s.size
     assert info.payload_off + info.payload_bytes == s.size
+    p2 = orc.encode(x, B, pow2=True)
+    pinfo = enc.enc_parse_header(p2[:256], p2.size)
+    assert (pinfo.flags, pinfo.total_bytes) == (2, p2.size)
     raw = orc.encode(synth.random_bits(5000, 3), B)
     ri = enc.enc_parse_header(raw[:256], raw.size)
     assert (ri.flags, ri.raw_off, ri.total_bytes) == (1, 256, 256 + 10000)

@@ -210,6 +210,51 @@ def test_one_pass_and_two_pass_streams_agree(E, orc, B):
         assert np.array_equal(host_u8(c2), ref), k
 
 
+@pytest.mark.parametrize("B", [128, 512, 4096])
+def test_pow2_widths_match_oracle(E, orc, B):
+    """ENC_OPT_POW2_WIDTHS: GPU streams (single pass and two passes) equal
+    the oracle's power-of-two-width streams byte for byte; they decode to the
+    input and pass the deep check."""
+    cases = [synth.gaussian_bits((777, 1111), 0.02, 98, B),
+             synth.stress("laplace", (1024, 4100)),
+             synth.stress("mixture", (512, 4096)),
+             synth.stress("const_exp", (256, 4096)),
+             synth.random_bits(70_001, 7),                               # RAW
+             synth.tiny()[:8192 * 3 + 5]]
+    for k, x in enumerate(cases):
+        x = np.ascontiguousarray(x).reshape(-1)
+        say("pow2 widths", k, "n=%d B=%d" % (x.size, B))
+        ref = orc.encode(x, B, pow2=True)
+        xd = dev(x)
+        big = torch.empty((E.enc_compress_bound(x.size),), dtype=torch.uint8, device="cuda")
+        c1, i1 = E.enc_compress(xd, B, out=big, pow2_widths=True)
+        exact = torch.empty((ref.size,), dtype=torch.uint8, device="cuda")
+        c2, i2 = E.enc_compress(xd, B, out=exact, pow2_widths=True)
+        torch.cuda.synchronize()
+        assert i1.total_bytes == i2.total_bytes == ref.size
+        assert i1.flags == (1 if ref[8] == 1 else 2)
+        assert np.array_equal(host_u8(c1), ref), k
+        assert np.array_equal(host_u8(c2), ref), k
+        out = E.enc_decompress(c1, i1)
+        assert np.array_equal(host_u16(out), x), k
+        assert E.enc_validate(c1, i1).kind == 0
+
+
+def test_pow2_layer_full_size(E, orc):
+    x = synth.layer(names=["gate"])["gate"].reshape(-1)
+    say("pow2 widths: gate 4096x14336 B=512")
+    ref = orc.encode(x, 512, pow2=True)
+    comp, info = E.enc_compress(dev(x), 512, pow2_widths=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(comp), ref)
+    out = E.enc_decompress(comp, info)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out), x)
+    plain = orc.stream_size(x, 512)
+    say("gate ratio: minimal widths %.4f, power-of-two widths %.4f"
+        % (2 * x.size / plain, 2 * x.size / ref.size))
+
+
 def test_look_back_give_up_falls_back_to_two_passes(E, orc):
     """With the look-back allowed no second poll (ENC_LOOKBACK_SPINS=0), a
     tile that finds a predecessor unpublished gives up at once; the call must

@@ -159,3 +159,23 @@ def test_full_size_m128_sampled(E, orc):
     Y, A = orc.gemm_f64_cols(X, W, cols)
     assert_within(run_fused(E, X, comp, info, N)[:, cols], Y, A, "fused M=128")
     assert_within(run_dense(E, X, W)[:, cols], Y, A, "dense M=128")
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_pow2_width_stream(E, orc, M):
+    """A stream with power-of-two widths (flag 2) multiplies like any other:
+    one-hot rows reproduce W exactly, random X within the tolerance."""
+    K, N = 256, 2048
+    W = synth.gaussian_bits((K, N), 0.02, 203, M)
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512, pow2=True)).cuda()
+    info = E.enc_read_info(comp)
+    assert info.flags == 2
+    rng = np.random.default_rng(M)
+    X = np.zeros((M, K), np.uint16)
+    ks = rng.integers(0, K, M)
+    X[np.arange(M), ks] = 0x3F80
+    say("pow2 stream one-hot M=%d" % M)
+    assert np.array_equal(run_fused(E, X, comp, info, N), bf16_f64(W)[ks])
+    Xr = synth.gemm_activations(M, K)
+    Y, A = orc.gemm_f64(Xr, W)
+    assert_within(run_fused(E, Xr, comp, info, N), Y, A, "pow2 M=%d" % M)

@@ -117,3 +117,18 @@ def test_debug_sync_changes_nothing(E):
     for a, b in zip(*results):
         assert torch.equal(a, b)
     assert np.array_equal(results[1][1].numpy().view(np.uint16), x.reshape(-1))
+
+
+def test_pow2_stream_width_check(E, orc):
+    x = synth.gaussian_bits((64, 4096), 0.02, 99, 0)
+    s = orc.encode(x.reshape(-1), 512, pow2=True)
+    meta = int.from_bytes(bytes(s[56:64]), "little")
+    nb = int.from_bytes(bytes(s[32:40]), "little")
+    ws = s[meta + 1: meta + 2 * nb: 2]
+    i = int(np.flatnonzero(ws == 4)[3])
+    b = s.copy(); b[meta + 2 * i + 1] = 3
+    for stream in (s, b):
+        d = dev8(stream)
+        chk = E.enc_validate(d, E.enc_read_info(d))
+        assert (chk.kind, chk.index) == orc.validate(stream)
+    assert orc.validate(b)[0] == 1
