@@ -277,6 +277,7 @@ def main():
 
     if not args.no_gemm:
         result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream)
+        result["fused_gemm_nt"] = bench_gemm_nt(enc, synth, torch, np, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth, np, torch, dev, args.cpu_sample_tensors, B)
@@ -363,6 +364,50 @@ def bench_gemm(enc, synth, torch, np, dev, stream):
                 "speedup_vs_dense_same_kernel": round(td / tf, 3),
                 "speedup_vs_hipblaslt": round(tb / tf, 3),
             }
+        except Exception as e:  # the GEMM kernels report through EncError
+            out["M%d" % M] = {"error": str(e)}
+    return out
+
+
+def bench_gemm_nt(enc, synth, torch, np, dev):
+    """Y = X W^T with W in linear-layer layout [14336, 4096], compressed at
+    B=512, against the same kernel on the dense W and torch's F.linear
+    (hipBLASLt); four rotating weight copies, HIP-graph replay timing."""
+    import torch.nn.functional as F
+    K, N = 4096, 14336
+    W = torch.from_numpy(synth.gaussian_bits((N, K), 0.02, 4, 1, outliers=False).view(np.int16)).to(dev)
+    copies = 4
+    Ws = [W.clone() for _ in range(copies)]
+    comps = [enc.enc_compress(w.reshape(-1), 512) for w in Ws]
+    out = {"shape": "X[M,4096] x W^T, W [14336,4096] compressed at B=512",
+           "w_bytes_compressed": comps[0][1].total_bytes}
+    for M in (1, 16, 128):
+        X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
+        Xb = X.view(torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = enc.gemm_nt_workspace(M, K, N, 512, dev)
+        k = [0]
+
+        def fused():
+            c, inf = comps[k[0] % copies]
+            enc.enc_decompress_gemm_nt(X, c, inf, N, y=Y, ws=ws)
+            k[0] += 1
+
+        def dense():
+            enc.enc_gemm_dense_nt(X, Ws[k[0] % copies], y=Y, ws=ws)
+            k[0] += 1
+
+        def blas():
+            F.linear(Xb, Ws[k[0] % copies].view(torch.bfloat16))
+            k[0] += 1
+
+        try:
+            tf, _ = _graph_time_us(fused, torch)
+            td, _ = _graph_time_us(dense, torch)
+            tb, _ = _graph_time_us(blas, torch)
+            out["M%d" % M] = {"fused_us": round(tf, 2), "dense_same_kernel_us": round(td, 2),
+                              "hipblaslt_linear_us": round(tb, 2),
+                              "speedup_vs_hipblaslt": round(tb / tf, 3)}
         except Exception as e:  # the GEMM kernels report through EncError
             out["M%d" % M] = {"error": str(e)}
     return out

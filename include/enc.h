@@ -177,6 +177,32 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
 enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
                           uint32_t N, float *d_y, void *d_ws, uint64_t ws_bytes, void *stream);
 
+/* Fused decompress-GEMM with W in the layout of a linear layer's weight
+ * (output features x input features):
+ *   Y[M,N] (fp32, overwritten) = X[M,K] (BF16 row-major) * W^T
+ * where W is the row-major BF16 matrix [N, K] compressed in d_wcomp
+ * (n_elems = N*K), so each block holds consecutive k of one output column and
+ * decodes straight into matrix-core operands (ZipServ Abstract: decompression
+ * fused into the GEMM, no intermediate decompressed weights). Requirements:
+ * N*K == n_elems, N % 64 == 0, K % 32 == 0, K % block_size == 0 for a coded
+ * stream, coded stream below 2 GiB, 1 <= M <= 4096; else ENC_ERR_SHAPE /
+ * ENC_ERR_UNSUPPORTED. A RAW stream is multiplied from its verbatim values.
+ * Workspace: at least enc_gemm_nt_workspace_bytes(M, K, N, block_size) bytes
+ * (split-K partial sums; no initialisation needed). A second kernel on the
+ * same stream adds the partial slices in K order (deterministic); calls
+ * sharing a workspace must not overlap. Accumulation is fp32. Asynchronous;
+ * allocates nothing. */
+uint64_t enc_gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size);
+enc_status enc_decompress_gemm_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
+                                  const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
+                                  uint64_t ws_bytes, void *stream);
+
+/* The same GEMM on an uncompressed BF16 W[N, K] (same kernel, plain loads):
+ * the baseline the fused [N, K] path is compared with. Workspace rules as
+ * above with block_size 512. */
+enc_status enc_gemm_dense_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
+                             uint32_t N, float *d_y, void *d_ws, uint64_t ws_bytes, void *stream);
+
 /* Deep check of a stream's device data (the header is checked on the host
  * by enc_parse_header / enc_read_info). In this order of precedence:
  *   ENC_CHECK_WIDTH    some block width is above 8 (or, in a flags-2

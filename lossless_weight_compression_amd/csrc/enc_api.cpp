@@ -571,6 +571,83 @@ enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uin
   return launched(launch_gemm(a, s), s, "GEMM launch");
 }
 
+uint64_t enc_gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size) {
+  const int lb = log2_block(block_size);
+  if (lb < 0 || M == 0 || K == 0 || N == 0) return 0;
+  return gemm_nt_workspace_bytes(M, K, N, (uint32_t)lb);
+}
+
+static enc_status gemm_nt_common(const uint16_t *d_x, uint32_t M, uint32_t K, uint32_t N,
+                                 uint32_t log2b, float *d_y, void *d_ws, uint64_t ws_bytes,
+                                 GemmArgs *a) {
+  if (!d_x || !d_y || !d_ws) return fail(ENC_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(d_x) || !aligned16(d_y) || !aligned16(d_ws))
+    return fail(ENC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (M == 0 || M > 4096 || K == 0 || N == 0)
+    return fail(ENC_ERR_SHAPE, "M=%u K=%u N=%u out of range", M, K, N);
+  if (N % 64) return fail(ENC_ERR_UNSUPPORTED, "N=%u must be a multiple of 64", N);
+  if (K % 32) return fail(ENC_ERR_UNSUPPORTED, "K=%u must be a multiple of 32", K);
+  const uint64_t need = gemm_nt_workspace_bytes(M, K, N, log2b);
+  if (ws_bytes < need)
+    return fail(ENC_ERR_CAPACITY, "GEMM workspace of %llu bytes needed", (unsigned long long)need);
+  memset(a, 0, sizeof *a);
+  a->x = d_x;
+  a->y = d_y;
+  a->M = M;
+  a->K = K;
+  a->N = N;
+  a->log2b = log2b;
+  a->partial = static_cast<float *>(d_ws);
+  return ENC_OK;
+}
+
+enc_status enc_decompress_gemm_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
+                                  const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
+                                  uint64_t ws_bytes, void *stream) {
+  clear_err();
+  enc_status st = check_info(h_winfo);
+  if (st != ENC_OK) return st;
+  if (!d_wcomp || !aligned16(d_wcomp)) return fail(ENC_ERR_INVALID_ARG, "d_wcomp NULL or unaligned");
+  if ((uint64_t)K * N != h_winfo->n_elems)
+    return fail(ENC_ERR_SHAPE, "K*N=%llu but the stream holds %llu elements",
+                (unsigned long long)K * N, (unsigned long long)h_winfo->n_elems);
+  const bool raw = h_winfo->flags == 1;
+  const int lb = log2_block(h_winfo->block_size);
+  if (!raw && K % h_winfo->block_size)
+    return fail(ENC_ERR_UNSUPPORTED, "K=%u not a multiple of the block size %u", K,
+                h_winfo->block_size);
+  if (!raw && h_winfo->total_bytes >= (1ull << 31))
+    return fail(ENC_ERR_UNSUPPORTED, "coded stream above 2 GiB (32-bit buffer offsets)");
+  GemmArgs a;
+  st = gemm_nt_common(d_x, M, K, N, raw ? 9u : (uint32_t)lb, d_y, d_ws, ws_bytes, &a);
+  if (st != ENC_OK) return st;
+  const uint8_t *w = static_cast<const uint8_t *>(d_wcomp);
+  if (raw) {
+    a.wdense = reinterpret_cast<const uint16_t *>(w + kHeaderBytes);
+  } else {
+    a.wstream = w;
+    a.nb = h_winfo->n_blocks;
+    a.meta_off = h_winfo->meta_off;
+    a.segoff_off = h_winfo->segoff_off;
+    a.payload_off = h_winfo->payload_off;
+    a.total = h_winfo->total_bytes;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_gemm_nt(a, s), s, "GEMM launch");
+}
+
+enc_status enc_gemm_dense_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const uint16_t *d_w,
+                             uint32_t N, float *d_y, void *d_ws, uint64_t ws_bytes, void *stream) {
+  clear_err();
+  if (!d_w || !aligned16(d_w)) return fail(ENC_ERR_INVALID_ARG, "d_w NULL or unaligned");
+  GemmArgs a;
+  const enc_status st = gemm_nt_common(d_x, M, K, N, 9u, d_y, d_ws, ws_bytes, &a);
+  if (st != ENC_OK) return st;
+  a.wdense = d_w;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_gemm_nt(a, s), s, "GEMM launch");
+}
+
 uint64_t enc_validate_workspace_bytes(void) { return 256; }
 
 enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, uint64_t ws_bytes,

@@ -142,6 +142,10 @@ struct GemmArgs {
 };
 uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// W stored [N, K] (linear-layer layout), Y = X . W^T; needs N % 64 == 0 and
+// K a multiple of the block size (dense: of 32).
+uint64_t gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t log2b);
+hipError_t launch_gemm_nt(const GemmArgs &a, hipStream_t s);
 void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *krows);
 
 }  // namespace enc

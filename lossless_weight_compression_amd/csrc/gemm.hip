@@ -819,6 +819,164 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// W stored [N, K] row-major -- the weight layout of a linear layer (output
+// features x input features) -- and Y = X . W^T.
+//
+// A block of W is then B consecutive k of one output column n, so the group
+// a lane decodes (8 consecutive k of one column) is exactly that lane's part
+// of an MFMA B fragment: for v_mfma_f32_16x16x32_bf16, lane L holds k =
+// 8 (L / 16) .. + 7 of column L % 16 ("ZipServ: Fast and Memory-Efficient LLM
+// Inference with Hardware-Aware Lossless Compression", Abstract: decode
+// straight into the matrix units' registers). No LDS transpose and no
+// barrier: each wave owns 16 columns and a K range, streams its 16 rows of W
+// (one group per lane per 32-k step, kNtDepth steps in flight) and keeps
+// MSUB 16 x 16 accumulator tiles. The A fragment is 16 bytes of an X row.
+// A lane's row stays fixed, so its block changes only at multiples of B in
+// k: the prologue finds the offsets and metas of the (at most kNtBlocks)
+// blocks of its K range, and the loop picks them with a wave-uniform index.
+// Rows past M read a clamped row and multiply zeros; steps past the range
+// load from past the buffer's range (zeros, no memory access).
+// Cost: every wave load instruction touches 16 rows of W (and 16 rows of X),
+// 32 bytes each, so this kernel is bound by cache-line accesses rather than
+// by HBM bytes or load latency (prefetch depth 2, 4 or 8 all measured the
+// same). The [K, N] kernels above read 512 contiguous bytes per row and are
+// faster; a caller that compresses offline can store W^T for them.
+// --------------------------------------------------------------------------
+constexpr uint32_t kNtCols = 16;     // columns per wave
+constexpr uint32_t kNtWaves = 4;     // waves per workgroup
+constexpr uint32_t kNtDepth = 4;     // 32-k steps in flight per wave
+constexpr uint32_t kNtBlocks = 4;    // blocks per row and K range, at most
+
+template <int MSUB, bool DENSE>
+__global__ __launch_bounds__(kNtWaves * 64) void k_gemm_nt(GemmArgs a) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t K = a.K, N = a.N, M = a.M;
+  const uint32_t n = (blockIdx.x * kNtWaves + wave) * kNtCols + (lane & 15);   // row of W
+  const uint32_t kq = lane >> 4;                                                // group of the step
+  const uint32_t k0 = blockIdx.y * a.krows;
+  const uint32_t k1 = min(k0 + a.krows, K);
+  const uint32_t nsteps = (k1 - k0) / 32;
+  const uint32_t m0 = blockIdx.z * 16 * MSUB;
+  const uint32_t log2b = a.log2b;
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
+
+  uint32_t b_off[kNtBlocks], b_meta[kNtBlocks];
+#pragma unroll
+  for (uint32_t j = 0; j < kNtBlocks; ++j) {
+    b_off[j] = 0;
+    b_meta[j] = 0;
+  }
+  if (!DENSE) {
+    const uint32_t nblk = (k1 - k0) >> log2b;
+#pragma unroll
+    for (uint32_t j = 0; j < kNtBlocks; ++j) {
+      if (j < nblk) {
+        uint64_t off, mw;
+        row_block<false>(a, ((uint64_t)n * K + k0 + (j << log2b)) >> log2b, off, mw);
+        uint32_t w = (uint32_t)(mw >> 8) & 0xFFu;
+        if (w > 8) w = 0;   // corrupted stream: decode as width 0 (reads stay range-checked)
+        b_off[j] = (uint32_t)off;
+        b_meta[j] = ((uint32_t)mw & 0xFFu) | (w << 8);
+      }
+    }
+  }
+
+  struct Slot {
+    u32x2 sm;
+    u32x3 q;
+    uint4 dv;
+    uint4 x[MSUB];
+    uint32_t info;   // base | w << 8 | lead byte << 16
+  };
+  auto load = [&](uint32_t st, Slot &S) {
+    const uint32_t dead = st < nsteps ? 0u : 0x80000000u;
+    const uint32_t stc = min(st, nsteps - 1);
+    const uint32_t k = k0 + 32 * stc + 8 * kq;
+    if (DENSE) {
+      S.dv = *reinterpret_cast<const uint4 *>(a.wdense + (uint64_t)n * K + k);
+    } else {
+      const uint32_t j = (32 * stc) >> log2b;                      // wave-uniform
+      uint32_t off = b_off[0], meta = b_meta[0];
+#pragma unroll
+      for (uint32_t t = 1; t < kNtBlocks; ++t) {
+        off = j == t ? b_off[t] : off;
+        meta = j == t ? b_meta[t] : meta;
+      }
+      const uint32_t w = meta >> 8;
+      const uint32_t pb = off + ((k & ((1u << log2b) - 1)) >> 3) * w;
+      S.sm = __builtin_amdgcn_raw_buffer_load_b64(rs, (kHeaderBytes + n * K + k) | dead, 0, 0);
+      S.q = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
+      S.info = meta | ((pb & 3u) << 16);
+    }
+#pragma unroll
+    for (uint32_t mi = 0; mi < MSUB; ++mi) {
+      const uint32_t m = m0 + 16 * mi + (lane & 15);
+      const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K + k);
+      const bool in = m < M;
+      S.x[mi] = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
+    }
+  };
+
+  f32x4 acc[MSUB];
+#pragma unroll
+  for (uint32_t mi = 0; mi < MSUB; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Slot &S) {
+    uint4 bw;
+    if (DENSE) {
+      bw = S.dv;
+    } else {
+      const uint32_t w = (S.info >> 8) & 0xFFu, sh = (S.info >> 16) * 8;
+      const uint32_t lo = __builtin_amdgcn_alignbit(S.q.y, S.q.x, sh);
+      const uint32_t hi = __builtin_amdgcn_alignbit(S.q.z, S.q.y, sh);
+      bw = join_group(lo, hi, w, (S.info & 0xFFu) * 0x01010101u, S.sm.x, S.sm.y);
+    }
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+    for (uint32_t mi = 0; mi < MSUB; ++mi)
+      acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, S.x[mi]), b, acc[mi],
+                                                         0, 0, 0);
+  };
+
+  Slot R[kNtDepth];
+#pragma unroll
+  for (uint32_t p = 0; p + 1 < kNtDepth; ++p) load(p, R[p]);
+  for (uint32_t st = 0; st < nsteps; st += kNtDepth) {
+#pragma unroll
+    for (uint32_t j = 0; j < kNtDepth; ++j) {
+      load(st + j + kNtDepth - 1, R[(j + kNtDepth - 1) % kNtDepth]);
+      if (st + j < nsteps) compute(R[j]);
+    }
+  }
+
+  splitk_finish(a, blockIdx.y, [&](auto fn) {
+#pragma unroll
+    for (uint32_t mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t m = m0 + 16 * mi + 4 * (lane >> 4) + j;
+        fn(m < M ? (int64_t)m * N + n : (int64_t)-1, acc[mi][j]);
+      }
+  });
+}
+
+template <bool DENSE>
+hipError_t launch_nt(const GemmArgs &a, hipStream_t s, uint32_t msub) {
+  const uint32_t mt = 16 * msub;
+  const dim3 grid(a.N / (kNtCols * kNtWaves), a.ksplit, (a.M + mt - 1) / mt);
+  const dim3 block(kNtWaves * 64);
+  switch (msub) {
+    case 1: hipLaunchKernelGGL((k_gemm_nt<1, DENSE>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_nt<2, DENSE>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_nt<4, DENSE>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+// M tile of k_gemm_nt in 16-row units (MSUB).
+uint32_t nt_msub(uint32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+
 }  // namespace
 
 // Which kernel serves a call: 0 = generic VALU (M < kMfmaMinM), 1 =
@@ -884,6 +1042,55 @@ uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
   return most;
 }
 
+// [N, K]-layout GEMM plan: K ranges of whole blocks (at most kNtBlocks), as
+// many as it takes to give the device about 3072 workgroups (measured on a
+// 14336 x 4096 W: 3072 beat 1536 by ~11% at M = 1..128, 768 was slower).
+void gemm_nt_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t log2b, uint32_t *ksplit,
+                  uint32_t *krows) {
+  const uint32_t B = 1u << log2b;
+  const uint32_t mt = 16 * nt_msub(M);
+  const uint64_t tiles = (uint64_t)(N / (kNtCols * kNtWaves)) * ((M + mt - 1) / mt);
+  uint64_t ks = tiles >= 3072 ? 1 : 3072 / tiles;
+  if (ks < 1) ks = 1;
+  uint32_t rows = (uint32_t)((K + ks - 1) / ks);
+  rows = (rows + B - 1) / B * B;                     // whole blocks
+  if (rows > kNtBlocks * B) rows = kNtBlocks * B;
+  *krows = rows;
+  *ksplit = (K + rows - 1) / rows;
+}
+
+uint64_t gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t log2b) {
+  uint32_t ks, kr;
+  gemm_nt_plan(M, K, N, log2b, &ks, &kr);
+  const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
+  return partial > 256 ? partial : 256;
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs &a, hipStream_t s) {
+  const uint64_t mn = (uint64_t)a.M * a.N;
+  uint64_t blocks = (mn + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  const dim3 g((uint32_t)blocks), t(256);
+  if (a.ksplit <= 4)
+    hipLaunchKernelGGL(k_splitk_reduce<4>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  else if (a.ksplit <= 8)
+    hipLaunchKernelGGL(k_splitk_reduce<8>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  else if (a.ksplit <= 16)
+    hipLaunchKernelGGL(k_splitk_reduce<16>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<32>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(const GemmArgs &a_in, hipStream_t s) {
+  GemmArgs a = a_in;
+  const bool dense = a.wstream == nullptr;
+  gemm_nt_plan(a.M, a.K, a.N, a.log2b, &a.ksplit, &a.krows);
+  const hipError_t e = dense ? launch_nt<true>(a, s, nt_msub(a.M)) : launch_nt<false>(a, s, nt_msub(a.M));
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  return launch_splitk_reduce(a, s);
+}
+
 hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
   GemmArgs a = a_in;
   const bool dense = a.wstream == nullptr;
@@ -899,19 +1106,7 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
   else
     e = dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
   if (e != hipSuccess || a.ksplit == 1) return e;
-  const uint64_t mn = (uint64_t)a.M * a.N;
-  uint64_t blocks = (mn + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  const dim3 g((uint32_t)blocks), t(256);
-  if (a.ksplit <= 4)
-    hipLaunchKernelGGL(k_splitk_reduce<4>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
-  else if (a.ksplit <= 8)
-    hipLaunchKernelGGL(k_splitk_reduce<8>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
-  else if (a.ksplit <= 16)
-    hipLaunchKernelGGL(k_splitk_reduce<16>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
-  else
-    hipLaunchKernelGGL(k_splitk_reduce<32>, g, t, 0, s, a.partial, a.y, mn, a.ksplit);
-  return hipGetLastError();
+  return launch_splitk_reduce(a, s);
 }
 
 }  // namespace enc

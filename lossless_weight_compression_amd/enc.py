@@ -78,6 +78,9 @@ SIGNATURES = {
     "enc_gemm_dense": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
     "enc_validate_workspace_bytes": (_U64, []),
     "enc_validate": (_ST, [_VP, _INFO_P, _VP, _U64, _VP, ctypes.POINTER(EncCheck)]),
+    "enc_gemm_nt_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
+    "enc_decompress_gemm_nt": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP, _U64, _VP]),
+    "enc_gemm_dense_nt": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
     "enc_status_string": (ctypes.c_char_p, [_ST]),
     "enc_last_error": (ctypes.c_char_p, []),
 }
@@ -260,6 +263,49 @@ def enc_gemm_dense(x, w, y=None, ws=None, stream=None):
         ws = gemm_workspace(M, K, N, 512, x.device)
     _check(lib().enc_gemm_dense(_ptr(x), M, K, _ptr(w), N, _ptr(y), _ptr(ws), ws.numel(),
                                 _stream(stream)))
+    return y
+
+
+def enc_gemm_nt_workspace_bytes(M, K, N, block_size=512):
+    return int(lib().enc_gemm_nt_workspace_bytes(M, K, N, block_size))
+
+
+def gemm_nt_workspace(M, K, N, block_size=512, device="cuda"):
+    """A workspace for the [N, K]-layout GEMM entry points (no initialisation needed)."""
+    import torch
+    return torch.empty(max(enc_gemm_nt_workspace_bytes(M, K, N, block_size), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def enc_decompress_gemm_nt(x, comp, info, N, y=None, ws=None, stream=None):
+    """Y[M,N] fp32 = X[M,K] bf16 @ W^T, W [N,K] (linear-layer layout) given compressed."""
+    import torch
+    x = _bits(x)
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = gemm_nt_workspace(M, K, N, info.block_size, x.device)
+    _check(lib().enc_decompress_gemm_nt(_ptr(x), M, K, _ptr(comp), ctypes.byref(info), N, _ptr(y),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def enc_gemm_dense_nt(x, w, y=None, ws=None, stream=None):
+    """Y[M,N] fp32 = X[M,K] bf16 @ W^T, W [N,K] bf16 uncompressed (baseline)."""
+    import torch
+    x = _bits(x)
+    w = _bits(w)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = gemm_nt_workspace(M, K, N, 512, x.device)
+    _check(lib().enc_gemm_dense_nt(_ptr(x), M, K, _ptr(w), N, _ptr(y), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
     return y
 
 
