@@ -791,15 +791,28 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
 // Step buffers per M tile size (ring depth of the prefetch). Measured at
 // M = 16 / 32 / 128: two beat three (register pressure).
 constexpr int kNB16 = 2, kNB32 = 2, kNB64 = 2;
+// Waves per workgroup for each M tile, and the resident workgroups the
+// split-K plan fills. More waves per workgroup share one decoded LDS tile
+// and need fewer registers each (2 rows per wave per step at 16 waves), so
+// the same device holds more rows in flight with fewer split-K slices.
+// Measured on a 4096 x 14336 W: 16 waves over 4 took M = 8 from 35.9 to
+// 29.8 us, M = 16 from 36.6 to 31.6, M = 32 from 42.3 to 38.9; at the
+// 64-row tile 16 waves were slower than 8 (M = 128: 91.8 vs 82.4 us).
+constexpr int kW16 = 16;
+constexpr uint64_t kSlots16 = 512;
+constexpr int kW32 = 16;
+constexpr uint64_t kSlots32 = 256;
+constexpr int kW64 = 8;
+constexpr uint64_t kSlots64 = 256;
 
 template <bool DENSE>
 hipError_t launch_mfmau(const GemmArgs &a, hipStream_t s) {
   const uint32_t MT = mfmau_tile_m(a.M);
   const dim3 grid(a.N / kStrip, a.ksplit, (a.M + MT - 1) / MT);
   switch (MT) {
-    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, 4, DENSE, kNB16>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, 4, DENSE, kNB32>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfmau<64, 8, DENSE, kNB64>), grid, dim3(512), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, kW16, DENSE, kNB16>), grid, dim3(kW16 * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, kW32, DENSE, kNB32>), grid, dim3(kW32 * 64), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfmau<64, kW64, DENSE, kNB64>), grid, dim3(kW64 * 64), 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -1006,10 +1019,10 @@ void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t 
   const uint64_t tiles = (uint64_t)(N / ncol) * ((M + MT - 1) / MT);
   uint64_t ks;
   if (kind == 3) {
-    // Resident k_gemm_mfmau workgroups: ~74 KB of LDS allows two per CU;
-    // the 8-wave 64-row variant needs ~170 registers per lane, one per CU.
-    // Fill the slots in one round: a partial second round doubles the time.
-    const uint64_t slots = MT == 64 ? 256 : 512;
+    // Resident k_gemm_mfmau workgroups (kSlots*: ~74 KB of LDS allows two
+    // per CU; the 8-wave 64-row variant's registers allow one). Fill the
+    // slots in one round: a partial second round doubles the time.
+    const uint64_t slots = MT == 64 ? kSlots64 : (MT == 16 ? kSlots16 : kSlots32);
     ks = tiles >= slots ? 1 : slots / tiles;
   } else {
     const uint64_t target = M <= 32 ? 512 : 256;
