@@ -86,6 +86,24 @@ def gaussian_bits(shape, sigma, set_id, tensor_id, outliers=True):
     return f32_to_bf16_bits(f).reshape(shape)
 
 
+def gaussian_values(shape, sigma, set_id, tensor_id, dtype, outliers=True):
+    """Bit patterns of N(0, sigma) weights (Bernoulli(0.001) entries x20 with
+    outliers) in another element type: dtype 2 = FP16 (numpy's float16
+    rounding, uint16 bits), 3 = FP32 (uint32 bits)."""
+    rng = _rng(set_id, 100 + tensor_id)
+    n = int(np.prod(shape))
+    f = rng.standard_normal(n, dtype=np.float32)
+    f *= np.float32(sigma)
+    if outliers:
+        mask = rng.random(n, dtype=np.float32) < OUTLIER_P
+        f[mask] *= np.float32(OUTLIER_SCALE)
+    if dtype == 2:
+        return f.astype(np.float16).view(np.uint16).reshape(shape)
+    if dtype == 3:
+        return f.view(np.uint32).reshape(shape)
+    raise ValueError(dtype)
+
+
 def tiny():
     """The 1024x1024 round-trip matrix, N(0, 0.02), no outliers."""
     return gaussian_bits((1024, 1024), 0.02, 0, 0, outliers=False)

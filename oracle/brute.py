@@ -16,6 +16,30 @@ Compression", Abstract (fixed-length format, parallel decoding).
 HEADER = 256
 SEG = 64
 
+# element type -> (bytes, bits, exponent shift, exponent bits); the rest of a
+# value (sign, mantissa) is kept as an (exponent shift + 1)-bit field
+DTYPES = {1: (2, 16, 7, 8), 2: (2, 16, 10, 5), 3: (4, 32, 23, 8)}
+
+
+def split_dt(x, dtype):
+    """Bit pattern -> (exponent field, sign+mantissa field), by bit lists."""
+    _, nbits, sh, eb = DTYPES[dtype]
+    bits = [(x >> k) & 1 for k in range(nbits)]
+    exp = sum(bits[sh + k] << k for k in range(eb))
+    sm = sum(bits[k] << k for k in range(sh)) + (bits[nbits - 1] << sh)
+    return exp, sm
+
+
+def join_dt(exp, sm, dtype):
+    _, nbits, sh, eb = DTYPES[dtype]
+    bits = [0] * nbits
+    for k in range(sh):
+        bits[k] = (sm >> k) & 1
+    for k in range(eb):
+        bits[sh + k] = (exp >> k) & 1
+    bits[nbits - 1] = (sm >> sh) & 1
+    return sum(b << k for k, b in enumerate(bits))
+
 
 def _align(v, a):
     return -(-v // a) * a
@@ -55,8 +79,8 @@ def _le(v, nbytes):
 
 
 def _header(flags, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
-            payload_bytes, raw_off, total):
-    h = list(b"ENCB") + _le(1, 2) + _le(1, 2) + _le(flags, 4) + _le(B, 4)
+            payload_bytes, raw_off, total, dtype=1):
+    h = list(b"ENCB") + _le(1, 2) + _le(dtype, 2) + _le(flags, 4) + _le(B, 4)
     h += _le(SEG, 4) + _le(0, 4)
     for v in (n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
               payload_bytes, raw_off, total):
@@ -64,13 +88,15 @@ def _header(flags, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
     return h + [0] * (HEADER - len(h))
 
 
-def encode(xs, B, pow2=False):
-    """Stream bytes for the BF16 patterns xs (list of ints) at block size B;
-    pow2: widths restricted to POW2_WIDTHS (stream flag 2)."""
+def encode(xs, B, pow2=False, dtype=1):
+    """Stream bytes for the bit patterns xs (list of ints) of element type
+    dtype at block size B; pow2: widths restricted to POW2_WIDTHS (flag 2)."""
     n = len(xs)
-    raw = _header(1, B, n, 0, 0, 0, 0, 0, 0, 0, HEADER, HEADER + 2 * n)
+    size = DTYPES[dtype][0]
+    S = DTYPES[dtype][2] + 1
+    raw = _header(1, B, n, 0, 0, 0, 0, 0, 0, 0, HEADER, HEADER + size * n, dtype)
     for x in xs:
-        raw += _le(x, 2)
+        raw += _le(x, size)
     if n == 0:
         return bytes(raw)
     blocks = [xs[i:i + B] for i in range(0, n, B)]
@@ -78,7 +104,7 @@ def encode(xs, B, pow2=False):
     nseg = -(-nb // SEG)
     metas, payloads = [], []
     for blk in blocks:
-        exps = [split(v)[0] for v in blk]
+        exps = [split_dt(v, dtype)[0] for v in blk]
         base = min(exps)
         codes = [e - base for e in exps]
         w = width_by_search(codes, POW2_WIDTHS if pow2 else range(9))
@@ -94,17 +120,23 @@ def encode(xs, B, pow2=False):
         metas.append((base, w))
         payloads.append(body)
     sm_off = HEADER
-    meta_off = sm_off + _align(n, 256)
+    meta_off = sm_off + _align(-(-S * n // 8), 256)
     segoff_off = meta_off + _align(2 * nb, 256)
     payload_off = segoff_off + _align(8 * nseg, 256)
     segoffs = [sum(len(p) for p in payloads[:SEG * s]) for s in range(nseg)]
     payload_bytes = sum(len(p) for p in payloads)
     total = payload_off + payload_bytes
-    if total >= HEADER + 2 * n:
+    if total >= HEADER + size * n:
         return bytes(raw)
     out = _header(2 if pow2 else 0, B, n, nb, nseg, sm_off, meta_off, segoff_off, payload_off,
-                  payload_bytes, 0, total)
-    out += [split(v)[1] for v in xs]
+                  payload_bytes, 0, total, dtype)
+    smbits = []
+    for v in xs:                             # S-bit fields, LSB first
+        sm = split_dt(v, dtype)[1]
+        smbits += [(sm >> b) & 1 for b in range(S)]
+    while len(smbits) % 8:
+        smbits.append(0)
+    out += [sum(smbits[8 * k + b] << b for b in range(8)) for k in range(len(smbits) // 8)]
     out += [0] * (meta_off - len(out))
     for base, w in metas:
         out += [base, w]
@@ -123,12 +155,15 @@ def _get(s, off, nbytes):
 
 
 def decode(s):
-    """BF16 patterns decoded from stream bytes s (walks every block)."""
+    """Bit patterns decoded from stream bytes s (walks every block)."""
     assert bytes(s[:4]) == b"ENCB"
+    dtype = _get(s, 6, 2)
+    size, _, sh, eb = DTYPES[dtype]
+    S = sh + 1
     flags, B = _get(s, 8, 4), _get(s, 12, 4)
     n = _get(s, 24, 8)
-    if flags & 1:
-        return [_get(s, HEADER + 2 * j, 2) for j in range(n)]
+    if flags == 1:
+        return [_get(s, HEADER + size * j, size) for j in range(n)]
     nb = _get(s, 32, 8)
     sm_off, meta_off = _get(s, 48, 8), _get(s, 56, 8)
     payload_off = _get(s, 72, 8)
@@ -140,7 +175,9 @@ def decode(s):
         bitstream = [(s[pos + k // 8] >> (k % 8)) & 1 for k in range(L * w)]
         for t in range(L):
             d = sum(bitstream[t * w + b] << b for b in range(w))
-            out.append(join((base + d) & 0xFF, s[sm_off + i * B + t]))
+            j = i * B + t
+            sm = sum(((s[sm_off + (j * S + b) // 8] >> ((j * S + b) % 8)) & 1) << b for b in range(S))
+            out.append(join_dt((base + d) & ((1 << eb) - 1), sm, dtype))
         pos += _align(-(-L * w // 8), 16)
     return out
 
@@ -156,6 +193,7 @@ def validate(s):
     flags, B = _get(s, 8, 4), _get(s, 12, 4)
     if flags & 1:
         return 0, 0
+    emax = (1 << DTYPES[_get(s, 6, 2)][3]) - 1
     n, nb, nseg = _get(s, 24, 8), _get(s, 32, 8), _get(s, 40, 8)
     meta_off, segoff_off = _get(s, 56, 8), _get(s, 64, 8)
     payload_off, payload_bytes = _get(s, 72, 8), _get(s, 80, 8)
@@ -175,7 +213,7 @@ def validate(s):
         L, base, w = min(B, n - i * B), s[meta_off + 2 * i], widths[i]
         for t in range(L):
             d = sum(((s[pos + (t * w + b) // 8] >> ((t * w + b) % 8)) & 1) << b for b in range(w))
-            if base + d > 255:
+            if base + d > emax:
                 return 3, i
         pos += sizes[i]
     return 0, 0

@@ -72,6 +72,27 @@ def lib():
         L.orc_decode_range.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                        _u16p]
         L.orc_decode_range.restype = ctypes.c_int
+        _vp = ctypes.c_void_p
+        L.orc_encode_dt.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                    ctypes.c_uint32, _u8p, ctypes.c_uint64]
+        L.orc_encode_dt.restype = ctypes.c_int64
+        L.orc_stream_size_dt.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                         ctypes.c_uint32]
+        L.orc_stream_size_dt.restype = ctypes.c_int64
+        L.orc_block_params_dt.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                          ctypes.c_uint32, _u8p, _u8p]
+        L.orc_block_params_dt.restype = ctypes.c_int64
+        L.orc_decode_dt.argtypes = [_u8p, ctypes.c_uint64, _vp, ctypes.c_uint64]
+        L.orc_decode_dt.restype = ctypes.c_int
+        L.orc_decode_range_dt.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _vp]
+        L.orc_decode_range_dt.restype = ctypes.c_int
+        L.orc_stream_dtype.argtypes = [_u8p, ctypes.c_uint64]
+        L.orc_stream_dtype.restype = ctypes.c_int64
+        for fn in ("orc_exponent_dt", "orc_signmant_dt"):
+            getattr(L, fn).argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+            getattr(L, fn).restype = ctypes.c_uint32
+        L.orc_join_dt.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+        L.orc_join_dt.restype = ctypes.c_uint32
         L.orc_validate.argtypes = [_u8p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
         L.orc_validate.restype = ctypes.c_int
         L.orc_gemm_f64.argtypes = [_u16p, ctypes.c_uint32, ctypes.c_uint32, _u16p,
@@ -99,6 +120,30 @@ def _u16(x):
     return x.reshape(-1)
 
 
+BF16, FP16, FP32 = 1, 2, 3
+_NP = {BF16: np.uint16, FP16: np.uint16, FP32: np.uint32}
+
+
+def _bits(x, dtype):
+    """x as contiguous bit patterns of the element type (uint16 or uint32)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype != _NP[dtype]:
+        raise TypeError("expected %s bit patterns for dtype %d" % (np.dtype(_NP[dtype]).name, dtype))
+    return x.reshape(-1)
+
+
+def exponent_dt(v, dtype):
+    return lib().orc_exponent_dt(int(v), dtype)
+
+
+def signmant_dt(v, dtype):
+    return lib().orc_signmant_dt(int(v), dtype)
+
+
+def join_dt(sm, e, dtype):
+    return lib().orc_join_dt(int(sm), int(e), dtype)
+
+
 def exponent(v):
     return lib().orc_exponent(int(v))
 
@@ -123,34 +168,36 @@ def pow2_width(r):
     return lib().orc_pow2_width(int(r))
 
 
-def block_params(x, B, pow2=False):
+def block_params(x, B, pow2=False, dtype=BF16):
     """(base[nb], width[nb]) as uint8 arrays."""
-    x = _u16(x)
+    x = _bits(x, dtype)
     nb = -(-x.size // B)
     base = np.zeros(max(nb, 1), np.uint8)
     w = np.zeros(max(nb, 1), np.uint8)
-    r = lib().orc_block_params_opts(_ptr(x, _u16p), x.size, B, 1 if pow2 else 0, _ptr(base, _u8p),
-                                    _ptr(w, _u8p))
+    r = lib().orc_block_params_dt(x.ctypes.data, x.size, dtype, B, 1 if pow2 else 0,
+                                  _ptr(base, _u8p), _ptr(w, _u8p))
     if r < 0:
         raise OracleError("block_params failed: %d" % r)
     return base[:nb], w[:nb]
 
 
-def stream_size(x, B, pow2=False):
-    x = _u16(x)
-    r = lib().orc_stream_size_opts(_ptr(x, _u16p), x.size, B, 1 if pow2 else 0)
+def stream_size(x, B, pow2=False, dtype=BF16):
+    x = _bits(x, dtype)
+    r = lib().orc_stream_size_dt(x.ctypes.data, x.size, dtype, B, 1 if pow2 else 0)
     if r < 0:
         raise OracleError("stream_size failed: %d" % r)
     return int(r)
 
 
-def encode(x, B, pow2=False):
-    """Stream bytes (np.uint8 array) for the BF16 patterns x at block size B;
-    pow2: widths rounded up to 0, 1, 2, 4 or 8 (stream flag 2)."""
-    x = _u16(x)
-    size = stream_size(x, B, pow2)
+def encode(x, B, pow2=False, dtype=BF16):
+    """Stream bytes (np.uint8 array) for the bit patterns x (uint16 for BF16
+    and FP16, uint32 for FP32) at block size B; pow2: widths rounded up to
+    0, 1, 2, 4 or 8 (stream flag 2)."""
+    x = _bits(x, dtype)
+    size = stream_size(x, B, pow2, dtype)
     out = np.empty(size, np.uint8)
-    r = lib().orc_encode_opts(_ptr(x, _u16p), x.size, B, 1 if pow2 else 0, _ptr(out, _u8p), out.size)
+    r = lib().orc_encode_dt(x.ctypes.data, x.size, dtype, B, 1 if pow2 else 0, _ptr(out, _u8p),
+                            out.size)
     if r < 0:
         raise OracleError("encode failed: %d" % r)
     assert r == size
@@ -162,13 +209,19 @@ def stream_elements(s):
     return int(lib().orc_stream_elements(_ptr(s, _u8p), s.size))
 
 
+def stream_dtype(s):
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    return int(lib().orc_stream_dtype(_ptr(s, _u8p), s.size))
+
+
 def decode(s):
+    """Decoded bit patterns (uint16 for BF16 / FP16 streams, uint32 for FP32)."""
     s = np.ascontiguousarray(s, dtype=np.uint8)
     n = stream_elements(s)
     if n < 0:
         raise OracleError("bad stream: %d" % n)
-    out = np.empty(max(n, 1), np.uint16)
-    r = lib().orc_decode(_ptr(s, _u8p), s.size, _ptr(out, _u16p), n)
+    out = np.empty(max(n, 1), _NP[stream_dtype(s)])
+    r = lib().orc_decode_dt(_ptr(s, _u8p), s.size, out.ctypes.data, n)
     if r != 0:
         raise OracleError("decode failed: %d" % r)
     return out[:n]
@@ -176,8 +229,8 @@ def decode(s):
 
 def decode_range(s, first, count):
     s = np.ascontiguousarray(s, dtype=np.uint8)
-    out = np.empty(max(count, 1), np.uint16)
-    r = lib().orc_decode_range(_ptr(s, _u8p), s.size, first, count, _ptr(out, _u16p))
+    out = np.empty(max(count, 1), _NP[stream_dtype(s)])
+    r = lib().orc_decode_range_dt(_ptr(s, _u8p), s.size, first, count, out.ctypes.data)
     if r != 0:
         raise OracleError("decode_range failed: %d" % r)
     return out[:count]

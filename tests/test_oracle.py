@@ -595,3 +595,101 @@ def test_pow2_validate(orc):
     assert brute.validate(bytes(b)) == orc.validate(b)
     c = orc.encode(x, 64)                                  # the same width is fine unflagged
     assert orc.validate(c) == (0, 0)
+
+
+# ------------------------------------------- FP16 and FP32 element types
+def test_fp16_fields_against_numpy(orc):
+    # every FP16 pattern: the oracle's exponent / sign+mantissa fields rebuild
+    # numpy's float16 value by the IEEE definition, and join(split(x)) == x
+    x = np.arange(65536, dtype=np.uint16)
+    f = x.view(np.float16).astype(np.float64)
+    for v in range(0, 65536, 7):
+        e, sm = orc.exponent_dt(v, orc.FP16), orc.signmant_dt(v, orc.FP16)
+        assert (e, sm) == brute.split_dt(v, 2)
+        assert orc.join_dt(sm, e, orc.FP16) == v
+        sign, mant = sm >> 10, sm & 0x3FF
+        if 0 < e < 31:
+            val = (-1) ** sign * 2.0 ** (e - 15) * (1 + mant / 1024)
+            assert val == f[v], v
+        elif e == 0:
+            assert (-1) ** sign * 2.0 ** -14 * (mant / 1024) == f[v], v
+
+
+def test_fp32_fields_against_numpy(orc):
+    rng = np.random.default_rng(17)
+    x = rng.integers(0, 1 << 32, 4000, dtype=np.uint64).astype(np.uint32)
+    with np.errstate(invalid="ignore"):                   # NaN patterns
+        f = x.view(np.float32).astype(np.float64)
+    for v, fv in zip(x.tolist(), f.tolist()):
+        e, sm = orc.exponent_dt(v, orc.FP32), orc.signmant_dt(v, orc.FP32)
+        assert (e, sm) == brute.split_dt(v, 3)
+        assert orc.join_dt(sm, e, orc.FP32) == v
+        sign, mant = sm >> 23, sm & 0x7FFFFF
+        if 0 < e < 255:
+            assert (-1) ** sign * 2.0 ** (e - 127) * (1 + mant / 2 ** 23) == fv
+
+
+def test_fp_hand_worked_sign_mantissa_fields(orc):
+    # FP32 1.0 = 0x3F800000 (sm 0) and -1.5 = 0xBFC00000 (mantissa 0x400000,
+    # sign -> bit 23: sm 0xC00000); 24-bit fields LSB first: bytes of value 0
+    # are 00 00 00, of value 1 are 00 00 C0. Exponents 127/127 -> width 0.
+    # 2000 pairs keep the stream below the RAW size.
+    x = np.array([0x3F800000, 0xBFC00000] * 2000, np.uint32)
+    s = orc.encode(x, 64, dtype=orc.FP32)
+    assert int.from_bytes(bytes(s[6:8]), "little") == 3 and s[8] == 0
+    assert s[256:262].tolist() == [0, 0, 0, 0, 0, 0xC0]
+    assert np.array_equal(orc.decode(s), x)
+    # FP16 1.0 = 0x3C00 (e 15, sm 0) and -2.5 = 0xC100 (e 16, mantissa 0x100,
+    # sign -> bit 10: sm 0x500); 11-bit fields: 0 then 0x500 << 11 = 0x280000
+    # -> bytes 00 00 28. Exponents {15, 16}: base 15, width 1.
+    y = np.array([0x3C00, 0xC100] * 3000, np.uint16)
+    s = orc.encode(y, 64, dtype=orc.FP16)
+    assert int.from_bytes(bytes(s[6:8]), "little") == 2 and s[8] == 0
+    assert s[256:259].tolist() == [0, 0, 0x28]
+    base, w = orc.block_params(y, 64, dtype=orc.FP16)
+    assert (int(base[0]), int(w[0])) == (15, 1)
+    assert np.array_equal(orc.decode(s), y)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+@pytest.mark.parametrize("B,n", [(8, 1000 + 3), (24, 64 * 24 + 7), (64, 3001)])
+def test_fp_brute_force(orc, dtype, B, n):
+    x = synth.gaussian_values((n,), 0.02, 30, B, dtype)
+    for pow2 in (False, True):
+        s = orc.encode(x, B, pow2=pow2, dtype=dtype)
+        assert bytes(s) == brute.encode([int(v) for v in x], B, pow2=pow2, dtype=dtype)
+        assert np.array_equal(orc.decode(s), x)
+        assert brute.decode(bytes(s)) == [int(v) for v in x]
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_fp_sizes_round_trip_and_raw(orc, dtype):
+    x = synth.gaussian_values((256, 1024), 0.02, 31, 0, dtype)
+    size, S = (2, 11) if dtype == 2 else (4, 24)
+    for B in (128, 512):
+        s = orc.encode(x, B, dtype=dtype)
+        assert np.array_equal(orc.decode(s), x.reshape(-1))
+        base, w = orc.block_params(x, B, dtype=dtype)
+        nb = w.size
+        a = lambda v: -(-v // 256) * 256
+        pay = sum(-(-(-(-int(wi) * B // 8)) // 16) * 16 for wi in w)
+        closed = 256 + a(-(-S * x.size // 8)) + a(2 * nb) + a(8 * (-(-nb // 64))) + pay
+        assert s.size == min(closed, 256 + size * x.size)
+        assert s[8] == 0 and s.size < 256 + size * x.size      # compresses
+    u = synth.random_bits(5000, 9) if dtype == 2 else \
+        np.random.default_rng(9).integers(0, 1 << 32, 5000, dtype=np.uint64).astype(np.uint32)
+    r = orc.encode(u, 512, dtype=dtype)
+    assert r[8] == 1 and r.size == 256 + size * 5000
+    assert np.array_equal(orc.decode(r), u)
+
+
+def test_fp16_exponent_ceiling_validate(orc):
+    # FP16 exponents stop at 31: base 29 with codes up to 2 (width 2) is
+    # valid; a planted code 3 gives 32 > 31
+    e = 29 + np.arange(64 * 60) % 3
+    x = (e << 10).astype(np.uint16) | (np.arange(e.size) % 1024).astype(np.uint16)
+    s = orc.encode(x, 64, dtype=orc.FP16)
+    assert s[8] == 0 and orc.validate(s) == (0, 0)
+    pay = int.from_bytes(bytes(s[72:80]), "little")
+    b = s.copy(); b[pay] |= 0b11                          # element 0's code -> 3
+    assert orc.validate(b) == (3, 0) == brute.validate(bytes(b))
