@@ -17,34 +17,46 @@
  *    weight is streamed once per generated token.
  *
  * Stream format (little-endian; all pad bytes zero):
- *   [0, 256)            header: "ENCB", u16 version=1, u16 dtype=1 (BF16),
+ *   [0, 256)            header: "ENCB", u16 version=1, u16 dtype (1 BF16,
+ *                       2 FP16, 3 FP32),
  *                       u32 flags (0 = coded, 1 = RAW, 2 = coded with
  *                       power-of-two widths), u32 block_size, u32 64,
  *                       u32 0, then u64 n_elems, n_blocks, n_segments, sm_off,
  *                       meta_off, segoff_off, payload_off, payload_bytes,
  *                       raw_off, total_bytes; bytes 104..255 zero.
- *   sm_off = 256        u8[n]: sign (bit 7) and mantissa (bits 6..0) of each
- *                       value, section padded to a multiple of 256.
+ *   sm_off = 256        the kept field of each value: sign on top of the
+ *                       mantissa, S bits (S = 8 for BF16: sign in bit 7,
+ *                       mantissa in bits 6..0; 11 for FP16; 24 for FP32),
+ *                       packed LSB first in element order (for BF16 one
+ *                       byte per value), ceil(S n / 8) bytes, section padded
+ *                       to a multiple of 256.
  *   meta_off            u8[2 * n_blocks]: {base, width} per block, padded.
  *   segoff_off          u64[n_segments]: exclusive prefix sum of padded block
  *                       payload sizes at each 64-block segment start, padded.
  *   payload_off         per block, ceil(width * len / 8) bytes rounded up to
  *                       16: the codes exponent - base, width bits each, packed
- *                       LSB first in element order.
+ *                       LSB first in element order. The exponent field is 8
+ *                       bits for BF16 and FP32, 5 bits for FP16.
  *   RAW streams (flags 1): header, then the n input values verbatim at
- *   raw_off = 256; chosen when the coded stream would not be smaller.
+ *   raw_off = 256 (2 or 4 bytes each); chosen when the coded stream would not
+ *   be smaller.
  *   Flags 2: the widths were rounded up to 0, 1, 2, 4 or 8 (ENEC Abstract:
  *   bit-width quantization with hierarchical halving bit-packing, read as
  *   power-of-two widths, so a byte holds exactly 8, 4, 2 or 1 codes); the
  *   layout is otherwise identical and every entry point reads such streams.
- *   A stream is valid only if every decoded exponent base + code is <= 255
- *   (always true for a stream written from BF16 input by these rules).
+ *   A stream is valid only if every decoded exponent base + code fits the
+ *   exponent field (<= 255, or <= 31 for FP16; always true for a stream
+ *   written by these rules).
+ *   FP16 and FP32 streams (the same code applied to the other float layouts)
+ *   are written by enc_compress_dt and read by enc_decompress, enc_read_info,
+ *   enc_parse_header and enc_validate; the batched decode and the GEMMs take
+ *   BF16 streams only (ENC_ERR_UNSUPPORTED otherwise).
  *
  * Conventions for every entry point:
  *  - d_ pointers are device (HBM) pointers, h_ pointers are host pointers.
  *    The caller owns every buffer; the library never allocates or frees
  *    device memory, and keeps no state between calls.
- *  - Device buffers holding streams, BF16 arrays and float arrays must be
+ *  - Device buffers holding streams, value arrays and float arrays must be
  *    16-byte aligned; inputs and outputs must not overlap.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls are asynchronous on that stream unless stated otherwise; a fault
@@ -112,6 +124,24 @@ enc_status enc_compress_ex(const uint16_t *d_in, uint64_t n_elems, uint32_t bloc
                            uint32_t options, void *d_out, uint64_t out_capacity, void *d_ws,
                            uint64_t ws_bytes, void *stream, enc_info *h_info);
 
+/* Largest stream an n-element input of the given dtype (1 BF16, 2 FP16,
+ * 3 FP32) can produce: 256 + element bytes x n (the RAW size); 0 for an
+ * unknown dtype. */
+uint64_t enc_compress_bound_dt(uint64_t n_elems, uint32_t dtype);
+
+/* Compress n values of the given dtype (bit patterns, 2 bytes each for BF16
+ * and FP16, 4 for FP32) -- the block code above with the element type's
+ * exponent and kept fields. dtype 1 is enc_compress_ex. For FP16 and FP32:
+ * a width kernel, the scan of segment sizes, one synchronisation of
+ * `stream` to read back the size, then the pack kernel (the input is read
+ * twice). Same block sizes, options, workspace size
+ * (enc_compress_workspace_bytes) and capacity rule (the final stream size;
+ * enc_compress_bound_dt always suffices). Unknown dtype:
+ * ENC_ERR_UNSUPPORTED. */
+enc_status enc_compress_dt(const void *d_in, uint64_t n_elems, uint32_t dtype, uint32_t block_size,
+                           uint32_t options, void *d_out, uint64_t out_capacity, void *d_ws,
+                           uint64_t ws_bytes, void *stream, enc_info *h_info);
+
 /* Parse and check a stream header held in host memory (header_bytes >= 256)
  * for a stream of comp_bytes bytes. Checks magic, version, dtype, flags,
  * block size, section offsets against n, and total <= comp_bytes. Host only;
@@ -123,18 +153,19 @@ enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_
  * `stream`) and parse it with enc_parse_header. */
 enc_status enc_read_info(const void *d_comp, uint64_t comp_bytes, void *stream, enc_info *h_info);
 
-/* Decompress a whole stream into out_elems BF16 values (ZipServ Abstract:
+/* Decompress a whole stream into out_elems values of the stream's dtype
+ * (2 bytes each for BF16 and FP16, 4 for FP32; ZipServ Abstract:
  * constant-time, parallel decoding). One kernel launch; asynchronous;
  * allocates nothing. h_info must describe d_comp (enc_read_info or the
  * enc_info enc_compress returned); out_elems must equal its n_elems. */
-enc_status enc_decompress(const void *d_comp, const enc_info *h_info, uint16_t *d_out,
+enc_status enc_decompress(const void *d_comp, const enc_info *h_info, void *d_out,
                           uint64_t out_elems, void *stream);
 
 /* Batched decompression: many streams, one launch (a model's whole weight
  * set decoded per step, as single-stream inference streams every weight
  * once per token -- MINE Abstract). */
 typedef struct enc_item {
-  const void *d_comp; /* device stream */
+  const void *d_comp; /* device stream (BF16) */
   uint16_t *d_out;    /* device output, info.n_elems values */
   enc_info info;      /* parsed header of d_comp */
 } enc_item;
@@ -211,8 +242,9 @@ enc_status enc_gemm_dense_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const 
  *                      prefix sum of the padded block payload sizes, or
  *                      payload_bytes differs from their total (ENEC
  *                      Abstract: block offsets come from a prefix scan);
- *   ENC_CHECK_EXPONENT some base + code exceeds 255 (the transform subtracts
- *                      the block minimum, so a valid code never does).
+ *   ENC_CHECK_EXPONENT some base + code exceeds the exponent field's
+ *                      maximum (255; 31 for FP16): the transform subtracts
+ *                      the block minimum, so a valid code never does.
  * index = the first failing block (width, exponent) or the first wrong stored
  * offset (offsets; index n_segments stands for payload_bytes). A RAW stream
  * has no device structure and always passes. d_ws: device workspace of at

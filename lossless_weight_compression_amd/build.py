@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libenc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["decode.hip", "encode.hip", "encode_onepass.hip", "gemm.hip", "validate.hip",
+SOURCES = ["decode.hip", "encode.hip", "encode_onepass.hip", "encode_wide.hip", "gemm.hip", "validate.hip",
            "enc_api.cpp"]
 ARCH = "gfx950"
 

@@ -60,7 +60,7 @@ __device__ __forceinline__ void copy_group_raw(const uint16_t *__restrict__ src,
 // all four 16-byte loads of a lane issued before the stores.
 __device__ __forceinline__ void copy_tile_raw(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
   const uint16_t *__restrict__ src = reinterpret_cast<const uint16_t *>(d.stream + kHeaderBytes);
-  uint16_t *__restrict__ out = d.out;
+  uint16_t *__restrict__ out = static_cast<uint16_t *>(d.out);
   const uint64_t e_a = tile * kTileElems + (uint64_t)tid * 8;
   const uint64_t e_b = e_a + 8 * kThreads, e_c = e_b + 8 * kThreads, e_d = e_c + 8 * kThreads;
   const uint4 z = make_uint4(0, 0, 0, 0);
@@ -75,13 +75,45 @@ __device__ __forceinline__ void copy_tile_raw(const DecodeDesc &d, uint64_t tile
 }
 static_assert(kGroupsPerThread == 4, "copy_tile_raw is written for 4 groups per lane");
 
+// Per-wave scan of the tile's segment: pk (lane j) = block j's base << 24 |
+// width << 20 | payload offset inside the segment, seg_payload = the
+// segment's payload start in the stream.
+__device__ __forceinline__ void segment_scan(const DecodeDesc &d, uint64_t seg, uint32_t lane,
+                                             uint32_t &pk, uint64_t &seg_payload) {
+  const uint8_t *__restrict__ s = d.stream;
+  const uint64_t n = d.n;
+  const uint64_t blk = (seg << 6) + lane;
+  uint32_t m = 0;
+  if (blk < d.nb) m = *reinterpret_cast<const uint16_t *>(s + d.meta_off + 2 * blk);
+  const uint32_t w = m >> 8;
+  const bool wide = __any(w > 8);   // wave-uniform
+  const uint32_t L = (blk + 1 == d.nb) ? (uint32_t)(n - ((d.nb - 1) << d.log2b)) : (1u << d.log2b);
+  const uint32_t P = (((w * L + 7) >> 3) + 15) & ~15u & (blk < d.nb ? ~0u : 0u);
+  pk = ((m & 0xFFu) << 24) | ((w & 15u) << 20);
+  const uint32_t incl = wave_incl_scan(P, lane);
+  pk |= incl - P;   // exclusive offset < 2^18 whenever every width is at most 8
+  const uint64_t seg_rel = *reinterpret_cast<const uint64_t *>(s + d.segoff_off + 8 * seg);
+  seg_payload = d.payload_off + seg_rel;
+  // Guard against corrupted streams (checked once per wave, not per group):
+  // a width above 8 or a segment whose payload runs past the stream end
+  // decodes as width 0, so no lane ever reads outside [0, total). The test
+  // is written without sums that could wrap (payload_off <= total holds for
+  // every header the host accepts).
+  const uint32_t seg_bytes = __shfl(incl, 63, 64);
+  const uint64_t room = d.total - d.payload_off;
+  if (wide || seg_rel > room || seg_bytes > room - seg_rel) {
+    pk = 0;
+    seg_payload = d.payload_off;
+  }
+}
+
 __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
   if (d.raw) {
     copy_tile_raw(d, tile, tid);
     return;
   }
   const uint8_t *__restrict__ s = d.stream;
-  uint16_t *__restrict__ out = d.out;
+  uint16_t *__restrict__ out = static_cast<uint16_t *>(d.out);
   const uint64_t n = d.n;
   const uint32_t lane = tid & 63;
   const uint32_t log2gpb = d.log2b - 3;       // groups per block
@@ -90,31 +122,9 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
   const uint64_t seg = g0 >> log2gps;
   const uint32_t gs0 = (uint32_t)(g0 & ((1ull << log2gps) - 1));
 
-  // Per-wave scan of the segment's padded block payload sizes.
-  const uint64_t blk = (seg << 6) + lane;
-  uint32_t P = 0, pk = 0;
-  if (blk < d.nb) {
-    const uint32_t m = *reinterpret_cast<const uint16_t *>(s + d.meta_off + 2 * blk);
-    const uint32_t w = m >> 8;
-    const uint32_t L = (blk + 1 == d.nb) ? (uint32_t)(n - ((d.nb - 1) << d.log2b)) : (1u << d.log2b);
-    P = (((w * L + 7) >> 3) + 15) & ~15u;
-    pk = ((m & 0xFFu) << 24) | (w << 20);
-  }
-  const uint32_t incl = wave_incl_scan(P, lane);
-  pk |= incl - P;   // exclusive offset < 2^18
-  const uint64_t seg_rel = *reinterpret_cast<const uint64_t *>(s + d.segoff_off + 8 * seg);
-  uint64_t seg_payload = d.payload_off + seg_rel;
-  // Guard against corrupted streams (checked once per wave, not per group):
-  // a width above 8 or a segment whose payload runs past the stream end
-  // decodes as width 0, so no lane ever reads outside [0, total). The test
-  // is written without sums that could wrap (payload_off <= total holds for
-  // every header the host accepts).
-  const uint32_t seg_bytes = __shfl(incl, 63, 64);
-  const uint64_t room = d.total - d.payload_off;
-  if (__any((pk >> 20 & 15u) > 8) || seg_rel > room || seg_bytes > room - seg_rel) {
-    pk = 0;
-    seg_payload = d.payload_off;
-  }
+  uint32_t pk;
+  uint64_t seg_payload;
+  segment_scan(d, seg, lane, pk, seg_payload);
 
   // Phase 1: issue every load of this lane's groups.
   uint32_t sml[GPT], smh[GPT], q0[GPT], q1[GPT], q2[GPT], info[GPT];
@@ -170,6 +180,142 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP16 (DT 2) and FP32 (DT 3) streams: the same exponent codes; the
+// sign+mantissa field is 11 / 24 bits per value, packed LSB first, so a
+// group's fields are 11 / 24 bytes at 11 g / 24 g of the section. Output
+// values are rebuilt field by field (sign << top | exponent << shift |
+// mantissa).
+// ---------------------------------------------------------------------------
+template <uint32_t DT>
+__device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
+  constexpr uint32_t ES = DT == 3 ? 4 : 2;        // element bytes
+  const uint8_t *__restrict__ s = d.stream;
+  uint8_t *__restrict__ outb = reinterpret_cast<uint8_t *>(d.out);
+  const uint64_t n = d.n;
+  const uint64_t g0 = tile * kTileGroups;
+  if (d.raw) {
+#pragma unroll
+    for (uint32_t it = 0; it < GPT; ++it) {
+      const uint64_t e0 = (g0 + it * kThreads + tid) * 8;
+      if (e0 >= n) continue;
+      if (e0 + 8 <= n) {
+#pragma unroll
+        for (uint32_t c = 0; c < ES / 2; ++c)
+          reinterpret_cast<uint4 *>(outb + e0 * ES)[c] =
+              reinterpret_cast<const uint4 *>(s + kHeaderBytes + e0 * ES)[c];
+      } else {
+        for (uint64_t b = e0 * ES; b < n * ES; ++b) outb[b] = s[kHeaderBytes + b];
+      }
+    }
+    return;
+  }
+  const uint32_t lane = tid & 63;
+  const uint32_t log2gpb = d.log2b - 3, log2gps = log2gpb + 6;
+  const uint64_t seg = g0 >> log2gps;
+  const uint32_t gs0 = (uint32_t)(g0 & ((1ull << log2gps) - 1));
+  uint32_t pk;
+  uint64_t seg_payload;
+  segment_scan(d, seg, lane, pk, seg_payload);
+
+#pragma unroll
+  for (uint32_t it = 0; it < GPT; ++it) {
+    const uint32_t q = it * kThreads + tid;
+    const uint64_t g = g0 + q;
+    const uint64_t e0 = g * 8;
+    const uint32_t gs = gs0 + q;
+    const uint32_t p = __shfl(pk, (int)(gs >> log2gpb), 64);   // with every lane active
+    if (e0 >= n) continue;
+    const uint32_t u = gs & ((1u << log2gpb) - 1);
+    const uint32_t w = (p >> 20) & 15u;
+    const uint64_t rem = n - e0;
+    const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
+    const uint32_t nbytes = (valid * w + 7) >> 3;
+    const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
+    uint32_t q0 = 0, q1 = 0, q2 = 0;
+    const uint32_t lead = (uint32_t)(pb & 3);
+    if (nbytes) {
+      const uint64_t a = pb & ~3ull;
+      q0 = ld32(s + a);
+      if (lead + nbytes > 4) q1 = ld32(s + a + 4);
+      if (lead + nbytes > 8) q2 = ld32(s + a + 8);
+    }
+    const uint32_t lo = __builtin_amdgcn_alignbit(q1, q0, lead * 8);
+    const uint32_t hi = __builtin_amdgcn_alignbit(q2, q1, lead * 8);
+    uint32_t el, eh;
+    codes_to_bytes(lo, hi, w, el, eh);
+    const uint32_t base4 = (p >> 24) * 0x01010101u;
+    el += base4;
+    eh += base4;
+    uint32_t e[8], sm[8];
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+      e[k] = (el >> (8 * k)) & 0xFFu;
+      e[k + 4] = (eh >> (8 * k)) & 0xFFu;
+    }
+    if (DT == 3) {
+      // 24-bit fields of 8 values: 24 bytes at 24 g (8-aligned). A tail
+      // group reads past the section's last field, never past the stream:
+      // the metadata and offset sections (256-byte aligned) follow.
+      const uint2 *src = reinterpret_cast<const uint2 *>(s + kHeaderBytes + 24 * g);
+      const uint2 v0 = src[0], v1 = src[1], v2 = src[2];
+      const uint32_t dw[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
+      sm[0] = dw[0] & 0xFFFFFFu;
+      sm[1] = __builtin_amdgcn_alignbit(dw[1], dw[0], 24) & 0xFFFFFFu;
+      sm[2] = __builtin_amdgcn_alignbit(dw[2], dw[1], 16) & 0xFFFFFFu;
+      sm[3] = dw[2] >> 8;
+      sm[4] = dw[3] & 0xFFFFFFu;
+      sm[5] = __builtin_amdgcn_alignbit(dw[4], dw[3], 24) & 0xFFFFFFu;
+      sm[6] = __builtin_amdgcn_alignbit(dw[5], dw[4], 16) & 0xFFFFFFu;
+      sm[7] = dw[5] >> 8;
+      uint32_t o[8];
+#pragma unroll
+      for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 23) << 31) | (e[k] << 23) | (sm[k] & 0x7FFFFFu);
+      uint32_t *dst = reinterpret_cast<uint32_t *>(outb) + e0;
+      if (valid == 8) {
+        reinterpret_cast<uint4 *>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4 *>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      } else {
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k)
+          if (k < valid) dst[k] = o[k];
+      }
+    } else {
+      // 11-bit fields of 8 values: 11 bytes at 11 g (any alignment), read as
+      // the 16-byte aligned-dword window that covers them (in the stream for
+      // the same reason as above)
+      const uint64_t b0 = kHeaderBytes + 11 * g;
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(s + (b0 & ~3ull));
+      const uint32_t sh = (uint32_t)(b0 & 3) * 8;
+      const uint32_t dw[4] = {src[0], src[1], src[2], src[3]};
+      const uint32_t f0 = __builtin_amdgcn_alignbit(dw[1], dw[0], sh);
+      const uint32_t f1 = __builtin_amdgcn_alignbit(dw[2], dw[1], sh);
+      const uint32_t f2 = __builtin_amdgcn_alignbit(dw[3], dw[2], sh);
+      // field k = bits [11 k, 11 k + 11) of f2:f1:f0
+      sm[0] = f0 & 0x7FFu;
+      sm[1] = (f0 >> 11) & 0x7FFu;
+      sm[2] = __builtin_amdgcn_alignbit(f1, f0, 22) & 0x7FFu;
+      sm[3] = (f1 >> 1) & 0x7FFu;
+      sm[4] = (f1 >> 12) & 0x7FFu;
+      sm[5] = __builtin_amdgcn_alignbit(f2, f1, 23) & 0x7FFu;
+      sm[6] = (f2 >> 2) & 0x7FFu;
+      sm[7] = (f2 >> 13) & 0x7FFu;
+      uint32_t o[8];
+#pragma unroll
+      for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 10) << 15) | ((e[k] & 0x1Fu) << 10) | (sm[k] & 0x3FFu);
+      uint16_t *dst = reinterpret_cast<uint16_t *>(outb) + e0;
+      if (valid == 8) {
+        *reinterpret_cast<uint4 *>(dst) =
+            make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16, o[6] | o[7] << 16);
+      } else {
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k)
+          if (k < valid) dst[k] = (uint16_t)o[k];
+      }
+    }
+  }
+}
+
 // Persistent grid, XCD-aware: workgroup i runs on XCD i mod 8 (round-robin
 // dispatch), so renumbering b = (i mod 8) * (G / 8) + i / 8 and giving each b
 // one contiguous run of tiles hands every XCD a contiguous eighth of the
@@ -189,6 +335,13 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeDesc d, uint64_t ntil
   uint64_t tb, te;
   tile_range(ntiles, tb, te);
   for (uint64_t t = tb; t < te; ++t) decode_tile(d, t, threadIdx.x);
+}
+
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_decode_wide(DecodeDesc d, uint64_t ntiles) {
+  uint64_t tb, te;
+  tile_range(ntiles, tb, te);
+  for (uint64_t t = tb; t < te; ++t) decode_tile_wide<DT>(d, t, threadIdx.x);
 }
 
 __global__ __launch_bounds__(kThreads) void k_decode_batch(const uint8_t *__restrict__ table) {
@@ -224,7 +377,13 @@ uint32_t persistent_grid(uint64_t ntiles) {
 hipError_t launch_decode(const DecodeDesc &d, hipStream_t s) {
   const uint64_t ntiles = tiles_for(d.n);
   if (ntiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode, dim3(persistent_grid(ntiles)), dim3(kThreads), 0, s, d, ntiles);
+  const dim3 grid(persistent_grid(ntiles));
+  if (d.dtype == 2)
+    hipLaunchKernelGGL(k_decode_wide<2>, grid, dim3(kThreads), 0, s, d, ntiles);
+  else if (d.dtype == 3)
+    hipLaunchKernelGGL(k_decode_wide<3>, grid, dim3(kThreads), 0, s, d, ntiles);
+  else
+    hipLaunchKernelGGL(k_decode, grid, dim3(kThreads), 0, s, d, ntiles);
   return hipGetLastError();
 }
 

@@ -70,17 +70,24 @@ int log2_block(uint32_t B) {
 
 constexpr uint64_t kMaxElems = 1ull << 40;
 
+// Header element types: 1 BF16, 2 FP16, 3 FP32. Bytes per value, bits of
+// the kept sign+mantissa field, and the largest exponent field value.
+bool dtype_known(uint32_t dt) { return dt >= 1 && dt <= 3; }
+uint32_t elem_bytes(uint32_t dt) { return dt == 3 ? 4u : 2u; }
+uint32_t kept_bits(uint32_t dt) { return dt == 2 ? 11u : dt == 3 ? 24u : 8u; }
+uint32_t exp_max(uint32_t dt) { return dt == 2 ? 31u : 255u; }
+
 struct Layout {
   uint64_t n, nb, nseg, sm_off, meta_off, segoff_off, payload_off;
 };
 
-Layout layout_of(uint64_t n, uint32_t B) {
+Layout layout_of(uint64_t n, uint32_t B, uint32_t dtype = 1) {
   Layout L;
   L.n = n;
   L.nb = (n + B - 1) / B;
   L.nseg = (L.nb + kSegBlocks - 1) / kSegBlocks;
   L.sm_off = kHeaderBytes;
-  L.meta_off = L.sm_off + align_up(n, kSectionAlign);
+  L.meta_off = L.sm_off + align_up((kept_bits(dtype) * n + 7) / 8, kSectionAlign);
   L.segoff_off = L.meta_off + align_up(2 * L.nb, kSectionAlign);
   L.payload_off = L.segoff_off + align_up(8 * L.nseg, kSectionAlign);
   return L;
@@ -112,29 +119,29 @@ HeaderImage header_of(const enc_info &i) {
   return h;
 }
 
-enc_info raw_info(uint64_t n, uint32_t B) {
+enc_info raw_info(uint64_t n, uint32_t B, uint32_t dtype = 1) {
   enc_info i;
   memset(&i, 0, sizeof i);
   i.version = 1;
-  i.dtype = 1;
+  i.dtype = dtype;
   i.flags = 1;
   i.block_size = B;
   i.n_elems = n;
   i.raw_off = kHeaderBytes;
-  i.total_bytes = kHeaderBytes + 2 * n;
+  i.total_bytes = kHeaderBytes + elem_bytes(dtype) * n;
   return i;
 }
 
 // Consistency of a parsed header with the format (no device data read).
 enc_status check_info(const enc_info *i) {
   if (!i) return fail(ENC_ERR_INVALID_ARG, "info is NULL");
-  if (i->version != 1 || i->dtype != 1)
+  if (i->version != 1 || !dtype_known(i->dtype))
     return fail(ENC_ERR_BAD_STREAM, "version %u / dtype %u not supported", i->version, i->dtype);
   if (i->n_elems > kMaxElems) return fail(ENC_ERR_UNSUPPORTED, "n_elems above 2^40");
   if (i->flags == 1) {
     if (i->n_blocks || i->n_segments || i->sm_off || i->meta_off || i->segoff_off ||
         i->payload_off || i->payload_bytes || i->raw_off != kHeaderBytes ||
-        i->total_bytes != kHeaderBytes + 2 * i->n_elems)
+        i->total_bytes != kHeaderBytes + elem_bytes(i->dtype) * i->n_elems)
       return fail(ENC_ERR_BAD_STREAM, "inconsistent RAW header");
     return ENC_OK;
   }
@@ -143,7 +150,7 @@ enc_status check_info(const enc_info *i) {
     return fail(ENC_ERR_UNSUPPORTED, "block size %u (library supports 128..4096, powers of two)",
                 i->block_size);
   if (i->n_elems == 0) return fail(ENC_ERR_BAD_STREAM, "coded stream with zero elements");
-  const Layout L = layout_of(i->n_elems, i->block_size);
+  const Layout L = layout_of(i->n_elems, i->block_size, i->dtype);
   if (i->n_blocks != L.nb || i->n_segments != L.nseg || i->sm_off != L.sm_off ||
       i->meta_off != L.meta_off || i->segoff_off != L.segoff_off ||
       i->payload_off != L.payload_off || i->raw_off != 0 ||
@@ -154,13 +161,14 @@ enc_status check_info(const enc_info *i) {
   return ENC_OK;
 }
 
-DecodeDesc desc_of(const void *d_comp, const enc_info &i, uint16_t *d_out) {
+DecodeDesc desc_of(const void *d_comp, const enc_info &i, void *d_out) {
   DecodeDesc d;
   memset(&d, 0, sizeof d);
   d.stream = static_cast<const uint8_t *>(d_comp);
   d.out = d_out;
   d.n = i.n_elems;
   d.total = i.total_bytes;
+  d.dtype = i.dtype;
   if (i.flags == 1) {
     d.raw = 1;
     d.log2b = kMinLog2B;
@@ -175,11 +183,11 @@ DecodeDesc desc_of(const void *d_comp, const enc_info &i, uint16_t *d_out) {
 }
 
 enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t payload,
-                    uint32_t pow2) {
+                    uint32_t pow2, uint32_t dtype = 1) {
   enc_info i;
   memset(&i, 0, sizeof i);
   i.version = 1;
-  i.dtype = 1;
+  i.dtype = dtype;
   i.flags = pow2 ? 2 : 0;
   i.block_size = block_size;
   i.n_elems = n;
@@ -261,6 +269,65 @@ enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_si
   return ENC_OK;
 }
 
+// FP16 / FP32 input: block parameters, the segment scan, then the pack
+// (reads the input twice); RAW when the coded stream would not be smaller.
+enc_status compress_wide(const void *d_in, uint64_t n, uint32_t dtype, uint32_t block_size,
+                         uint32_t pow2, uint8_t *d_out, uint64_t cap, uint8_t *d_ws,
+                         hipStream_t s, enc_info *h_info) {
+  const Layout L = layout_of(n, block_size, dtype);
+  EncodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.in = static_cast<const uint16_t *>(d_in);
+  a.out = d_out;
+  a.ws_meta = d_ws;
+  a.ws_segsum = reinterpret_cast<uint64_t *>(a.ws_meta + align_up(2 * L.nb, kSectionAlign));
+  a.ws_total = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(a.ws_segsum) +
+                                            align_up(8 * L.nseg, kSectionAlign));
+  a.n = n;
+  a.nb = L.nb;
+  a.nseg = L.nseg;
+  a.meta_off = L.meta_off;
+  a.segoff_off = L.segoff_off;
+  a.payload_off = L.payload_off;
+  a.log2b = (uint32_t)log2_block(block_size);
+  a.pow2 = pow2;
+  hipError_t e = launch_encode_wide_params(a, dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "width kernel launch");
+  e = launch_encode_scan(a, s);
+  if (e != hipSuccess) return hip_fail(e, "scan kernel launch");
+  uint64_t payload = 0;
+  e = hipMemcpyAsync(&payload, a.ws_total, sizeof payload, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "size read-back");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  const uint64_t raw_total = kHeaderBytes + elem_bytes(dtype) * n;
+  const uint64_t coded_total = L.payload_off + payload;
+  enc_info i;
+  if (coded_total >= raw_total) {
+    if (cap < raw_total)
+      return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
+                  (unsigned long long)cap, (unsigned long long)raw_total);
+    i = raw_info(n, block_size, dtype);
+    // the verbatim copy moves 16-bit units
+    const enc_status st = launched(launch_encode_raw(a.in, d_out, n * (elem_bytes(dtype) / 2),
+                                                     header_of(i), s),
+                                   s, "raw copy launch");
+    if (st != ENC_OK) return st;
+  } else {
+    if (cap < coded_total)
+      return fail(ENC_ERR_CAPACITY, "output capacity %llu below stream size %llu",
+                  (unsigned long long)cap, (unsigned long long)coded_total);
+    i = coded_info(n, block_size, L, payload, pow2, dtype);
+    e = launch_encode_wide_pack(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
+    const enc_status st = launched(launch_encode_wide_finish(a, dtype, header_of(i), s), s,
+                                   "finish kernel launch");
+    if (st != ENC_OK) return st;
+  }
+  *h_info = i;
+  return ENC_OK;
+}
+
 uint64_t batch_bytes(int count) {
   return align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
                       8 * ((uint64_t)count + 1),
@@ -272,6 +339,10 @@ uint64_t batch_bytes(int count) {
 extern "C" {
 
 uint64_t enc_compress_bound(uint64_t n_elems) { return kHeaderBytes + 2 * n_elems; }
+
+uint64_t enc_compress_bound_dt(uint64_t n_elems, uint32_t dtype) {
+  return dtype_known(dtype) ? kHeaderBytes + elem_bytes(dtype) * n_elems : 0;
+}
 
 uint64_t enc_compress_workspace_bytes(uint64_t n_elems, uint32_t block_size) {
   if (log2_block(block_size) < 0) return 0;
@@ -382,6 +453,44 @@ enc_status enc_compress_ex(const uint16_t *d_in, uint64_t n, uint32_t block_size
   return ENC_OK;
 }
 
+enc_status enc_compress_dt(const void *d_in, uint64_t n, uint32_t dtype, uint32_t block_size,
+                           uint32_t options, void *d_out, uint64_t out_capacity, void *d_ws,
+                           uint64_t ws_bytes, void *stream, enc_info *h_info) {
+  clear_err();
+  if (!dtype_known(dtype)) return fail(ENC_ERR_UNSUPPORTED, "dtype %u (1 BF16, 2 FP16, 3 FP32)", dtype);
+  if (dtype == 1)
+    return enc_compress_ex(static_cast<const uint16_t *>(d_in), n, block_size, options, d_out,
+                           out_capacity, d_ws, ws_bytes, stream, h_info);
+  if (options & ~(uint32_t)ENC_OPT_POW2_WIDTHS)
+    return fail(ENC_ERR_INVALID_ARG, "unknown options 0x%x", options);
+  const uint32_t pow2 = (options & ENC_OPT_POW2_WIDTHS) ? 1u : 0u;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!h_info) return fail(ENC_ERR_INVALID_ARG, "h_info is NULL");
+  if (!d_out) return fail(ENC_ERR_INVALID_ARG, "d_out is NULL");
+  if (n > 0 && !d_in) return fail(ENC_ERR_INVALID_ARG, "d_in is NULL");
+  if (log2_block(block_size) < 0)
+    return fail(ENC_ERR_UNSUPPORTED, "block size %u (supported: 128..4096, powers of two)",
+                block_size);
+  if (n > kMaxElems) return fail(ENC_ERR_UNSUPPORTED, "n above 2^40");
+  if (!aligned16(d_in) || !aligned16(d_out) || !aligned16(d_ws))
+    return fail(ENC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (n == 0) {
+    if (out_capacity < kHeaderBytes) return fail(ENC_ERR_CAPACITY, "output capacity below 256");
+    const enc_info i = raw_info(0, block_size, dtype);
+    const enc_status st = launched(launch_encode_raw(static_cast<const uint16_t *>(d_in),
+                                                     static_cast<uint8_t *>(d_out), 0, header_of(i), s),
+                                   s, "raw header launch");
+    if (st != ENC_OK) return st;
+    *h_info = i;
+    return ENC_OK;
+  }
+  const uint64_t need_ws = enc_compress_workspace_bytes(n, block_size);
+  if (!d_ws || ws_bytes < need_ws)
+    return fail(ENC_ERR_CAPACITY, "workspace of %llu bytes needed", (unsigned long long)need_ws);
+  return compress_wide(d_in, n, dtype, block_size, pow2, static_cast<uint8_t *>(d_out),
+                       out_capacity, static_cast<uint8_t *>(d_ws), s, h_info);
+}
+
 enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_t comp_bytes,
                             enc_info *h_info) {
   clear_err();
@@ -426,7 +535,7 @@ enc_status enc_read_info(const void *d_comp, uint64_t comp_bytes, void *stream, 
   return enc_parse_header(h, kHeaderBytes, comp_bytes, h_info);
 }
 
-enc_status enc_decompress(const void *d_comp, const enc_info *h_info, uint16_t *d_out,
+enc_status enc_decompress(const void *d_comp, const enc_info *h_info, void *d_out,
                           uint64_t out_elems, void *stream) {
   clear_err();
   const enc_status st = check_info(h_info);
@@ -471,6 +580,8 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
       memcpy(why, g_err, sizeof why);
       return fail(st, "item %d: %s", k, why);
     }
+    if (it.info.dtype != 1)
+      return fail(ENC_ERR_UNSUPPORTED, "item %d: the batched decode takes BF16 streams only", k);
     if (!it.d_comp || (it.info.n_elems && !it.d_out))
       return fail(ENC_ERR_INVALID_ARG, "item %d: NULL pointer", k);
     if (!aligned16(it.d_comp) || !aligned16(it.d_out))
@@ -533,6 +644,7 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
   clear_err();
   enc_status st = check_info(h_winfo);
   if (st != ENC_OK) return st;
+  if (h_winfo->dtype != 1) return fail(ENC_ERR_UNSUPPORTED, "the GEMM takes BF16 weights only");
   if (!d_wcomp || !aligned16(d_wcomp)) return fail(ENC_ERR_INVALID_ARG, "d_wcomp NULL or unaligned");
   if ((uint64_t)K * N != h_winfo->n_elems)
     return fail(ENC_ERR_SHAPE, "K*N=%llu but the stream holds %llu elements",
@@ -607,6 +719,7 @@ enc_status enc_decompress_gemm_nt(const uint16_t *d_x, uint32_t M, uint32_t K, c
   clear_err();
   enc_status st = check_info(h_winfo);
   if (st != ENC_OK) return st;
+  if (h_winfo->dtype != 1) return fail(ENC_ERR_UNSUPPORTED, "the GEMM takes BF16 weights only");
   if (!d_wcomp || !aligned16(d_wcomp)) return fail(ENC_ERR_INVALID_ARG, "d_wcomp NULL or unaligned");
   if ((uint64_t)K * N != h_winfo->n_elems)
     return fail(ENC_ERR_SHAPE, "K*N=%llu but the stream holds %llu elements",
@@ -675,6 +788,7 @@ enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, 
   a.payload_bytes = h_info->payload_bytes;
   a.log2b = (uint32_t)log2_block(h_info->block_size);
   a.pow2 = h_info->flags == 2;
+  a.emax = exp_max(h_info->dtype);
   hipError_t e = hipMemsetAsync(d_ws, 0xFF, 3 * sizeof(unsigned long long), s);
   if (e != hipSuccess) return hip_fail(e, "result initialisation");
   e = launch_validate(a, s);
@@ -688,7 +802,7 @@ enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, 
                                       "in a stream that declares power-of-two widths)",
                                       "stored segment offset %llu is not the prefix sum of the "
                                       "block sizes (index n_segments = payload_bytes)",
-                                      "block %llu decodes an exponent above 255"};
+                                      "block %llu decodes an exponent above the field's maximum"};
   for (int k = 0; k < 3; ++k) {
     if (r[k] != ~0ull) {
       if (h_check) {

@@ -46,7 +46,7 @@ __host__ __device__ inline uint32_t block_width(uint32_t r, uint32_t pow2) {
 // batched calls). 80 bytes.
 struct DecodeDesc {
   const uint8_t *stream;   // device stream base
-  uint16_t *out;           // device output
+  void *out;               // device output (element type from dtype)
   uint64_t n;              // elements
   uint64_t nb;             // blocks (0 for RAW)
   uint64_t meta_off;       // section offsets inside the stream
@@ -55,7 +55,8 @@ struct DecodeDesc {
   uint64_t total;          // stream bytes (reads never go past it)
   uint32_t log2b;          // log2 of the block size
   uint32_t raw;            // 1 = RAW stream (verbatim values at offset 256)
-  uint64_t reserved;
+  uint32_t dtype;          // header element type: 0 or 1 BF16, 2 FP16, 3 FP32
+  uint32_t reserved;
 };
 static_assert(sizeof(DecodeDesc) == 80, "table entry layout");
 
@@ -113,6 +114,11 @@ hipError_t launch_encode_finish(const EncodeArgs &a, const HeaderImage &h, hipSt
 hipError_t launch_encode_pads(const EncodeArgs &a, const HeaderImage &h, hipStream_t s);
 hipError_t launch_encode_raw(const uint16_t *in, uint8_t *out, uint64_t n, const HeaderImage &h,
                              hipStream_t s);
+// FP16 (dtype 2) and FP32 (dtype 3) input; the scan is launch_encode_scan.
+hipError_t launch_encode_wide_params(const EncodeArgs &a, uint32_t dtype, hipStream_t s);
+hipError_t launch_encode_wide_pack(const EncodeArgs &a, uint32_t dtype, hipStream_t s);
+hipError_t launch_encode_wide_finish(const EncodeArgs &a, uint32_t dtype, const HeaderImage &h,
+                                     hipStream_t s);
 
 // ---- deep stream check ------------------------------------------------------
 struct ValidateArgs {
@@ -122,6 +128,7 @@ struct ValidateArgs {
   uint64_t meta_off, segoff_off, payload_off, payload_bytes;
   uint32_t log2b;
   uint32_t pow2;         // 1: the stream declares power-of-two widths
+  uint32_t emax;         // largest exponent field value: 255 (BF16, FP32), 31 (FP16)
 };
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 

@@ -4,7 +4,8 @@
 // a power of two in a stream that declares power-of-two widths),
 // (2) the stored segment offsets are the exclusive prefix sums of the padded
 // block payload sizes (and payload_bytes is their total), and (3) every
-// decoded exponent base + code fits in a byte. Condition (2) is what lets a
+// decoded exponent base + code fits the element type's exponent field (255
+// for BF16 and FP32, 31 for FP16). Condition (2) is what lets a
 // decoder locate any block from its segment offset and an intra-segment scan
 // ("ENEC: A Lossless AI Model Compression Method Enabling Fast Inference on
 // Ascend NPUs", Abstract: intra-segment prefix scan of block sizes); (3) is
@@ -18,10 +19,11 @@
 //             0. If stored[0..k) are right and stored[k] is not, the first
 //             failing difference is at s = k - 1, so reporting s + 1 yields
 //             the first wrong offset, k, as the minimum over all waves;
-//  * exponent: only lanes whose base + 2^w - 1 can exceed 255 read their
-//             codes (never, for streams written from BF16 input), and only
+//  * exponent: only lanes whose base + 2^w - 1 can exceed the maximum read
+//             their codes (never, for streams the encoders write), and only
 //             when the segment's payload range lies inside the payload
-//             section, so every read stays in bounds.
+//             section, so every read stays in bounds; a width-0 block fails
+//             on its base alone, without a read.
 // Failures are reported with one 64-bit atomic minimum per failing lane into
 // result[kind] (initialised to all ones by the host).
 #include "enc_common.h"
@@ -59,14 +61,15 @@ __global__ __launch_bounds__(kThreads) void k_validate(ValidateArgs a) {
     }
 
     const bool inside = so <= a.payload_bytes && seg_sum <= a.payload_bytes - so;
-    if (valid && inside && w >= 1 && w <= 8 && base + (1u << w) - 1 > 255) {
+    if (valid && w == 0 && base > a.emax) atomicMin(&a.result[2], (unsigned long long)blk);
+    if (valid && inside && w >= 1 && w <= 8 && base + (1u << w) - 1 > a.emax) {
       const uint8_t *q = s + a.payload_off + so + (incl - P);
       for (uint32_t t = 0; t < L; ++t) {
         const uint32_t bit = t * w, byte = bit >> 3, sh = bit & 7;
         uint32_t v = q[byte];
         if (sh + w > 8) v |= (uint32_t)q[byte + 1] << 8;   // the field's bits end in that byte
         const uint32_t d = (v >> sh) & ((1u << w) - 1);
-        if (base + d > 255) {
+        if (base + d > a.emax) {
           atomicMin(&a.result[2], (unsigned long long)blk);
           break;
         }

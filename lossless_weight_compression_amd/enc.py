@@ -67,6 +67,8 @@ SIGNATURES = {
     "enc_compress_workspace_bytes": (_U64, [_U64, _U32]),
     "enc_compress": (_ST, [_VP, _U64, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
     "enc_compress_ex": (_ST, [_VP, _U64, _U32, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
+    "enc_compress_bound_dt": (_U64, [_U64, _U32]),
+    "enc_compress_dt": (_ST, [_VP, _U64, _U32, _U32, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
     "enc_parse_header": (_ST, [_VP, _U64, _U64, _INFO_P]),
     "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
     "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
@@ -132,6 +134,25 @@ def _bits(x):
     return x.view(torch.int16)
 
 
+BF16, FP16, FP32 = 1, 2, 3           # header element types
+ELEM_BYTES = {BF16: 2, FP16: 2, FP32: 4}
+
+
+def _dtype_of(x, dtype):
+    """Header element type of x: given, or float16 -> FP16, float32 -> FP32,
+    anything else of 2 bytes (bfloat16, or BF16 bit patterns) -> BF16."""
+    import torch
+    if dtype is None:
+        dtype = {torch.float16: FP16, torch.float32: FP32}.get(x.dtype, BF16)
+    if dtype not in ELEM_BYTES:
+        raise ValueError("dtype must be 1 (BF16), 2 (FP16) or 3 (FP32)")
+    if x.element_size() != ELEM_BYTES[dtype]:
+        raise TypeError("a dtype-%d tensor needs %d-byte elements" % (dtype, ELEM_BYTES[dtype]))
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("expected a contiguous CUDA tensor")
+    return dtype
+
+
 def _empty_u8(nbytes, device):
     import torch
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
@@ -149,10 +170,28 @@ def enc_compress_workspace_bytes(n_elems, block_size):
 ENC_OPT_POW2_WIDTHS = 1
 
 
-def enc_compress(x, block_size=512, out=None, ws=None, stream=None, pow2_widths=False):
-    """Compress the BF16 tensor x. Returns (stream bytes as a uint8 CUDA tensor
-    sliced to the stream size, EncInfo). pow2_widths: enc_compress_ex with
-    ENC_OPT_POW2_WIDTHS."""
+def enc_compress_bound_dt(n_elems, dtype):
+    return int(lib().enc_compress_bound_dt(n_elems, dtype))
+
+
+def enc_compress(x, block_size=512, out=None, ws=None, stream=None, pow2_widths=False, dtype=None):
+    """Compress the tensor x. Returns (stream bytes as a uint8 CUDA tensor
+    sliced to the stream size, EncInfo). pow2_widths: ENC_OPT_POW2_WIDTHS.
+    BF16 input goes through enc_compress / enc_compress_ex, FP16 and FP32
+    input (dtype inferred from x, see _dtype_of) through enc_compress_dt."""
+    dtype = _dtype_of(x, dtype)
+    if dtype != BF16:
+        n = x.numel()
+        if out is None:
+            out = _empty_u8(enc_compress_bound_dt(n, dtype), x.device)
+        if ws is None:
+            ws = _empty_u8(enc_compress_workspace_bytes(n, block_size), x.device)
+        info = EncInfo()
+        _check(lib().enc_compress_dt(_ptr(x), n, dtype, block_size,
+                                     ENC_OPT_POW2_WIDTHS if pow2_widths else 0, _ptr(out),
+                                     out.numel(), _ptr(ws), ws.numel(), _stream(stream),
+                                     ctypes.byref(info)))
+        return out[:info.total_bytes], info
     x = _bits(x)
     n = x.numel()
     if out is None:
@@ -189,10 +228,12 @@ def enc_read_info(comp, stream=None):
 
 
 def enc_decompress(comp, info, out=None, stream=None):
-    """Decode a stream into an int16 CUDA tensor of info.n_elems BF16 bit patterns."""
+    """Decode a stream into a CUDA tensor of info.n_elems bit patterns: int16
+    for BF16 and FP16 streams, int32 for FP32 streams."""
     import torch
     if out is None:
-        out = torch.empty(max(info.n_elems, 1), dtype=torch.int16, device=comp.device)[:info.n_elems]
+        tdt = torch.int32 if info.dtype == FP32 else torch.int16
+        out = torch.empty(max(info.n_elems, 1), dtype=tdt, device=comp.device)[:info.n_elems]
     _check(lib().enc_decompress(_ptr(comp), ctypes.byref(info), _ptr(out), out.numel(),
                                 _stream(stream)))
     return out

@@ -136,3 +136,56 @@ def test_host_validation_before_any_launch(L):
     assert L.enc_decompress_batch(vp(16), -1, vp(0)) == -1
     assert L.enc_decompress_batch(vp(0), 3, vp(0)) == -1
     assert L.enc_batch_prepare(None, 1, vp(16), 1 << 20, vp(0)) == -1
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_parse_oracle_wide_headers(L, orc, dtype):
+    """FP16 / FP32 streams of the oracle parse to the layout their kept-field
+    width fixes (11 or 24 bits per value), coded and RAW."""
+    x = synth.gaussian_values((96, 1000), 0.02, 81, dtype, dtype)
+    B = 512
+    s = orc.encode(x.reshape(-1), B, dtype=dtype)
+    info = enc.enc_parse_header(s[:256], s.size)
+    n = x.size
+    S = 11 if dtype == 2 else 24
+    assert (info.version, info.dtype, info.flags, info.block_size) == (1, dtype, 0, B)
+    assert info.meta_off == 256 + -(-((S * n + 7) // 8) // 256) * 256
+    assert info.total_bytes == s.size
+    # the same stream claiming the other wide type no longer matches its layout
+    b = np.array(s[:256]); b[6] = 5 - dtype
+    with pytest.raises(enc.EncError) as e:
+        enc.enc_parse_header(b, s.size)
+    assert e.value.status == -4
+    bits = (np.arange(3000, dtype=np.uint64) * 2654435761) % (1 << 32)
+    raw_in = (bits & 0xFFFF).astype(np.uint16) if dtype == 2 else bits.astype(np.uint32)
+    raw = orc.encode(raw_in, B, dtype=dtype)
+    ri = enc.enc_parse_header(raw[:256], raw.size)
+    assert (ri.flags, ri.dtype, ri.total_bytes) == (1, dtype, 256 + (2 if dtype == 2 else 4) * 3000)
+
+
+def test_wide_entry_points_host_checks(L):
+    assert enc.enc_compress_bound_dt(1000, 1) == 2256
+    assert enc.enc_compress_bound_dt(1000, 2) == 2256
+    assert enc.enc_compress_bound_dt(1000, 3) == 4256
+    assert enc.enc_compress_bound_dt(1000, 4) == 0
+    vp = ctypes.c_void_p
+    out = enc.EncInfo()
+    # unknown dtype, bad block size, missing workspace, unknown option: before any launch
+    assert L.enc_compress_dt(vp(16), 100, 4, 512, 0, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -2
+    assert L.enc_compress_dt(vp(16), 100, 3, 300, 0, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -2
+    assert L.enc_compress_dt(vp(16), 100000, 2, 512, 0, vp(16), 300000, vp(0), 0, vp(0), ctypes.byref(out)) == -3
+    assert L.enc_compress_dt(vp(16), 100, 3, 512, 8, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -1
+    # FP16 / FP32 streams: the batched decode and the GEMMs refuse them
+    info = enc.EncInfo()
+    info.version, info.dtype, info.flags = 1, 3, 1
+    info.n_elems, info.raw_off, info.total_bytes = 4096 * 512, 256, 256 + 4 * 4096 * 512
+    assert L.enc_decompress_gemm(vp(16), 1, 4096, vp(16), ctypes.byref(info), 512, vp(16), vp(16),
+                                 1 << 30, vp(0)) == -2
+    assert L.enc_decompress_gemm_nt(vp(16), 1, 4096, vp(16), ctypes.byref(info), 512, vp(16), vp(16),
+                                    1 << 30, vp(0)) == -2
+    item = enc.EncItem()
+    item.d_comp, item.d_out, item.info = 16, 16, info
+    assert L.enc_batch_prepare(ctypes.byref(item), 1, vp(16), 1 << 20, vp(0)) == -2
+    # a RAW FP32 header with the BF16 total is inconsistent
+    info.total_bytes = 256 + 2 * 4096 * 512
+    assert L.enc_decompress(vp(16), ctypes.byref(info), vp(16), 4096 * 512, vp(0)) == -4

@@ -1,0 +1,203 @@
+"""FP16 and FP32 streams on the GPU (header dtype 2 and 3) against the CPU
+oracle, through the C ABI: the same block code with the element type's
+exponent field coded and the sign+mantissa field kept (11 or 24 bits).
+
+Parity is bit-exact: enc_compress_dt must write the oracle's stream byte for
+byte (coded, power-of-two widths and RAW), enc_decompress must return the
+input bits for oracle streams, and enc_validate must name the oracle's
+failure on damaged streams. Sizes span single groups, ragged tails, several
+tiles and segments, every block size class, and a full 4096 x 14336 layer.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import corruptions
+from lossless_weight_compression_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TORCH_INT = {2: "int16", 3: "int32"}
+NP_INT = {2: np.int16, 3: np.int32}
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def E():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_weight_compression_amd import enc
+    enc.lib()
+    return enc
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(NP_INT[dtype])).cuda()
+
+
+def dev8(s):
+    return torch.from_numpy(np.ascontiguousarray(s, dtype=np.uint8)).cuda()
+
+
+def host_bits(t, dtype):
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if dtype == 2 else a.view(np.uint32)
+
+
+def values(n, dtype, seed):
+    return synth.gaussian_values((n,), 0.02, 120 + dtype, seed, dtype)
+
+
+def gpu_stream(E, x, dtype, B, pow2=False):
+    comp, info = E.enc_compress(dev(x, dtype), B, pow2_widths=pow2, dtype=dtype)
+    torch.cuda.synchronize()
+    return comp.cpu().numpy(), info
+
+
+SIZES = [1, 7, 8, 9, 85, 1000, 8191, 8192, 8193, 65536 + 24, 300_001]
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+@pytest.mark.parametrize("n", SIZES)
+def test_encode_matches_oracle(E, orc, dtype, n):
+    x = values(n, dtype, n)
+    for B in (128, 512, 4096):
+        say("wide encode dtype=%d n=%d B=%d" % (dtype, n, B))
+        want = orc.encode(x, B, dtype=dtype)
+        got, info = gpu_stream(E, x, dtype, B)
+        assert info.dtype == dtype and info.total_bytes == want.size
+        assert np.array_equal(got, want), (dtype, n, B)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+@pytest.mark.parametrize("B", [128, 256, 1024, 2048])
+def test_pow2_widths_match_oracle(E, orc, dtype, B):
+    x = values(200_003, dtype, B)
+    say("wide pow2 dtype=%d B=%d" % (dtype, B))
+    want = orc.encode(x, B, pow2=True, dtype=dtype)
+    got, info = gpu_stream(E, x, dtype, B, pow2=True)
+    assert info.flags == 2
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_raw_and_empty(E, orc, dtype):
+    rng = np.random.default_rng(dtype)
+    bits = rng.integers(0, 1 << (16 if dtype == 2 else 32), 50_001, dtype=np.uint64)
+    x = bits.astype(np.uint16 if dtype == 2 else np.uint32)
+    say("wide RAW dtype=%d" % dtype)
+    want = orc.encode(x, 512, dtype=dtype)
+    got, info = gpu_stream(E, x, dtype, 512)
+    assert info.flags == 1 and np.array_equal(got, want)
+    out = E.enc_decompress(dev8(want), E.enc_read_info(dev8(want)))
+    assert np.array_equal(host_bits(out, dtype), x)
+    empty = np.zeros(0, x.dtype)
+    want = orc.encode(empty, 512, dtype=dtype)
+    comp, info = E.enc_compress(torch.zeros(8, dtype=getattr(torch, TORCH_INT[dtype]),
+                                            device="cuda")[:0], 512, dtype=dtype)
+    assert info.n_elems == 0 and np.array_equal(comp.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+@pytest.mark.parametrize("n", [9, 8193, 300_001])
+def test_decode_oracle_streams(E, orc, dtype, n):
+    x = values(n, dtype, 7 + n)
+    for B in (128, 512, 4096):
+        for pow2 in (False, True):
+            s = orc.encode(x, B, pow2=pow2, dtype=dtype)
+            say("wide decode dtype=%d n=%d B=%d pow2=%d" % (dtype, n, B, pow2))
+            d = dev8(s)
+            out = E.enc_decompress(d, E.enc_read_info(d))
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits(out, dtype), x), (dtype, n, B, pow2)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_special_values(E, orc, dtype):
+    # zeros of both signs, subnormals, infinities, NaNs, the extreme exponents
+    if dtype == 2:
+        specials = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x7C00, 0xFC00, 0x7E00, 0x7BFF,
+                             0x0400, 0x3C00], np.uint16)
+    else:
+        specials = np.array([0, 0x80000000, 1, 0x007FFFFF, 0x7F800000, 0xFF800000, 0x7FC00000,
+                             0x7F7FFFFF, 0x00800000, 0x3F800000], np.uint32)
+    x = np.tile(specials, 1000)
+    for B in (128, 512):
+        say("wide specials dtype=%d B=%d" % (dtype, B))
+        want = orc.encode(x, B, dtype=dtype)
+        got, info = gpu_stream(E, x, dtype, B)
+        assert np.array_equal(got, want)
+        out = E.enc_decompress(dev8(got), info)
+        assert np.array_equal(host_bits(out, dtype), x)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_full_layer(E, orc, dtype):
+    """A 4096 x 14336 projection as FP16 / FP32: the whole stream equals the
+    oracle's, and the GPU round trip is exact."""
+    x = synth.gaussian_values((4096, 14336), 0.02, 1, 5, dtype).reshape(-1)
+    say("wide full layer dtype=%d" % dtype)
+    got, info = gpu_stream(E, x, dtype, 512)
+    want = orc.encode(x, 512, dtype=dtype)
+    assert info.flags == 0 and np.array_equal(got, want)
+    out = E.enc_decompress(dev8(got), info)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out, dtype), x)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_validate_matches_oracle(E, orc, dtype):
+    x = synth.gaussian_values((384, 4096), 0.02, 93, dtype, dtype).reshape(-1)
+    s = orc.encode(x, 512, dtype=dtype)
+    assert s[8] == 0
+    kinds_seen = set()
+    for seed, kind in enumerate(corruptions.KINDS * 2):
+        b = corruptions.corrupt(s, kind, 9100 + 10 * dtype + seed)
+        want = orc.validate(b)
+        kinds_seen.add(want[0])
+        say("wide corruption dtype=%d" % dtype, kind, "seed", seed, "oracle says", want)
+        d = dev8(b)
+        info = E.enc_read_info(d)
+        chk = E.enc_validate(d, info)
+        assert (chk.kind, chk.index) == want, (kind, seed)
+        out = E.enc_decompress(d, info)   # runs to completion on any damage
+        torch.cuda.synchronize()
+        if want[0] == 0:
+            assert np.array_equal(host_bits(out, dtype), orc.decode(b)), (kind, seed)
+    assert kinds_seen >= {0, 1, 2, 3}
+
+
+def test_fp16_exponent_ceiling(E, orc):
+    """FP16 exponents stop at 31: a base of 31 with width 1 decodes a 32
+    wherever the code is 1, which the check reports for that block (and a
+    base above 31 with width 0 on its own)."""
+    x = values(64 * 512, 2, 77)
+    s = orc.encode(x, 512, dtype=2)
+    meta = int.from_bytes(bytes(s[56:64]), "little")
+    nb = int.from_bytes(bytes(s[32:40]), "little")
+    widths = s[meta + 1: meta + 2 * nb: 2]
+    i = int(np.flatnonzero(widths >= 1)[5])
+    b = s.copy(); b[meta + 2 * i] = 31
+    want = orc.validate(b)
+    assert want == (3, i)
+    d = dev8(b)
+    chk = E.enc_validate(d, E.enc_read_info(d))
+    assert (chk.kind, chk.index) == want
+    # width-0 blocks (one exponent everywhere): a base above 31 fails alone
+    c = orc.encode(np.full(16 * 512, 0x3C00, np.uint16), 512, dtype=2)
+    assert c[8] == 0
+    meta_c = int.from_bytes(bytes(c[56:64]), "little")
+    b = c.copy(); b[meta_c] = 31
+    assert orc.validate(b) == (0, 0)
+    b[meta_c + 2 * 3] = 40
+    want = orc.validate(b)
+    assert want == (3, 3)
+    d = dev8(b)
+    chk = E.enc_validate(d, E.enc_read_info(d))
+    assert (chk.kind, chk.index) == want
