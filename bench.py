@@ -46,6 +46,10 @@ def parse():
                    help="decoder layers in the set (32 = the full 8B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-wide", action="store_true",
+                   help="skip the FP16 / FP32 measurement")
+    p.add_argument("--wide-layers", type=int, default=4,
+                   help="layers of the set measured as FP16 and FP32")
     p.add_argument("--no-pow2", action="store_true",
                    help="skip the power-of-two-width variant of the decode step")
     p.add_argument("--cpu-sample-tensors", type=int, default=21,
@@ -275,6 +279,9 @@ def main():
     if pow2 is not None:
         result["pow2_widths"] = pow2
 
+    if not args.no_wide:
+        result["wide_types"] = bench_wide(enc, synth, torch, np, dev, stream, args)
+
     if not args.no_gemm:
         result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream)
         result["fused_gemm_nt"] = bench_gemm_nt(enc, synth, torch, np, dev)
@@ -283,6 +290,74 @@ def main():
         result["cpu_baseline"] = cpu_baseline(synth, np, torch, dev, args.cpu_sample_tensors, B)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_wide(enc, synth, torch, np, dev, stream, args):
+    """The same code on FP16 and FP32 weights (header dtype 2 and 3): the
+    tensors of the set's first layers generated in that type, compressed on
+    the GPU, then decoded with one enc_decompress launch per tensor per step
+    (the batched decode takes BF16 streams only). Bit-exactness is checked
+    after the timing."""
+    shapes = synth.set8b_shapes()
+    keep = ["L%d." % l for l in range(args.wide_layers)]
+    idx = [i for i, (nm, _, _) in enumerate(shapes) if any(nm.startswith(k) for k in keep)]
+    res = {"workload": "set8b layers 0..%d (%d tensors), same value recipe"
+                       % (args.wide_layers - 1, len(idx))}
+    B = args.block_size
+    for dt, name in ((2, "fp16"), (3, "fp32")):
+        esize = 2 if dt == 2 else 4
+        streams, n_total, comp_total, read, enc_ms = [], 0, 0, 0, 0.0
+        S = 11 if dt == 2 else 24
+        for i in idx:
+            x = synth.set8b_tensor_gpu_dt(i, dt, device=dev).reshape(-1)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            comp, info = enc.enc_compress(x, B, dtype=dt)
+            torch.cuda.synchronize()
+            enc_ms += (time.perf_counter() - t0) * 1e3
+            streams.append((comp.clone(), info))
+            n_total += info.n_elems
+            comp_total += info.total_bytes
+            read += (esize * info.n_elems if info.flags == 1 else
+                     (S * info.n_elems + 7) // 8 + 2 * info.n_blocks + 8 * info.n_segments
+                     + info.payload_bytes)
+            del x, comp
+        outs = [torch.empty(inf.n_elems, dtype=torch.int16 if dt == 2 else torch.int32,
+                            device=dev) for _, inf in streams]
+
+        def step():
+            for (c, inf), o in zip(streams, outs):
+                enc.enc_decompress(c, inf, out=o)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        for k, i in enumerate(idx):
+            x = synth.set8b_tensor_gpu_dt(i, dt, device=dev).reshape(-1)
+            if not torch.equal(outs[k], x):
+                log("MISMATCH in %s tensor %s" % (name, shapes[i][0]))
+                sys.exit(1)
+            del x
+        out_bytes = esize * n_total
+        res[name] = {
+            "elements": n_total,
+            "compression_ratio": round(out_bytes / comp_total, 5),
+            "encode_gbs": round((out_bytes + comp_total) / (enc_ms * 1e-3) / 1e9, 1),
+            "decode_ms_per_step": round(ms, 4),
+            "out_gbs": round(out_bytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_gbs": round((read + out_bytes) / (ms * 1e-3) / 1e9, 1),
+        }
+        log("%s: ratio %.4f, encode %.1f ms, decode %.3f ms/step (%.1f GB/s HBM), bit-exact"
+            % (name, res[name]["compression_ratio"], enc_ms, ms, res[name]["hbm_gbs"]))
+        del streams, outs
+        torch.cuda.empty_cache()
+    return res
 
 
 def _graph_time_us(fn, torch, calls=8, replays=20):

@@ -181,3 +181,26 @@ def set8b_tensor_gpu(index, device="cuda"):
     out = f.to(torch.bfloat16).view(torch.int16)
     del f
     return out
+
+
+def set8b_tensor_gpu_dt(index, dtype, device="cuda"):
+    """Tensor ``index`` of the 8B-shaped set in another element type, generated
+    on the GPU like set8b_tensor_gpu: dtype 2 = FP16 (int16 bits), 3 = FP32
+    (int32 bits)."""
+    import torch
+    name, r, c = set8b_shapes()[index]
+    sigma = float(set8b_sigmas()[index])
+    g = torch.Generator(device=device)
+    g.manual_seed((SEED_TAG << 32) | ((16 + dtype) << 24) | index)
+    f = torch.randn((r, c), generator=g, device=device, dtype=torch.float32)
+    f.mul_(sigma)
+    mask = torch.rand((r, c), generator=g, device=device, dtype=torch.float32) < OUTLIER_P
+    f[mask] *= OUTLIER_SCALE
+    del mask
+    if dtype == 2:
+        out = f.to(torch.float16).view(torch.int16)
+        del f
+        return out
+    if dtype == 3:
+        return f.view(torch.int32)
+    raise ValueError(dtype)
