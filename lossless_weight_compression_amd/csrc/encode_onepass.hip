@@ -28,8 +28,10 @@
 // Per group the work is byte-parallel, as in the decoder: v_perm splits the
 // exponent and sign+mantissa bytes of 4 values at once, min/max use packed
 // 16-bit integer ops, and 4 codes pack with one bit-field extract each.
-// Then wave 0 publishes the workgroup's payload total, looks back for its
-// offset, publishes the prefix, stores the offsets of the segments that
+// Once the last sub-tile's block sizes are known, wave 0 publishes the
+// workgroup's payload total and reads the first look-back window, and that
+// read is in flight while the last sub-tile is packed. Then wave 0 finishes
+// the look-back for the workgroup's offset, publishes the prefix, stores the offsets of the segments that
 // start in this tile (and, in the last tile, the stream's payload size), and
 // the LDS image goes out with 16-byte stores.
 // Status words hold flag and value together and are read and written with
@@ -70,21 +72,26 @@ __device__ __forceinline__ void publish(uint64_t *status, uint64_t tile, uint64_
   __hip_atomic_store(status + tile, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Lane l's status word of the window whose top is tile `top` (positions
+// below tile 0 read as a full prefix of 0).
+__device__ __forceinline__ uint64_t window_word(const uint64_t *status, int64_t top, uint32_t lane) {
+  const int64_t idx = top - (int64_t)lane;
+  return idx >= 0 ? __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : kFlagPre;
+}
+
 // Sum of the payload totals of tiles [0, tile), by the whole wave. Lane l
 // reads tile top - l; the window is usable once every tile from the top down
-// to the nearest full prefix has published (a position below tile 0 counts
-// as a full prefix of 0); otherwise the wave sleeps briefly and reads it
-// again.
+// to the nearest full prefix has published; otherwise the wave sleeps
+// briefly and reads it again. `first` is the caller's read of the first
+// window (top = tile - 1), issued early so that its latency overlaps work.
 __device__ uint64_t look_back(uint64_t *status, uint64_t tile, uint32_t lane, uint32_t *error,
-                              uint32_t spin_limit) {
+                              uint32_t spin_limit, uint64_t first) {
   uint64_t excl = 0;
   int64_t top = (int64_t)tile - 1;
   uint32_t spins = 0;
+  uint64_t v = first;
   while (top >= 0) {
-    const int64_t idx = top - (int64_t)lane;
-    uint64_t v = kFlagPre;
-    if (idx >= 0)
-      v = __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t flag = v >> 62;
     const uint64_t pre = __ballot(flag == 2);
     const uint64_t none = __ballot(flag == 0);
@@ -95,11 +102,13 @@ __device__ uint64_t look_back(uint64_t *status, uint64_t tile, uint32_t lane, ui
         return 0;
       }
       __builtin_amdgcn_s_sleep(1);
+      v = window_word(status, top, lane);
       continue;
     }
     excl += wave_sum64(((need >> lane) & 1) ? (v & kValMask) : 0);
     if (pre) break;
     top -= 64;
+    v = window_word(status, top, lane);
   }
   return excl;
 }
@@ -221,6 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
   if (tid == 0) s_run = 0;
   for (uint32_t i = tid; i < kPayBytes / 4; i += kThreads) pay[i] = 0;
 
+  uint64_t lb_first = kFlagPre;   // wave 0: first look-back window, read early
   uint4 g[kGroupsPerThread], gn[kGroupsPerThread];
   uint32_t valid[kGroupsPerThread], vn[kGroupsPerThread];
   load_sub(in_rs, left, 0, tid, x_last, g, valid);
@@ -280,6 +290,13 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
         s_suboff[sub] = run;
         s_run = run + sub_total;
       }
+      if (sub + 1 == nsub) {
+        // the workgroup's payload total is known: publish it and read the
+        // first look-back window now, so that the read is in flight while
+        // the last sub-tile is packed
+        if (lane == 0) publish(a.status, tile, (tile == 0 ? kFlagPre : kFlagAgg) | (run + sub_total));
+        lb_first = window_word(a.status, (int64_t)tile - 1, lane);
+      }
     }
     lds_barrier();
 
@@ -327,8 +344,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
   // the workgroup's payload offset
   if (wave == 0) {
     const uint32_t agg = s_run;
-    if (lane == 0) publish(a.status, tile, (tile == 0 ? kFlagPre : kFlagAgg) | agg);
-    const uint64_t excl = look_back(a.status, tile, lane, a.error, a.spin_limit);
+    const uint64_t excl = look_back(a.status, tile, lane, a.error, a.spin_limit, lb_first);
     if (lane == 0) {
       if (tile > 0) publish(a.status, tile, kFlagPre | (excl + agg));
       if (tile + 1 == a.ntiles) *a.ws_total = excl + agg;
