@@ -204,3 +204,22 @@ def set8b_tensor_gpu_dt(index, dtype, device="cuda"):
     if dtype == 3:
         return f.view(torch.int32)
     raise ValueError(dtype)
+
+
+def gaussian_bits_gpu(n, sigma, seed, device="cuda", chunk=1 << 28):
+    """n BF16 values N(0, sigma) with the usual outliers, generated on the GPU
+    in chunks (for sizes the host generator would take minutes over);
+    returned as a flat int16 tensor of bits."""
+    import torch
+    out = torch.empty(n, dtype=torch.int16, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed((SEED_TAG << 32) | (3 << 24) | seed)
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        f = torch.randn(m, generator=g, device=device, dtype=torch.float32)
+        f.mul_(sigma)
+        mask = torch.rand(m, generator=g, device=device, dtype=torch.float32) < OUTLIER_P
+        f[mask] *= OUTLIER_SCALE
+        out[s:s + m] = f.to(torch.bfloat16).view(torch.int16)
+        del f, mask
+    return out
