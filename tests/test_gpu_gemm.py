@@ -68,7 +68,7 @@ def compress_oracle(orc, W, B):
     return comp, None
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 15, 16, 17, 40, 128, 129])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 15, 16, 17, 40, 65, 128, 129, 200])
 def test_one_hot_rows_exact(E, orc, M):
     K, N = 256, 1024
     W = synth.gaussian_bits((K, N), 0.02, 200, M)
@@ -86,7 +86,7 @@ def test_one_hot_rows_exact(E, orc, M):
 
 
 @pytest.mark.parametrize("B", [128, 256, 512, 1024, 4096])
-@pytest.mark.parametrize("M", [1, 4, 5, 16, 33])
+@pytest.mark.parametrize("M", [1, 4, 5, 16, 33, 130])
 def test_block_sizes_small(E, orc, B, M):
     K, N = 520, 4096                                  # K not a multiple of the K ranges
     W = synth.gaussian_bits((K, N), 0.02, 201, B)
