@@ -22,7 +22,8 @@
 //    turn into fp32 with v_perm; M x 8 fp32 FMAs per row.
 //  * k_gemm_mfmau (larger M, B >= 512, or dense W): wave-uniform rows are
 //    decoded into k-pair dwords in an LDS tile, B fragments of
-//    v_mfma_f32_16x16x32_bf16 are read from it, A fragments are X rows.
+//    v_mfma_f32_16x16x32_bf16 are read from it, A fragments from the step's
+//    X slice, staged in LDS once per workgroup.
 //  * k_gemm_valu / k_gemm_mfma: the same two schemes for B < 512, where a
 //    512-column run spans several blocks and each lane finds its own block.
 //  * split K: workgroups over K ranges write fp32 partial slices, and
@@ -594,25 +595,29 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// M tile of k_gemm_mfmau. Up to 64 rows every wave loads its A fragments
-// from X itself; the 128-row tile stages each step's X slice in LDS instead
-// (its 32 accumulator tiles per wave leave no registers for per-wave copies),
-// so W is decoded once for M up to 128.
+// M tile of k_gemm_mfmau; larger M runs several 128-row tiles.
 uint32_t mfmau_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 constexpr uint32_t kXsPitch = 40;   // bf16 per LDS row of the staged X slice (32 + 8)
 
+// Each K step, the workgroup's threads load the step's X slice (MT rows x 32
+// k, one 16-byte piece per thread) and store it in LDS next to the decoded W
+// rows; every wave then reads its A fragments there. Compared with each wave
+// loading its own A fragments from X, this keeps the accumulators and the
+// two-step ring within 128 registers at 16 waves for every M tile, so W is
+// decoded once for M up to 128 (measured on a 4096 x 14336 W: M = 32 38.7 ->
+// 34.1 us, M = 64 50.5 -> 39.7, M = 128 57.8 -> 52.7).
 template <int MT, int WAVES, bool DENSE, int NB>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   constexpr uint32_t RPW = 32 / WAVES;          // rows decoded per wave per step
   constexpr uint32_t NSUB = 32 / WAVES;         // 16-column subtiles per wave
   constexpr uint32_t MSUB = MT / 16;
   constexpr uint32_t NTHR = WAVES * 64;
-  constexpr bool XLDS = MT >= 128;              // X slice staged in LDS
+  constexpr uint32_t XP = MT * 4;               // 16-byte pieces of a step's X slice
   static_assert(RPW % 2 == 0, "rows are decoded in pairs");
-  static_assert(!XLDS || MT * 4 == NTHR, "one 16-byte X piece per thread");
+  static_assert(XP <= NTHR, "at most one X piece per thread");
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][16 * kPitchU];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[XLDS ? 2 : 1][XLDS ? MT * kXsPitch : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * kXsPitch];
   __shared__ uint32_t tbl_off[1024], tbl_meta[1024];
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
     u32x2 sm[RPW];
     u32x3 q[RPW];
     uint4 dv[RPW];
-    uint4 x[XLDS ? 1 : MSUB];   // XLDS: this thread's piece of the X slice
+    uint4 x;                    // this thread's piece of the X slice
   };
   // Every load is issued unconditionally, from a clamped (always valid) row
   // or X element; out-of-range data is discarded after the load. Loads under
@@ -668,24 +673,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
         S.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
       }
     }
-    if (XLDS) {
-      // row tid / 4, k = kb + 8 (tid % 4) .. + 7
-      const uint32_t m = m0 + (tid >> 2), kx = kb + 8 * (tid & 3);
-      const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K +
-                                                       min(kx, k1 - 8));
-      const bool in = m < M && kx < k1;
-      S.x[0] = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
-    } else {
-      const uint32_t kx = kb + 8 * (lane >> 4);
-#pragma unroll
-      for (uint32_t mi = 0; mi < MSUB; ++mi) {
-        const uint32_t m = m0 + 16 * mi + (lane & 15);
-        const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K +
-                                                         min(kx, k1 - 8));
-        const bool in = m < M && kx < k1;
-        S.x[mi] = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
-      }
-    }
+    // piece p = tid mod XP: row p / 4, k = kb + 8 (p % 4) .. + 7 (threads
+    // past XP load a duplicate and do not store it)
+    const uint32_t p = tid % XP;
+    const uint32_t m = m0 + (p >> 2), kx = kb + 8 * (p & 3);
+    const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K +
+                                                     min(kx, k1 - 8));
+    const bool in = m < M && kx < k1;
+    S.x = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
   };
   auto decode_row = [&](uint32_t st, const Step &S, uint32_t j) -> uint4 {
     const uint32_t kr = k0 + 32 * st + wave * RPW + j;   // uniform
@@ -722,39 +717,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
       *reinterpret_cast<uint4 *>(dst) = lo4;
       *reinterpret_cast<uint4 *>(dst + 4) = hi4;
     }
-    if (XLDS)
-      *reinterpret_cast<uint4 *>(&xs[XLDS ? buf : 0][(tid >> 2) * kXsPitch + 8 * (tid & 3)]) = S.x[0];
+    if (tid < XP) *reinterpret_cast<uint4 *>(&xs[buf][(tid >> 2) * kXsPitch + 8 * (tid & 3)]) = S.x;
   };
   f32x4 acc[MSUB][NSUB];
 #pragma unroll
   for (uint32_t mi = 0; mi < MSUB; ++mi)
 #pragma unroll
     for (uint32_t ns = 0; ns < NSUB; ++ns) acc[mi][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mfma_step = [&](uint32_t buf, const Step &S) {
+  auto mfma_step = [&](uint32_t buf) {
     const uint32_t kq = 4 * (lane >> 4);
-    if (XLDS) {
-      bf16x8 b[NSUB];
-#pragma unroll
-      for (uint32_t ns = 0; ns < NSUB; ++ns) {
-        const uint32_t n = wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
-        uint4 bw;
-        bw.x = tile[buf][(kq + 0) * kPitchU + n];
-        bw.y = tile[buf][(kq + 1) * kPitchU + n];
-        bw.z = tile[buf][(kq + 2) * kPitchU + n];
-        bw.w = tile[buf][(kq + 3) * kPitchU + n];
-        b[ns] = __builtin_bit_cast(bf16x8, bw);
-      }
-#pragma unroll
-      for (uint32_t mi = 0; mi < MSUB; ++mi) {
-        const uint4 av = *reinterpret_cast<const uint4 *>(
-            &xs[XLDS ? buf : 0][(16 * mi + (lane & 15)) * kXsPitch + 8 * (lane >> 4)]);
-        const bf16x8 af = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-        for (uint32_t ns = 0; ns < NSUB; ++ns)
-          acc[mi][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[ns], acc[mi][ns], 0, 0, 0);
-      }
-      return;
-    }
+    bf16x8 b[NSUB];
 #pragma unroll
     for (uint32_t ns = 0; ns < NSUB; ++ns) {
       const uint32_t n = wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
@@ -763,11 +735,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
       bw.y = tile[buf][(kq + 1) * kPitchU + n];
       bw.z = tile[buf][(kq + 2) * kPitchU + n];
       bw.w = tile[buf][(kq + 3) * kPitchU + n];
-      const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+      b[ns] = __builtin_bit_cast(bf16x8, bw);
+    }
 #pragma unroll
-      for (uint32_t mi = 0; mi < MSUB; ++mi)
-        acc[mi][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, S.x[mi]), b,
-                                                               acc[mi][ns], 0, 0, 0);
+    for (uint32_t mi = 0; mi < MSUB; ++mi) {
+      const uint4 av =
+          *reinterpret_cast<const uint4 *>(&xs[buf][(16 * mi + (lane & 15)) * kXsPitch + 8 * (lane >> 4)]);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (uint32_t ns = 0; ns < NSUB; ++ns)
+        acc[mi][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[ns], acc[mi][ns], 0, 0, 0);
     }
   };
 
@@ -785,7 +762,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
       if (st + j < nsteps) {
         decode_step(st + j, S[j], (st + j) & 1);
         lds_barrier();
-        mfma_step((st + j) & 1, S[j]);
+        mfma_step((st + j) & 1);
       }
     }
   }
@@ -831,32 +808,31 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
 
 // Step buffers per M tile size (ring depth of the prefetch). Measured at
 // M = 16 / 32 / 128: two beat three (register pressure).
-constexpr int kNB16 = 2, kNB32 = 2, kNB64 = 2, kNB128 = 2;
-// Waves per workgroup for each M tile, and the resident workgroups the
-// split-K plan fills. More waves per workgroup share one decoded LDS tile
-// and need fewer registers each (2 rows per wave per step at 16 waves), so
-// the same device holds more rows in flight with fewer split-K slices.
-// Measured on a 4096 x 14336 W: 16 waves over 4 took M = 8 from 35.9 to
-// 29.8 us, M = 16 from 36.6 to 31.6, M = 32 from 42.3 to 38.9; at the
-// 64-row tile 16 waves were slower than 8 (M = 128: 91.8 vs 82.4 us).
-constexpr int kW16 = 16;
+constexpr int kMfmauNB = 2;       // K steps in the load ring
+// 16 waves per workgroup for every M tile: more waves share one decoded LDS
+// tile and need fewer registers each (2 rows per wave per step), so the
+// device holds more rows in flight with fewer split-K slices (measured on a
+// 4096 x 14336 W, 16 waves over 4: M = 8 35.9 -> 29.8 us, M = 16 36.6 ->
+// 31.6, M = 32 42.3 -> 38.9; with the X slice in LDS the 64- and 128-row
+// tiles gained from 16 waves over 8 too). The split-K plan fills the
+// resident workgroups: two per CU for the 16-row tile (LDS and registers
+// allow it), one for the others.
+constexpr int kMfmauWaves = 16;
 constexpr uint64_t kSlots16 = 512;
-constexpr int kW32 = 16;
 constexpr uint64_t kSlots32 = 256;
-constexpr int kW64 = 8;
 constexpr uint64_t kSlots64 = 256;
-constexpr int kW128 = 8;
 constexpr uint64_t kSlots128 = 256;
 
 template <bool DENSE>
 hipError_t launch_mfmau(const GemmArgs &a, hipStream_t s) {
+  constexpr int W = kMfmauWaves, NB = kMfmauNB;
   const uint32_t MT = mfmau_tile_m(a.M);
-  const dim3 grid(a.N / kStrip, a.ksplit, (a.M + MT - 1) / MT);
+  const dim3 grid(a.N / kStrip, a.ksplit, (a.M + MT - 1) / MT), block(W * 64);
   switch (MT) {
-    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, kW16, DENSE, kNB16>), grid, dim3(kW16 * 64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, kW32, DENSE, kNB32>), grid, dim3(kW32 * 64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_gemm_mfmau<64, kW64, DENSE, kNB64>), grid, dim3(kW64 * 64), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfmau<128, kW128, DENSE, kNB128>), grid, dim3(kW128 * 64), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, W, DENSE, NB>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, W, DENSE, NB>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_gemm_mfmau<64, W, DENSE, NB>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfmau<128, W, DENSE, NB>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -1063,9 +1039,9 @@ void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t 
   const uint64_t tiles = (uint64_t)(N / ncol) * ((M + MT - 1) / MT);
   uint64_t ks;
   if (kind == 3) {
-    // Resident k_gemm_mfmau workgroups (kSlots*: ~74 KB of LDS allows two
-    // per CU; the 8-wave 64-row variant's registers allow one). Fill the
-    // slots in one round: a partial second round doubles the time.
+    // Resident k_gemm_mfmau workgroups (kSlots*: two per CU for the 16-row
+    // tile, one for the others). Fill the slots in one round: a partial
+    // second round doubles the time.
     const uint64_t slots = MT == 128 ? kSlots128 : MT == 64 ? kSlots64 : (MT == 16 ? kSlots16 : kSlots32);
     ks = tiles >= slots ? 1 : slots / tiles;
   } else {
