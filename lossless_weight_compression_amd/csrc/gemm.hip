@@ -12,10 +12,10 @@
 // blocks of that segment. Every block of W is full (N % B == 0), so a block's
 // payload is w * B / 8 bytes.
 //
-// Small M (below kMfmaMinM = 5) runs on VALU FMAs, larger M on MFMA; above
+// Small M (below kMfmaMinM = 3) runs on VALU FMAs, larger M on MFMA; above
 // that crossover the MFMA kernels' cost hardly depends on M (measured on a
-// 4096 x 14336 W: M = 4 31.5 us on VALU vs 33.1 on MFMA, M = 5 33.7 vs 33.4,
-// M = 15 68.3 vs 36.1).
+// 4096 x 14336 W, GPU time per call: M = 2 27.5 us either way, M = 3 29.2 on
+// VALU vs 27.7 on MFMA, M = 4 31.3 vs 28.0).
 //  * k_gemm_rowu (small M, B >= 512): a wave owns a 512-column strip and 32
 //    rows; every row's width, base and block offset are wave-uniform, so
 //    codes come in with one buffer load per lane and row and the byte planes
@@ -35,8 +35,8 @@
 namespace enc {
 namespace {
 
-constexpr uint32_t kMfmaMinM = 5;              // smallest M routed to the MFMA kernels
-static_assert(kMfmaMinM == 5, "the VALU launchers instantiate M = 1..4");
+constexpr uint32_t kMfmaMinM = 3;              // smallest M routed to the MFMA kernels
+static_assert(kMfmaMinM == 3, "the VALU launchers instantiate M = 1..2");
 constexpr uint32_t kStrip = 512;               // VALU path: columns per workgroup
 constexpr uint32_t kValuRowsPerWave = 64;
 constexpr uint32_t kValuRows = 4 * kValuRowsPerWave;
@@ -787,7 +787,7 @@ hipError_t launch_valu(const GemmArgs &a, hipStream_t s) {
   switch (a.M) {
 #define CASE(m) \
   case m: hipLaunchKernelGGL((k_gemm_valu<m, DENSE>), grid, dim3(256), 0, s, a); break;
-    CASE(1) CASE(2) CASE(3) CASE(4)
+    CASE(1) CASE(2)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
@@ -799,7 +799,7 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
   switch (a.M) {
 #define CASE(m) \
   case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(256), 0, s, a); break;
-    CASE(1) CASE(2) CASE(3) CASE(4)
+    CASE(1) CASE(2)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
