@@ -26,6 +26,10 @@
 //    X slice, staged in LDS once per workgroup.
 //  * k_gemm_valu / k_gemm_mfma: the same two schemes for B < 512, where a
 //    512-column run spans several blocks and each lane finds its own block.
+//  * W stored [N, K] (a linear layer's layout, Y = X W^T): k_gemm_ntu
+//    decodes 128-k runs of TN rows into an LDS tile read as MFMA fragments
+//    (B >= 512, or dense W); k_gemm_nt decodes groups straight into
+//    fragments (any other block size).
 //  * split K: workgroups over K ranges write fp32 partial slices, and
 //    k_splitk_reduce, launched next on the same stream, adds them in K order
 //    (deterministic).
@@ -873,8 +877,9 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {
 // Cost: every wave load instruction touches 16 rows of W (and 16 rows of X),
 // 32 bytes each, so this kernel is bound by cache-line accesses rather than
 // by HBM bytes or load latency (prefetch depth 2, 4 or 8 all measured the
-// same). The [K, N] kernels above read 512 contiguous bytes per row and are
-// faster; a caller that compresses offline can store W^T for them.
+// same). It serves the block sizes below 512; k_gemm_ntu below, which reads
+// 256 contiguous bytes per row, serves the rest (M = 16: 55 -> 28 us on a
+// 14336 x 4096 W).
 // --------------------------------------------------------------------------
 constexpr uint32_t kNtCols = 16;     // columns per wave
 constexpr uint32_t kNtWaves = 4;     // waves per workgroup
@@ -994,6 +999,196 @@ __global__ __launch_bounds__(kNtWaves * 64) void k_gemm_nt(GemmArgs a) {
   });
 }
 
+// --------------------------------------------------------------------------
+// [N, K] layout, B >= 512 (or dense W with K % 128 == 0): staged rows.
+//
+// k_gemm_nt's loads touch 16 rows of W per instruction, 32 bytes each. Here a
+// workgroup (16 waves) owns TN rows of W (output columns) and walks its K
+// range in steps of 128 k: 16 lanes decode 16 consecutive groups of one row
+// (256 contiguous sign+mantissa bytes, one contiguous code run: with B >= 512
+// a 128-k run lies in one block, so its width, base and offset are shared),
+// and store them row-major in an LDS tile, where an MFMA B fragment (8
+// consecutive k of one column) is one 16-byte read. The step's X slice (MT
+// rows x 128 k) is staged next to it. Wave w multiplies n-subtile w mod
+// (TN/16) over its share of the step's four 32-k slices; the waves that share
+// an n-subtile add their accumulators at the end, in wave order
+// (deterministic). Loads run two steps ahead and are issued on every path,
+// as in k_gemm_mfmau.
+// --------------------------------------------------------------------------
+constexpr uint32_t kNtuWaves = 16;
+constexpr uint32_t kNtuStepK = 128;
+constexpr uint32_t kNtuPitch = kNtuStepK + 8;      // bf16 per LDS row (272 bytes)
+constexpr uint32_t kNtuMaxBlocks = 8;              // blocks per row and K range, at most
+
+template <int MT, int TN, bool DENSE>
+__global__ __launch_bounds__(kNtuWaves * 64) void k_gemm_ntu(GemmArgs a) {
+  constexpr uint32_t NTHR = kNtuWaves * 64;
+  constexpr uint32_t MSUB = MT / 16;
+  constexpr uint32_t NSUBT = TN / 16;                      // n-subtiles of the tile
+  constexpr uint32_t KG = kNtuWaves / NSUBT;               // waves sharing an n-subtile
+  constexpr uint32_t KPW = 4 / KG;                         // 32-k slices per wave per step
+  constexpr uint32_t GPT = TN * 16 / NTHR;                 // W groups per thread per step
+  constexpr uint32_t XP = MT * 16;                         // 16-byte X pieces per step
+  constexpr uint32_t XPT = (XP + NTHR - 1) / NTHR;         // X pieces per thread
+  constexpr uint32_t NB = 2;
+  static_assert(GPT >= 1 && KPW >= 1 && KG * KPW == 4, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][TN * kNtuPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * kNtuPitch];
+  __shared__ uint32_t tbl_off[DENSE ? 1 : TN * kNtuMaxBlocks], tbl_meta[DENSE ? 1 : TN * kNtuMaxBlocks];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t K = a.K, N = a.N, M = a.M, log2b = a.log2b;
+  const uint32_t n0 = blockIdx.x * TN, m0 = blockIdx.z * MT;
+  const uint32_t k0 = blockIdx.y * a.krows;
+  const uint32_t k1 = min(k0 + a.krows, K);
+  const uint32_t nsteps = (k1 - k0) / kNtuStepK;
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
+
+  if (!DENSE) {
+    const uint32_t jb = (k1 - k0) >> log2b;                // blocks per row in the range
+    for (uint32_t i = tid; i < TN * jb; i += NTHR) {
+      const uint32_t r = i / jb, j = i % jb;
+      uint64_t off, mw;
+      row_block<false>(a, ((uint64_t)(n0 + r) * K + k0 + (j << log2b)) >> log2b, off, mw);
+      uint32_t w = (uint32_t)(mw >> 8) & 0xFFu;
+      if (w > 8) w = 0;   // corrupted stream: decode as width 0 (reads stay range-checked)
+      tbl_off[r * kNtuMaxBlocks + j] = (uint32_t)off;
+      tbl_meta[r * kNtuMaxBlocks + j] = ((uint32_t)mw & 0xFFu) | (w << 8);
+    }
+    __syncthreads();
+  }
+
+  struct Step {
+    u32x2 sm[GPT];
+    u32x3 q[GPT];
+    uint4 dv[GPT];
+    uint4 x[XPT];
+  };
+  // group q of the step: row q / 16, k = kb + 8 (q % 16)
+  auto load_step = [&](uint32_t st, Step &S) {
+    const uint32_t dead = st < nsteps ? 0u : 0x80000000u;
+    const uint32_t kb = k0 + kNtuStepK * min(st, nsteps - 1);
+#pragma unroll
+    for (uint32_t h = 0; h < GPT; ++h) {
+      const uint32_t q = tid + NTHR * h;
+      const uint32_t r = q >> 4, k = kb + 8 * (q & 15);
+      if (DENSE) {
+        S.dv[h] = *reinterpret_cast<const uint4 *>(a.wdense + (uint64_t)(n0 + r) * K + k);
+      } else {
+        const uint32_t j = (k - k0) >> log2b;
+        const uint32_t off = tbl_off[r * kNtuMaxBlocks + j];
+        const uint32_t meta = tbl_meta[r * kNtuMaxBlocks + j];
+        const uint32_t w = meta >> 8;
+        const uint32_t pb = off + ((k & ((1u << log2b) - 1)) >> 3) * w;
+        S.sm[h] = __builtin_amdgcn_raw_buffer_load_b64(rs, (kHeaderBytes + (n0 + r) * K + k) | dead, 0, 0);
+        S.q[h] = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
+      }
+    }
+#pragma unroll
+    for (uint32_t h = 0; h < XPT; ++h) {
+      // X piece p: row p / 16, k = kb + 8 (p % 16); threads past XP load a
+      // duplicate and do not store it
+      const uint32_t p = (tid + NTHR * h) % XP;
+      const uint32_t m = m0 + (p >> 4), kx = kb + 8 * (p & 15);
+      const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K + kx);
+      const bool in = m < M;
+      S.x[h] = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
+    }
+  };
+  auto decode_step = [&](uint32_t st, const Step &S, uint32_t buf) {
+    const uint32_t kb = k0 + kNtuStepK * st;
+#pragma unroll
+    for (uint32_t h = 0; h < GPT; ++h) {
+      const uint32_t q = tid + NTHR * h;
+      const uint32_t r = q >> 4, g = q & 15;
+      uint4 v;
+      if (DENSE) {
+        v = S.dv[h];
+      } else {
+        const uint32_t k = kb + 8 * g;
+        const uint32_t j = (k - k0) >> log2b;
+        const uint32_t off = tbl_off[r * kNtuMaxBlocks + j];
+        const uint32_t meta = tbl_meta[r * kNtuMaxBlocks + j];
+        const uint32_t w = (meta >> 8) & 15u;
+        const uint32_t sh = ((off + ((k & ((1u << log2b) - 1)) >> 3) * w) & 3u) * 8;
+        const uint32_t lo = __builtin_amdgcn_alignbit(S.q[h].y, S.q[h].x, sh);
+        const uint32_t hi = __builtin_amdgcn_alignbit(S.q[h].z, S.q[h].y, sh);
+        v = join_group(lo, hi, w, (meta & 0xFFu) * 0x01010101u, S.sm[h].x, S.sm[h].y);
+      }
+      *reinterpret_cast<uint4 *>(&wt[buf][r * kNtuPitch + 8 * g]) = v;
+    }
+#pragma unroll
+    for (uint32_t h = 0; h < XPT; ++h) {
+      const uint32_t p = tid + NTHR * h;
+      if (p < XP) *reinterpret_cast<uint4 *>(&xs[buf][(p >> 4) * kNtuPitch + 8 * (p & 15)]) = S.x[h];
+    }
+  };
+
+  const uint32_t ns = wave % NSUBT, kg = wave / NSUBT;
+  f32x4 acc[MSUB];
+#pragma unroll
+  for (uint32_t mi = 0; mi < MSUB; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mfma_step = [&](uint32_t buf) {
+#pragma unroll
+    for (uint32_t t = 0; t < KPW; ++t) {
+      const uint32_t kk = 32 * (kg * KPW + t) + 8 * (lane >> 4);
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4 *>(&wt[buf][(16 * ns + (lane & 15)) * kNtuPitch + kk]));
+#pragma unroll
+      for (uint32_t mi = 0; mi < MSUB; ++mi) {
+        const bf16x8 af = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(&xs[buf][(16 * mi + (lane & 15)) * kNtuPitch + kk]));
+        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b, acc[mi], 0, 0, 0);
+      }
+    }
+  };
+
+  Step S[NB];
+  load_step(0, S[0]);
+  for (uint32_t st = 0; st < nsteps; st += NB) {
+#pragma unroll
+    for (uint32_t j = 0; j < NB; ++j) {
+      load_step(st + j + 1, S[(j + 1) % NB]);
+      if (st + j < nsteps) {
+        decode_step(st + j, S[j], (st + j) & 1);
+        lds_barrier();
+        mfma_step((st + j) & 1);
+      }
+    }
+  }
+
+  // waves kg = 1 .. KG-1 hand their sums to wave kg = 0 of the same
+  // n-subtile, one at a time, through the (now free) W tile
+  float *red = reinterpret_cast<float *>(&wt[0][0]);
+  static_assert(NSUBT * 64 * MSUB * 4 * 4 <= sizeof(wt), "reduction buffer");
+#pragma unroll 1
+  for (uint32_t r = 1; r < KG; ++r) {
+    __syncthreads();
+    if (kg == r) {
+#pragma unroll
+      for (uint32_t mi = 0; mi < MSUB; ++mi)
+        *reinterpret_cast<f32x4 *>(&red[((ns * MSUB + mi) * 64 + lane) * 4]) = acc[mi];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (uint32_t mi = 0; mi < MSUB; ++mi)
+        acc[mi] += *reinterpret_cast<const f32x4 *>(&red[((ns * MSUB + mi) * 64 + lane) * 4]);
+    }
+  }
+  if (kg != 0) return;
+  splitk_finish(a, blockIdx.y, [&](auto fn) {
+#pragma unroll
+    for (uint32_t mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t m = m0 + 16 * mi + 4 * (lane >> 4) + j;
+        const uint32_t n = n0 + 16 * ns + (lane & 15);
+        fn(m < M ? (int64_t)m * N + n : (int64_t)-1, acc[mi][j]);
+      }
+  });
+}
+
 template <bool DENSE>
 hipError_t launch_nt(const GemmArgs &a, hipStream_t s, uint32_t msub) {
   const uint32_t mt = 16 * msub;
@@ -1009,6 +1204,48 @@ hipError_t launch_nt(const GemmArgs &a, hipStream_t s, uint32_t msub) {
 
 // M tile of k_gemm_nt in 16-row units (MSUB).
 uint32_t nt_msub(uint32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+
+// k_gemm_ntu serves a call when its 128-k steps and blocks line up: coded W
+// with B >= 512 (K % B == 0 is checked by the caller), or dense W with
+// K % 128 == 0. TN = 128 rows of W per workgroup when N allows, else 64.
+constexpr uint32_t kNtuTN = 128;
+bool ntu_ok(bool dense, uint32_t K, uint32_t log2b) { return dense ? K % kNtuStepK == 0 : log2b >= 9; }
+uint32_t ntu_tn(uint32_t N) { return N % kNtuTN == 0 ? kNtuTN : 64; }
+
+template <bool DENSE, int TN>
+hipError_t launch_ntu_tn(const GemmArgs &a, hipStream_t s) {
+  const uint32_t MT = mfmau_tile_m(a.M);
+  const dim3 grid(a.N / TN, a.ksplit, (a.M + MT - 1) / MT), block(kNtuWaves * 64);
+  switch (MT) {
+    case 16: hipLaunchKernelGGL((k_gemm_ntu<16, TN, DENSE>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_ntu<32, TN, DENSE>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_gemm_ntu<64, TN, DENSE>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_ntu<128, TN, DENSE>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool DENSE>
+hipError_t launch_ntu(const GemmArgs &a, hipStream_t s) {
+  return ntu_tn(a.N) == 128 ? launch_ntu_tn<DENSE, 128>(a, s) : launch_ntu_tn<DENSE, 64>(a, s);
+}
+
+// k_gemm_ntu plan: one workgroup per CU (16 waves, up to 144 KB of LDS);
+// K ranges of whole 128-k steps and whole blocks, at most kNtuMaxBlocks
+// blocks per row, as many as it takes to fill the CUs.
+void gemm_ntu_plan(bool dense, uint32_t M, uint32_t K, uint32_t N, uint32_t log2b, uint32_t *ksplit,
+                   uint32_t *krows) {
+  const uint32_t MT = mfmau_tile_m(M);
+  const uint64_t tiles = (uint64_t)(N / ntu_tn(N)) * ((M + MT - 1) / MT);
+  const uint64_t slots = 256;
+  uint64_t ks = tiles >= slots ? 1 : slots / tiles;
+  const uint32_t align = dense ? kNtuStepK : (1u << log2b);
+  uint32_t rows = (uint32_t)((K + ks - 1) / ks);
+  rows = (rows + align - 1) / align * align;
+  if (!dense && rows > kNtuMaxBlocks * align) rows = kNtuMaxBlocks * align;
+  *krows = rows;
+  *ksplit = (K + rows - 1) / rows;
+}
 
 }  // namespace
 
@@ -1093,10 +1330,23 @@ void gemm_nt_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t log2b, uint32_t *
 }
 
 uint64_t gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t log2b) {
+  // the split-K slices of whichever kernel and plan a call with this block
+  // size can select (coded, or a RAW stream / dense W multiplied directly)
+  uint64_t most = 256;
   uint32_t ks, kr;
-  gemm_nt_plan(M, K, N, log2b, &ks, &kr);
-  const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
-  return partial > 256 ? partial : 256;
+  for (int v = 0; v < 4; ++v) {
+    const bool dense = v & 1;
+    const uint32_t lb = dense ? 9u : log2b;
+    if (v < 2)
+      gemm_nt_plan(M, K, N, lb, &ks, &kr);
+    else if (ntu_ok(dense, K, lb))
+      gemm_ntu_plan(dense, M, K, N, lb, &ks, &kr);
+    else
+      continue;
+    const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
+    if (partial > most) most = partial;
+  }
+  return most;
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs &a, hipStream_t s) {
@@ -1118,8 +1368,14 @@ hipError_t launch_splitk_reduce(const GemmArgs &a, hipStream_t s) {
 hipError_t launch_gemm_nt(const GemmArgs &a_in, hipStream_t s) {
   GemmArgs a = a_in;
   const bool dense = a.wstream == nullptr;
-  gemm_nt_plan(a.M, a.K, a.N, a.log2b, &a.ksplit, &a.krows);
-  const hipError_t e = dense ? launch_nt<true>(a, s, nt_msub(a.M)) : launch_nt<false>(a, s, nt_msub(a.M));
+  hipError_t e;
+  if (ntu_ok(dense, a.K, a.log2b)) {
+    gemm_ntu_plan(dense, a.M, a.K, a.N, a.log2b, &a.ksplit, &a.krows);
+    e = dense ? launch_ntu<true>(a, s) : launch_ntu<false>(a, s);
+  } else {
+    gemm_nt_plan(a.M, a.K, a.N, a.log2b, &a.ksplit, &a.krows);
+    e = dense ? launch_nt<true>(a, s, nt_msub(a.M)) : launch_nt<false>(a, s, nt_msub(a.M));
+  }
   if (e != hipSuccess || a.ksplit == 1) return e;
   return launch_splitk_reduce(a, s);
 }
