@@ -180,3 +180,16 @@ def test_graph_replay(E):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, ref), rep
+
+
+@pytest.mark.parametrize("K", [160, 384, 2080])
+@pytest.mark.parametrize("M", [1, 16, 70])
+def test_dense_k_steps(E, orc, K, M):
+    """The uncompressed [N, K] GEMM for K a multiple of 128 (staged-row
+    kernel) and not (fragment kernel)."""
+    N = 128
+    W = synth.gaussian_bits((N, K), 0.02, 216, K)
+    X = synth.gemm_activations(M, K)
+    Y, A = oracle_nt(orc, X, W)
+    say("nt dense K=%d M=%d" % (K, M))
+    assert_within(run_dense(E, X, W), Y, A, "dense K=%d M=%d" % (K, M))
