@@ -132,3 +132,34 @@ def test_pow2_stream_width_check(E, orc):
         chk = E.enc_validate(d, E.enc_read_info(d))
         assert (chk.kind, chk.index) == orc.validate(stream)
     assert orc.validate(b)[0] == 1
+
+
+@pytest.mark.parametrize("B", [128, 512])
+def test_corruptions_linear_layout_gemm(E, orc, B):
+    """The [N, K]-layout GEMM runs to completion on every damaged stream (its
+    reads stay inside the stream by construction) and, where the check
+    accepts the stream, multiplies exactly the oracle-decoded W."""
+    N, K = 256, 4096
+    w = synth.gaussian_bits((N, K), 0.02, 95, B)
+    s = orc.encode(w.reshape(-1), B)
+    assert s[8] == 0
+    X = dev16(synth.gemm_activations(16, K)).reshape(16, K)
+    one_hot = np.zeros((1, K), np.uint16)
+    one_hot[0, 1234] = 0x3F80
+    X1 = dev16(one_hot).reshape(1, K)
+    ws = E.gemm_nt_workspace(16, K, N, B)
+    for seed, kind in enumerate(corruptions.KINDS):
+        b = corruptions.corrupt(s, kind, 8100 + 10 * B + seed)
+        want = orc.validate(b)
+        say("nt corruption", kind, "seed", seed, "B=%d" % B, "oracle says", want)
+        d = dev8(b)
+        info = E.enc_read_info(d)
+        E.enc_decompress_gemm_nt(X, d, info, N, ws=ws)
+        y1 = E.enc_decompress_gemm_nt(X1, d, info, N, ws=ws)
+        torch.cuda.synchronize()
+        if want[0] == 0:
+            wd = orc.decode(b).reshape(N, K)
+            if ((wd >> 7) & 0xFF == 0xFF).any():
+                continue   # a damaged payload made an Inf or NaN: 0 x Inf is NaN
+            col = wd[:, 1234].astype(np.uint32) << 16
+            assert np.array_equal(y1.cpu().numpy()[0], col.view(np.float32)), (kind, seed)
