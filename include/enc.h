@@ -48,8 +48,8 @@
  *   exponent field (<= 255, or <= 31 for FP16; always true for a stream
  *   written by these rules).
  *   FP16 and FP32 streams (the same code applied to the other float layouts)
- *   are written by enc_compress_dt and read by enc_decompress, enc_read_info,
- *   enc_parse_header and enc_validate; the batched decode and the GEMMs take
+ *   are written by enc_compress_dt and read by enc_decompress, the batched
+ *   decode, enc_read_info, enc_parse_header and enc_validate; the GEMMs take
  *   BF16 streams only (ENC_ERR_UNSUPPORTED otherwise).
  *
  * Conventions for every entry point:
@@ -165,8 +165,8 @@ enc_status enc_decompress(const void *d_comp, const enc_info *h_info, void *d_ou
  * set decoded per step, as single-stream inference streams every weight
  * once per token -- MINE Abstract). */
 typedef struct enc_item {
-  const void *d_comp; /* device stream (BF16) */
-  uint16_t *d_out;    /* device output, info.n_elems values */
+  const void *d_comp; /* device stream (any dtype; items may mix them) */
+  void *d_out;        /* device output, info.n_elems values of the stream's dtype */
   enc_info info;      /* parsed header of d_comp */
 } enc_item;
 

@@ -330,7 +330,7 @@ enc_status compress_wide(const void *d_in, uint64_t n, uint32_t dtype, uint32_t 
 
 uint64_t batch_bytes(int count) {
   return align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
-                      8 * ((uint64_t)count + 1),
+                      2 * 8 * ((uint64_t)count + 1),
                   256);
 }
 
@@ -571,7 +571,8 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
   DecodeDesc *descs = reinterpret_cast<DecodeDesc *>(host.data() + sizeof(BatchHeader));
   uint64_t *tiles = reinterpret_cast<uint64_t *>(host.data() + sizeof(BatchHeader) +
                                                  (uint64_t)count * sizeof(DecodeDesc));
-  uint64_t t = 0;
+  uint64_t *wide = tiles + count + 1;   // the FP16 / FP32 items' tile list
+  uint64_t t = 0, tw = 0;
   for (int k = 0; k < count; ++k) {
     const enc_item &it = h_items[k];
     const enc_status st = check_info(&it.info);
@@ -580,18 +581,19 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
       memcpy(why, g_err, sizeof why);
       return fail(st, "item %d: %s", k, why);
     }
-    if (it.info.dtype != 1)
-      return fail(ENC_ERR_UNSUPPORTED, "item %d: the batched decode takes BF16 streams only", k);
     if (!it.d_comp || (it.info.n_elems && !it.d_out))
       return fail(ENC_ERR_INVALID_ARG, "item %d: NULL pointer", k);
     if (!aligned16(it.d_comp) || !aligned16(it.d_out))
       return fail(ENC_ERR_INVALID_ARG, "item %d: unaligned pointer", k);
     descs[k] = desc_of(it.d_comp, it.info, it.d_out);
     tiles[k] = t;
-    t += tiles_for(it.info.n_elems);
+    wide[k] = tw;
+    (it.info.dtype == 1 ? t : tw) += tiles_for(it.info.n_elems);
   }
   tiles[count] = t;
+  wide[count] = tw;
   hdr.total_tiles = t;
+  hdr.wide_tiles = tw;
   memcpy(host.data(), &hdr, sizeof hdr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(d_table, host.data(), need, hipMemcpyHostToDevice, s);

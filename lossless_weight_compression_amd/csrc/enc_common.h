@@ -60,13 +60,16 @@ struct DecodeDesc {
 };
 static_assert(sizeof(DecodeDesc) == 80, "table entry layout");
 
-// Batch table in device memory: header, then `count` DecodeDesc, then
-// `count + 1` u64 tile prefixes (first tile of each item, then the total).
+// Batch table in device memory: header, then `count` DecodeDesc, then two
+// lists of `count + 1` u64 tile prefixes (first tile of each item, then the
+// total): over the BF16 items' tiles, then over the FP16 / FP32 items' tiles
+// (an item's tiles count in its own list only).
 struct BatchHeader {
-  uint64_t total_tiles;
+  uint64_t total_tiles;   // tiles of BF16 items
   uint32_t count;
   uint32_t magic;
-  uint64_t reserved[6];
+  uint64_t wide_tiles;    // tiles of FP16 and FP32 items
+  uint64_t reserved[5];
 };
 static_assert(sizeof(BatchHeader) == 64, "table header layout");
 constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"

@@ -175,7 +175,7 @@ def test_wide_entry_points_host_checks(L):
     assert L.enc_compress_dt(vp(16), 100, 3, 300, 0, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -2
     assert L.enc_compress_dt(vp(16), 100000, 2, 512, 0, vp(16), 300000, vp(0), 0, vp(0), ctypes.byref(out)) == -3
     assert L.enc_compress_dt(vp(16), 100, 3, 512, 8, vp(16), 1000, vp(16), 1000, vp(0), ctypes.byref(out)) == -1
-    # FP16 / FP32 streams: the batched decode and the GEMMs refuse them
+    # FP16 / FP32 streams: the GEMMs refuse them
     info = enc.EncInfo()
     info.version, info.dtype, info.flags = 1, 3, 1
     info.n_elems, info.raw_off, info.total_bytes = 4096 * 512, 256, 256 + 4 * 4096 * 512
@@ -183,9 +183,6 @@ def test_wide_entry_points_host_checks(L):
                                  1 << 30, vp(0)) == -2
     assert L.enc_decompress_gemm_nt(vp(16), 1, 4096, vp(16), ctypes.byref(info), 512, vp(16), vp(16),
                                     1 << 30, vp(0)) == -2
-    item = enc.EncItem()
-    item.d_comp, item.d_out, item.info = 16, 16, info
-    assert L.enc_batch_prepare(ctypes.byref(item), 1, vp(16), 1 << 20, vp(0)) == -2
     # a RAW FP32 header with the BF16 total is inconsistent
     info.total_bytes = 256 + 2 * 4096 * 512
     assert L.enc_decompress(vp(16), ctypes.byref(info), vp(16), 4096 * 512, vp(0)) == -4

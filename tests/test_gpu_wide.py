@@ -201,3 +201,36 @@ def test_fp16_exponent_ceiling(E, orc):
     d = dev8(b)
     chk = E.enc_validate(d, E.enc_read_info(d))
     assert (chk.kind, chk.index) == want
+
+
+def test_batch_mixed_types(E, orc):
+    """One batched launch over BF16, FP16 and FP32 items, coded and RAW, of
+    ragged sizes: every output equals the input bits (the streams are the
+    oracle's)."""
+    rng = np.random.default_rng(31)
+    cases = [
+        (1, synth.gaussian_bits((300_001,), 0.02, 130, 1), 512),
+        (2, values(200_003, 2, 2), 512),
+        (3, values(100_005, 3, 3), 128),
+        (2, rng.integers(0, 1 << 16, 9_999, dtype=np.uint64).astype(np.uint16), 512),    # RAW
+        (3, rng.integers(0, 1 << 32, 7_777, dtype=np.uint64).astype(np.uint32), 4096),   # RAW
+        (1, synth.gaussian_bits((8_192,), 0.03, 130, 2), 256),
+        (3, values(65_536 * 3 + 8, 3, 4), 1024),
+    ]
+    items, wants = [], []
+    for dt, x, B in cases:
+        s = orc.encode(x, B, dtype=dt)
+        d = dev8(s)
+        info = E.enc_read_info(d)
+        assert info.dtype == dt
+        out = torch.empty(x.size, dtype=torch.int32 if dt == 3 else torch.int16, device="cuda")
+        items.append((d, info, out))
+        wants.append((dt, x))
+    say("wide batch of %d mixed items" % len(items))
+    table = E.enc_batch_prepare(items)
+    E.enc_decompress_batch(table, len(items))
+    torch.cuda.synchronize()
+    for (d, info, out), (dt, x) in zip(items, wants):
+        got = out.cpu().numpy()
+        got = got.view(np.uint32) if dt == 3 else got.view(np.uint16)
+        assert np.array_equal(got, x), (dt, x.size, info.flags)
