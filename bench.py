@@ -46,6 +46,8 @@ def parse():
                    help="decoder layers in the set (32 = the full 8B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other configurations (tiny, layer sweep, stress)")
     p.add_argument("--no-wide", action="store_true",
                    help="skip the FP16 / FP32 measurement")
     p.add_argument("--wide-layers", type=int, default=4,
@@ -282,6 +284,9 @@ def main():
     if not args.no_wide:
         result["wide_types"] = bench_wide(enc, synth, torch, np, dev, stream, args)
 
+    if not args.no_configs:
+        result["other_configs"] = bench_configs(enc, synth, torch, np, dev, stream, args)
+
     if not args.no_gemm:
         result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream)
         result["fused_gemm_nt"] = bench_gemm_nt(enc, synth, torch, np, dev)
@@ -364,6 +369,76 @@ def bench_wide(enc, synth, torch, np, dev, stream, args):
             "launches %.3f ms), bit-exact" % (name, res[name]["compression_ratio"], enc_ms, ms,
                                              res[name]["hbm_gbs"], pt_ms))
         del streams, outs, table
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_configs(enc, synth, torch, np, dev, stream, args):
+    """Ratio and throughput of the other configurations (context for the
+    headline, not the headline): the tiny matrix, one Llama-3-8B layer at
+    B = 256 / 512 / 1024, and the five 2^27-value stress distributions at the
+    same block sizes. Each case is compressed on the GPU (wall clock, one
+    host synchronisation per tensor) and decoded with one batched launch per
+    step, rotating over four copies of the streams and outputs so the
+    working set exceeds the 256 MB last-level cache (the tiny case does not:
+    it is launch-bound). Outputs are checked bit-exactly after the timing."""
+    cases = [("tiny", [synth.tiny()], (512,))]
+    layer = synth.layer()
+    cases.append(("layer", [layer[k] for k in sorted(layer)], (256, 512, 1024)))
+    for kind in synth.STRESS_KINDS:
+        cases.append(("stress." + kind, [synth.stress(kind)], (256, 512, 1024)))
+    res = {}
+    for name, tensors, blocks in cases:
+        xs = [torch.from_numpy(np.ascontiguousarray(t).reshape(-1).view(np.int16)).to(dev) for t in tensors]
+        n = sum(x.numel() for x in xs)
+        for B in blocks:
+            copies, total, enc_s = [], 0, 0.0
+            for c in range(4):
+                st = []
+                for x in xs:
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    comp, info = enc.enc_compress(x, B)
+                    torch.cuda.synchronize()
+                    enc_s += time.perf_counter() - t0
+                    st.append((comp.clone(), info))
+                    if c == 0:
+                        total += info.total_bytes
+                    del comp
+                outs = [torch.empty_like(x) for x in xs]
+                table = enc.enc_batch_prepare([(cp, inf, o) for (cp, inf), o in zip(st, outs)])
+                copies.append((st, outs, table))
+            for k in range(args.warmup):
+                st, outs, table = copies[k % 4]
+                enc.enc_decompress_batch(table, len(outs))
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            steps = max(args.steps, 4)
+            e0.record(stream)
+            for k in range(steps):
+                st, outs, table = copies[k % 4]
+                enc.enc_decompress_batch(table, len(outs))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            for st, outs, _ in copies:
+                for x, o in zip(xs, outs):
+                    if not torch.equal(o, x):
+                        log("MISMATCH in config %s B=%d" % (name, B))
+                        sys.exit(1)
+            res["%s.B%d" % (name, B)] = {
+                "elements": n,
+                "compression_ratio": round(2 * n / total, 5),
+                "raw_tensors": sum(1 for _, inf in copies[0][0] if inf.flags == 1),
+                "decode_ms": round(ms, 4),
+                "bf16_out_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+                "hbm_gbs": round((2 * n + total) / (ms * 1e-3) / 1e9, 1),
+                "encode_gbs_wall": round(4 * (2 * n + total) / enc_s / 1e9, 1),
+            }
+            log("config %-18s B=%4d: ratio %.4f, decode %.3f ms (%.0f GB/s HBM), bit-exact"
+                % (name, B, 2 * n / total, ms, res["%s.B%d" % (name, B)]["hbm_gbs"]))
+            del copies
+        del xs
         torch.cuda.empty_cache()
     return res
 
