@@ -234,9 +234,21 @@ def enc_decompress(comp, info, out=None, stream=None):
     if out is None:
         tdt = torch.int32 if info.dtype == FP32 else torch.int16
         out = torch.empty(max(info.n_elems, 1), dtype=tdt, device=comp.device)[:info.n_elems]
+    _check_out(out, info)
     _check(lib().enc_decompress(_ptr(comp), ctypes.byref(info), _ptr(out), out.numel(),
                                 _stream(stream)))
     return out
+
+
+def _check_out(out, info):
+    """The C ABI sees only a pointer and an element count: make sure the
+    output tensor holds that many elements of the stream's size."""
+    size = ELEM_BYTES.get(info.dtype)
+    if size is not None and out.element_size() != size:
+        raise TypeError("a dtype-%d stream decodes to %d-byte elements, the output has %d"
+                        % (info.dtype, size, out.element_size()))
+    if not out.is_contiguous():
+        raise ValueError("the output must be contiguous")
 
 
 def enc_batch_table_bytes(count):
@@ -249,6 +261,10 @@ def enc_batch_prepare(items, table=None, stream=None):
     arr = (EncItem * max(count, 1))()
     device = None
     for k, (comp, info, out) in enumerate(items):
+        _check_out(out, info)
+        if out.numel() != info.n_elems:
+            raise ValueError("item %d: output holds %d elements, the stream %d"
+                             % (k, out.numel(), info.n_elems))
         arr[k].d_comp = comp.data_ptr()
         arr[k].d_out = out.data_ptr()
         arr[k].info = info

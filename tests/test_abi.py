@@ -186,3 +186,19 @@ def test_wide_entry_points_host_checks(L):
     # a RAW FP32 header with the BF16 total is inconsistent
     info.total_bytes = 256 + 2 * 4096 * 512
     assert L.enc_decompress(vp(16), ctypes.byref(info), vp(16), 4096 * 512, vp(0)) == -4
+
+
+def test_binding_checks_output_element_size():
+    """The C ABI takes a pointer and an element count only; the binding
+    refuses an output whose element size does not match the stream's type."""
+    torch = pytest.importorskip("torch")
+    info = enc.EncInfo()
+    info.dtype, info.n_elems = 3, 10
+    with pytest.raises(TypeError):
+        enc._check_out(torch.empty(10, dtype=torch.int16), info)
+    enc._check_out(torch.empty(10, dtype=torch.int32), info)
+    info.dtype = 2
+    with pytest.raises(TypeError):
+        enc._check_out(torch.empty(10, dtype=torch.int32), info)
+    with pytest.raises(ValueError):
+        enc._check_out(torch.empty(20, dtype=torch.int16)[::2], info)
