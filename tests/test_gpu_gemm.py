@@ -179,3 +179,23 @@ def test_pow2_width_stream(E, orc, M):
     Xr = synth.gemm_activations(M, K)
     Y, A = orc.gemm_f64(Xr, W)
     assert_within(run_fused(E, Xr, comp, info, N), Y, A, "pow2 M=%d" % M)
+
+
+def test_largest_m(E, orc):
+    """M = 4096, the largest the entry point accepts: 32 M tiles of 128 rows;
+    one-hot rows reproduce W exactly, the fused and dense paths agree."""
+    M, K, N = 4096, 512, 512
+    W = synth.gaussian_bits((K, N), 0.02, 204, 0)
+    rng = np.random.default_rng(4096)
+    X = np.zeros((M, K), np.uint16)
+    ks = rng.integers(0, K, M)
+    X[np.arange(M), ks] = 0x3F80
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512)).cuda()
+    info = E.enc_read_info(comp)
+    say("largest M=4096")
+    want = bf16_f64(W)[ks]
+    assert np.array_equal(run_fused(E, X, comp, info, N), want)
+    assert np.array_equal(run_dense(E, X, W), want)
+    with pytest.raises(E.EncError) as e:
+        E.enc_decompress_gemm(dev(np.zeros((4097, K), np.uint16)), comp, info, N)
+    assert e.value.status == -5

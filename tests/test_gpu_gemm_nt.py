@@ -193,3 +193,17 @@ def test_dense_k_steps(E, orc, K, M):
     Y, A = oracle_nt(orc, X, W)
     say("nt dense K=%d M=%d" % (K, M))
     assert_within(run_dense(E, X, W), Y, A, "dense K=%d M=%d" % (K, M))
+
+
+def test_largest_m(E, orc):
+    M, N, K = 4096, 128, 512
+    W = synth.gaussian_bits((N, K), 0.02, 217, 0)
+    rng = np.random.default_rng(4097)
+    X = np.zeros((M, K), np.uint16)
+    ks = rng.integers(0, K, M)
+    X[np.arange(M), ks] = 0x3F80
+    comp, info = oracle_stream(E, orc, W, 512)
+    say("nt largest M=4096")
+    want = bf16_f64(W)[:, ks].T
+    assert np.array_equal(run_fused(E, X, comp, info, N), want)
+    assert np.array_equal(run_dense(E, X, W), want)
