@@ -142,6 +142,38 @@ enc_status enc_compress_dt(const void *d_in, uint64_t n_elems, uint32_t dtype, u
                            uint32_t options, void *d_out, uint64_t out_capacity, void *d_ws,
                            uint64_t ws_bytes, void *stream, enc_info *h_info);
 
+/* Batched compression of BF16 tensors (ENEC Abstract: the same per-block
+ * code and decoupled prefix scan as enc_compress_ex; one kernel launch
+ * covers every tensor, which matters for a model's many small tensors).
+ * Each item's stream is byte-identical to what enc_compress_ex writes for
+ * it with the same block size and options. */
+typedef struct enc_citem {
+  const uint16_t *d_in;  /* device BF16 bit patterns, 16-byte aligned (NULL allowed if n_elems is 0) */
+  uint64_t n_elems;      /* values */
+  void *d_out;           /* device output, 16-byte aligned */
+  uint64_t out_capacity; /* bytes of d_out: at least enc_compress_bound(n_elems) */
+} enc_citem;
+
+/* Device workspace bytes for enc_compress_batch over these items: the batch
+ * tables, per-item look-back state, and room for enc_compress_ex of the
+ * largest item. Returns 0 for an unsupported block size, a negative count or
+ * NULL items with count > 0. */
+uint64_t enc_compress_batch_workspace_bytes(const enc_citem *h_items, int count,
+                                            uint32_t block_size);
+
+/* Compress `count` items: one single-pass launch over all of them, one
+ * synchronisation of `stream` to read back their sizes, one launch that
+ * writes the coded headers and section padding, a RAW copy launch per item
+ * whose coded stream would not be smaller (and for empty items), then a
+ * second synchronisation (the host tables live only for the call). Items
+ * whose look-back wait gave up are re-encoded with enc_compress_ex. Fills
+ * h_infos[k] for each item. Errors: an item's capacity below its RAW size
+ * is ENC_ERR_CAPACITY, as is a short workspace; all checks run before any
+ * launch. Options as enc_compress_ex. count 0 does nothing. */
+enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t block_size,
+                              uint32_t options, void *d_ws, uint64_t ws_bytes, void *stream,
+                              enc_info *h_infos);
+
 /* Parse and check a stream header held in host memory (header_bytes >= 256)
  * for a stream of comp_bytes bytes. Checks magic, version, dtype, flags,
  * block size, section offsets against n, and total <= comp_bytes. Host only;

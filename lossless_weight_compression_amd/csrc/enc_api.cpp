@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "enc_common.h"
+#include "encode_batch.h"
 
 using namespace enc;
 
@@ -328,6 +329,30 @@ enc_status compress_wide(const void *d_in, uint64_t n, uint32_t dtype, uint32_t 
   return ENC_OK;
 }
 
+// Workspace of enc_compress_batch, in order: the single-pass table, the
+// header/pads table, one 16-byte result slot per item (payload bytes, then
+// the error word in the upper half of the second u64), the per-item status
+// words (64-byte aligned runs). The status words and result slots are one
+// contiguous range, cleared by one memset.
+struct BatchEncLayout {
+  uint64_t table, pads, results, status, status_bytes, total;
+};
+
+BatchEncLayout batch_enc_layout(const enc_citem *items, int count) {
+  BatchEncLayout b;
+  b.table = 0;
+  b.pads = align_up(sizeof(EncBatchHeader) + (uint64_t)count * sizeof(EncodeArgs) +
+                        8 * ((uint64_t)count + 1),
+                    kSectionAlign);
+  b.results = b.pads + align_up((uint64_t)count * sizeof(PadsItem), kSectionAlign);
+  b.status = b.results + align_up(16 * (uint64_t)count, kSectionAlign);
+  b.status_bytes = 0;
+  for (int k = 0; k < count; ++k)
+    if (items[k].n_elems > 0) b.status_bytes += align_up(8 * onepass_batch_tiles(items[k].n_elems), 64);
+  b.total = b.status + align_up(b.status_bytes, kSectionAlign);
+  return b;
+}
+
 uint64_t batch_bytes(int count) {
   return align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
                       2 * 8 * ((uint64_t)count + 1),
@@ -489,6 +514,175 @@ enc_status enc_compress_dt(const void *d_in, uint64_t n, uint32_t dtype, uint32_
     return fail(ENC_ERR_CAPACITY, "workspace of %llu bytes needed", (unsigned long long)need_ws);
   return compress_wide(d_in, n, dtype, block_size, pow2, static_cast<uint8_t *>(d_out),
                        out_capacity, static_cast<uint8_t *>(d_ws), s, h_info);
+}
+
+uint64_t enc_compress_batch_workspace_bytes(const enc_citem *h_items, int count,
+                                            uint32_t block_size) {
+  if (log2_block(block_size) < 0 || count < 0 || (count > 0 && !h_items)) return 0;
+  uint64_t need = batch_enc_layout(h_items, count).total;
+  for (int k = 0; k < count; ++k) {
+    const uint64_t one = enc_compress_workspace_bytes(h_items[k].n_elems, block_size);
+    if (one > need) need = one;
+  }
+  return need;
+}
+
+enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t block_size,
+                              uint32_t options, void *d_ws, uint64_t ws_bytes, void *stream,
+                              enc_info *h_infos) {
+  clear_err();
+  if (options & ~(uint32_t)ENC_OPT_POW2_WIDTHS)
+    return fail(ENC_ERR_INVALID_ARG, "unknown options 0x%x", options);
+  const uint32_t pow2 = (options & ENC_OPT_POW2_WIDTHS) ? 1u : 0u;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (count < 0) return fail(ENC_ERR_INVALID_ARG, "count %d", count);
+  if (count == 0) return ENC_OK;
+  if (!h_items || !h_infos) return fail(ENC_ERR_INVALID_ARG, "h_items or h_infos is NULL");
+  const int lb = log2_block(block_size);
+  if (lb < 0)
+    return fail(ENC_ERR_UNSUPPORTED, "block size %u (supported: 128..4096, powers of two)",
+                block_size);
+  uint64_t total_wgs = 0;
+  for (int k = 0; k < count; ++k) {
+    const enc_citem &it = h_items[k];
+    if (!it.d_out) return fail(ENC_ERR_INVALID_ARG, "item %d: d_out is NULL", k);
+    if (it.n_elems > 0 && !it.d_in) return fail(ENC_ERR_INVALID_ARG, "item %d: d_in is NULL", k);
+    if (it.n_elems > kMaxElems) return fail(ENC_ERR_UNSUPPORTED, "item %d: n above 2^40", k);
+    if (!aligned16(it.d_in) || !aligned16(it.d_out))
+      return fail(ENC_ERR_INVALID_ARG, "item %d: device buffers must be 16-byte aligned", k);
+    if (it.out_capacity < kHeaderBytes + 2 * it.n_elems)
+      return fail(ENC_ERR_CAPACITY, "item %d: output capacity %llu below the RAW size %llu", k,
+                  (unsigned long long)it.out_capacity,
+                  (unsigned long long)(kHeaderBytes + 2 * it.n_elems));
+    total_wgs += onepass_batch_tiles(it.n_elems);
+  }
+  // one launch: the grid's work-item count (256 per workgroup) is a u32
+  if (total_wgs >= (1ull << 24)) return fail(ENC_ERR_UNSUPPORTED, "batch above 2^24 tiles");
+  if (!aligned16(d_ws)) return fail(ENC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const uint64_t need_ws = enc_compress_batch_workspace_bytes(h_items, count, block_size);
+  if (!d_ws || ws_bytes < need_ws)
+    return fail(ENC_ERR_CAPACITY, "workspace of %llu bytes needed", (unsigned long long)need_ws);
+
+  // Items the single pass takes; the others (empty, or fixed sections past
+  // the RAW size, which always ends RAW) get their RAW stream directly.
+  uint8_t *ws = static_cast<uint8_t *>(d_ws);
+  const BatchEncLayout W = batch_enc_layout(h_items, count);
+  std::vector<uint8_t> table(W.pads, 0);
+  EncBatchHeader *th = reinterpret_cast<EncBatchHeader *>(table.data());
+  EncodeArgs *targs = reinterpret_cast<EncodeArgs *>(table.data() + sizeof(EncBatchHeader));
+  std::vector<int> coded_items, raw_items;
+  const uint32_t spins = lookback_spin_limit();
+  uint64_t status_at = W.status, wgs = 0;
+  std::vector<uint64_t> begin;
+  for (int k = 0; k < count; ++k) {
+    const enc_citem &it = h_items[k];
+    const uint64_t n = it.n_elems;
+    if (n == 0) {
+      raw_items.push_back(k);
+      continue;
+    }
+    const Layout L = layout_of(n, block_size);
+    if (L.payload_off > kHeaderBytes + 2 * n) {
+      raw_items.push_back(k);
+      continue;
+    }
+    EncodeArgs &a = targs[coded_items.size()];
+    memset(&a, 0, sizeof a);
+    a.pow2 = pow2;
+    a.in = it.d_in;
+    a.out = static_cast<uint8_t *>(it.d_out);
+    a.n = n;
+    a.nb = L.nb;
+    a.nseg = L.nseg;
+    a.meta_off = L.meta_off;
+    a.segoff_off = L.segoff_off;
+    a.payload_off = L.payload_off;
+    a.log2b = (uint32_t)lb;
+    a.ntiles = onepass_batch_tiles(n);
+    a.cap = it.out_capacity;
+    a.status = reinterpret_cast<uint64_t *>(ws + status_at);
+    a.ws_total = reinterpret_cast<uint64_t *>(ws + W.results + 16 * coded_items.size());
+    a.error = reinterpret_cast<uint32_t *>(ws + W.results + 16 * coded_items.size() + 12);
+    a.spin_limit = spins;
+    status_at += align_up(8 * a.ntiles, 64);
+    begin.push_back(wgs);
+    wgs += a.ntiles;
+    coded_items.push_back(k);
+  }
+  const uint32_t nc = (uint32_t)coded_items.size();
+  begin.push_back(wgs);
+  th->total_wgs = wgs;
+  th->count = nc;
+  th->magic = kEncBatchMagic;
+  // the prefix list follows the nc argument records actually used
+  memcpy(table.data() + sizeof(EncBatchHeader) + nc * sizeof(EncodeArgs), begin.data(),
+         8 * begin.size());
+
+  hipError_t e;
+  std::vector<uint64_t> back(2 * (size_t)nc, 0);
+  if (nc > 0) {
+    e = hipMemsetAsync(ws + W.results, 0, W.total - W.results, s);
+    if (e != hipSuccess) return hip_fail(e, "look-back state initialisation");
+    e = hipMemcpyAsync(ws + W.table, table.data(), table.size(), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "batch table upload");
+    e = launch_encode_onepass_batch(ws + W.table, wgs, s);
+    if (e != hipSuccess) return hip_fail(e, "batched single-pass kernel launch");
+    e = hipMemcpyAsync(back.data(), ws + W.results, 16 * (uint64_t)nc, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "size read-back");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  }
+
+  // Headers and pads of the coded results, one launch; RAW copies and the
+  // items whose look-back gave up (two-pass encoder) one by one.
+  std::vector<PadsItem> pads;
+  std::vector<int> retry;
+  for (uint32_t c = 0; c < nc; ++c) {
+    const int k = coded_items[c];
+    const uint64_t n = h_items[k].n_elems;
+    if (back[2 * c + 1] >> 32) {
+      retry.push_back(k);
+      continue;
+    }
+    const uint64_t payload = back[2 * c];
+    const Layout L = layout_of(n, block_size);
+    if (L.payload_off + payload >= kHeaderBytes + 2 * n) {
+      raw_items.push_back(k);
+      continue;
+    }
+    h_infos[k] = coded_info(n, block_size, L, payload, pow2);
+    PadsItem p;
+    p.a = targs[c];
+    p.h = header_of(h_infos[k]);
+    pads.push_back(p);
+  }
+  if (!pads.empty()) {
+    e = hipMemcpyAsync(ws + W.pads, pads.data(), pads.size() * sizeof(PadsItem),
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "pads table upload");
+    const enc_status st = launched(launch_encode_pads_batch(ws + W.pads, (uint32_t)pads.size(), s),
+                                   s, "header kernel launch");
+    if (st != ENC_OK) return st;
+  }
+  for (const int k : raw_items) {
+    const enc_citem &it = h_items[k];
+    const enc_info i = raw_info(it.n_elems, block_size);
+    const enc_status st = launched(launch_encode_raw(it.d_in, static_cast<uint8_t *>(it.d_out),
+                                                     it.n_elems, header_of(i), s),
+                                   s, "raw copy launch");
+    if (st != ENC_OK) return st;
+    h_infos[k] = i;
+  }
+  // The host tables above must outlive their uploads.
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  for (const int k : retry) {
+    const enc_citem &it = h_items[k];
+    const enc_status st = enc_compress_ex(it.d_in, it.n_elems, block_size, options, it.d_out,
+                                          it.out_capacity, d_ws, ws_bytes, stream, &h_infos[k]);
+    if (st != ENC_OK) return st;
+  }
+  return ENC_OK;
 }
 
 enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_t comp_bytes,

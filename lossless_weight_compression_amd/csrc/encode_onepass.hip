@@ -37,7 +37,7 @@
 // Status words hold flag and value together and are read and written with
 // agent-scope relaxed atomics, so no fence is needed; every wait is bounded
 // (on give-up the kernel flags an error and the host falls back).
-#include "enc_common.h"
+#include "encode_batch.h"
 
 namespace enc {
 namespace {
@@ -199,15 +199,16 @@ __device__ __forceinline__ uint32_t pack4(uint32_t d, uint32_t w) {
          (__builtin_amdgcn_ubfe(d, 16, 8) << (2 * w)) | ((d >> 24) << (3 * w));
 }
 
+// One workgroup's tile of stream `a` (the kernel body, shared by the
+// single-stream and the batched launch).
 template <uint32_t SUB>
-__global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
+__device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile) {
   constexpr uint32_t kPayBytes = SUB * kTileGroups * 8 + 16;   // a tile's payload, at most
   __shared__ uint32_t pay[kPayBytes / 4];
   __shared__ uint32_t smin[64], smax[64], sblk[64], s_suboff[SUB];
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_run;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t tile = blockIdx.x;
   const uint32_t log2b = a.log2b, log2gpb = log2b - 3;
   const uint32_t bps = (uint32_t)(kTileElems >> log2b);            // blocks per sub-tile
   const uint64_t n = a.n;
@@ -365,11 +366,37 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
   }
 }
 
+template <uint32_t SUB>
+__global__ __launch_bounds__(kThreads) void k_enc_onepass(EncodeArgs a) {
+  onepass_tile<SUB>(a, blockIdx.x);
+}
+
+// Many streams in one launch (table layout in encode_batch.h): workgroup b
+// runs tile b - begin[k] of the stream k whose range holds b. Tiles of one
+// stream keep their order, so the look-back still only waits for workgroups
+// dispatched earlier. All streams take the largest tile (kOnePassMaxSub
+// sub-tiles): with many streams in flight at once, small ones no longer
+// need more workgroups to fill the device.
+__global__ __launch_bounds__(kThreads) void k_enc_onepass_batch(const uint8_t *__restrict__ table) {
+  const EncBatchHeader *h = reinterpret_cast<const EncBatchHeader *>(table);
+  const uint32_t count = h->count;
+  const EncodeArgs *items = reinterpret_cast<const EncodeArgs *>(table + sizeof(EncBatchHeader));
+  const uint64_t *begin = reinterpret_cast<const uint64_t *>(table + sizeof(EncBatchHeader) +
+                                                             count * sizeof(EncodeArgs));
+  const uint64_t b = blockIdx.x;
+  uint32_t lo = 0, hi = count;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (begin[mid] <= b) lo = mid; else hi = mid;
+  }
+  const EncodeArgs a = items[lo];
+  onepass_tile<kOnePassMaxSub>(a, b - begin[lo]);
+}
+
 // Header and the zero padding of the sm, meta and segment-offset sections of
-// a stream the single pass wrote.
-__global__ __launch_bounds__(kThreads) void k_enc_pads(EncodeArgs a, HeaderImage h) {
-  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+// a stream the single pass wrote (threads tid, tid + stride, ...).
+__device__ __forceinline__ void pads_body(const EncodeArgs &a, const HeaderImage &h, uint64_t tid,
+                                          uint64_t stride) {
   if (tid < 64) reinterpret_cast<uint32_t *>(a.out)[tid] = reinterpret_cast<const uint32_t *>(h.bytes)[tid];
   const uint64_t sm_from = kHeaderBytes + align_up(a.n, 8), sm_to = a.meta_off;
   const uint64_t meta_from = a.meta_off + 2 * a.nb, meta_to = a.segoff_off;
@@ -379,6 +406,15 @@ __global__ __launch_bounds__(kThreads) void k_enc_pads(EncodeArgs a, HeaderImage
     const uint64_t at = i < l0 ? sm_from + i : i < l0 + l1 ? meta_from + (i - l0) : seg_from + (i - l0 - l1);
     a.out[at] = 0;
   }
+}
+
+__global__ __launch_bounds__(kThreads) void k_enc_pads(EncodeArgs a, HeaderImage h) {
+  pads_body(a, h, (uint64_t)blockIdx.x * blockDim.x + threadIdx.x, (uint64_t)gridDim.x * blockDim.x);
+}
+
+// One workgroup per stream of a PadsItem table.
+__global__ __launch_bounds__(kThreads) void k_enc_pads_batch(const PadsItem *__restrict__ items) {
+  pads_body(items[blockIdx.x].a, items[blockIdx.x].h, threadIdx.x, blockDim.x);
 }
 
 }  // namespace
@@ -394,6 +430,20 @@ hipError_t launch_encode_onepass(const EncodeArgs &a, hipStream_t s) {
 
 hipError_t launch_encode_pads(const EncodeArgs &a, const HeaderImage &h, hipStream_t s) {
   hipLaunchKernelGGL(k_enc_pads, dim3(4), dim3(kThreads), 0, s, a, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_onepass_batch(const void *table, uint64_t total_wgs, hipStream_t s) {
+  if (total_wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_enc_onepass_batch, dim3((uint32_t)total_wgs), dim3(kThreads), 0, s,
+                     static_cast<const uint8_t *>(table));
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_pads_batch(const void *items, uint32_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_enc_pads_batch, dim3(count), dim3(kThreads), 0, s,
+                     static_cast<const PadsItem *>(items));
   return hipGetLastError();
 }
 

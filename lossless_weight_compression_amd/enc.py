@@ -55,6 +55,11 @@ class EncItem(ctypes.Structure):
     _fields_ = [("d_comp", ctypes.c_void_p), ("d_out", ctypes.c_void_p), ("info", EncInfo)]
 
 
+class EncCItem(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_void_p), ("n_elems", ctypes.c_uint64),
+                ("d_out", ctypes.c_void_p), ("out_capacity", ctypes.c_uint64)]
+
+
 _VP = ctypes.c_void_p
 _U32 = ctypes.c_uint32
 _U64 = ctypes.c_uint64
@@ -69,6 +74,9 @@ SIGNATURES = {
     "enc_compress_ex": (_ST, [_VP, _U64, _U32, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
     "enc_compress_bound_dt": (_U64, [_U64, _U32]),
     "enc_compress_dt": (_ST, [_VP, _U64, _U32, _U32, _U32, _VP, _U64, _VP, _U64, _VP, _INFO_P]),
+    "enc_compress_batch_workspace_bytes": (_U64, [ctypes.POINTER(EncCItem), ctypes.c_int, _U32]),
+    "enc_compress_batch": (_ST, [ctypes.POINTER(EncCItem), ctypes.c_int, _U32, _U32, _VP, _U64, _VP,
+                                 _INFO_P]),
     "enc_parse_header": (_ST, [_VP, _U64, _U64, _INFO_P]),
     "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
     "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
@@ -207,6 +215,46 @@ def enc_compress(x, block_size=512, out=None, ws=None, stream=None, pow2_widths=
         _check(lib().enc_compress(_ptr(x), n, block_size, _ptr(out), out.numel(), _ptr(ws),
                                   ws.numel(), _stream(stream), ctypes.byref(info)))
     return out[:info.total_bytes], info
+
+
+def _citems(xs, outs):
+    arr = (EncCItem * max(len(xs), 1))()
+    for k, (x, out) in enumerate(zip(xs, outs)):
+        arr[k].d_in = x.data_ptr()
+        arr[k].n_elems = x.numel()
+        arr[k].d_out = out.data_ptr()
+        arr[k].out_capacity = out.numel() * out.element_size()
+    return arr
+
+
+def enc_compress_batch_workspace_bytes(xs, block_size=512):
+    """Workspace bytes enc_compress_batch needs for these BF16 tensors."""
+    xs = [_bits(x) for x in xs]
+    return lib().enc_compress_batch_workspace_bytes(_citems(xs, xs), len(xs), block_size)
+
+
+def enc_compress_batch(xs, block_size=512, outs=None, ws=None, stream=None, pow2_widths=False):
+    """Compress a list of BF16 tensors with one encoder launch. Returns a list
+    of (stream bytes as a uint8 CUDA tensor sliced to its size, EncInfo), each
+    byte-identical to enc_compress of the same tensor. outs: uint8 tensors of
+    at least enc_compress_bound(n) bytes each (allocated if None)."""
+    xs = [_bits(x) for x in xs]
+    if not xs:
+        return []
+    if outs is None:
+        outs = [_empty_u8(enc_compress_bound(x.numel()), x.device) for x in xs]
+    if len(outs) != len(xs):
+        raise ValueError("outs must match xs")
+    arr = _citems(xs, outs)
+    if ws is None:
+        ws = _empty_u8(lib().enc_compress_batch_workspace_bytes(arr, len(xs), block_size),
+                       xs[0].device)
+    infos = (EncInfo * len(xs))()
+    _check(lib().enc_compress_batch(arr, len(xs), block_size,
+                                    ENC_OPT_POW2_WIDTHS if pow2_widths else 0, _ptr(ws), ws.numel(),
+                                    _stream(stream), infos))
+    return [(out[:infos[k].total_bytes], EncInfo.from_buffer_copy(infos[k]))
+            for k, out in enumerate(outs)]
 
 
 def enc_parse_header(header, comp_bytes=None):

@@ -40,6 +40,7 @@ def test_exports_every_declared_symbol(L):
 def test_struct_layouts():
     assert ctypes.sizeof(enc.EncInfo) == 96
     assert ctypes.sizeof(enc.EncItem) == 112
+    assert ctypes.sizeof(enc.EncCItem) == 32
 
 
 def test_sizes(L):
@@ -202,3 +203,38 @@ def test_binding_checks_output_element_size():
         enc._check_out(torch.empty(10, dtype=torch.int32), info)
     with pytest.raises(ValueError):
         enc._check_out(torch.empty(20, dtype=torch.int16)[::2], info)
+
+
+def test_batch_compress_host_checks(L):
+    """enc_compress_batch rejects bad arguments before any launch, and its
+    workspace size covers the batch tables and the single-tensor fallback."""
+    vp = ctypes.c_void_p
+    items = (enc.EncCItem * 2)()
+    for k, n in enumerate([1 << 20, 1000]):
+        items[k].d_in, items[k].n_elems = 16 * (k + 1), n
+        items[k].d_out, items[k].out_capacity = 4096 * (k + 1), 256 + 2 * n
+    ws = L.enc_compress_batch_workspace_bytes(items, 2, 512)
+    assert ws % 256 == 0
+    assert ws >= enc.enc_compress_workspace_bytes(1 << 20, 512)
+    # tables (64 + 2 x 136 + 3 x 8 -> 512; 2 x 392 -> 1024), two result slots
+    # (256), status words (32 + 1 tiles of 32768 values: 256 + 64 -> 512)
+    assert ws >= 512 + 1024 + 256 + 512
+    assert L.enc_compress_batch_workspace_bytes(items, 2, 300) == 0
+    assert L.enc_compress_batch_workspace_bytes(items, -1, 512) == 0
+    assert L.enc_compress_batch_workspace_bytes(None, 1, 512) == 0
+    infos = (enc.EncInfo * 2)()
+    assert L.enc_compress_batch(items, 0, 512, 0, vp(0), 0, vp(0), infos) == 0   # nothing to do
+    assert L.enc_compress_batch(items, -1, 512, 0, vp(16), ws, vp(0), infos) == -1
+    assert L.enc_compress_batch(items, 2, 512, 8, vp(16), ws, vp(0), infos) == -1    # option
+    assert L.enc_compress_batch(items, 2, 300, 0, vp(16), ws, vp(0), infos) == -2    # block size
+    assert L.enc_compress_batch(items, 2, 512, 0, vp(16), ws - 16, vp(0), infos) == -3
+    assert L.enc_compress_batch(items, 2, 512, 0, vp(0), 0, vp(0), infos) == -3
+    assert L.enc_compress_batch(items, 2, 512, 0, vp(24), ws, vp(0), infos) == -1    # unaligned ws
+    items[1].out_capacity -= 1
+    assert L.enc_compress_batch(items, 2, 512, 0, vp(16), ws, vp(0), infos) == -3
+    assert "item 1" in enc.enc_last_error()
+    items[1].out_capacity += 1
+    items[0].d_out = 4100
+    assert L.enc_compress_batch(items, 2, 512, 0, vp(16), ws, vp(0), infos) == -1
+    items[0].d_out = 0
+    assert L.enc_compress_batch(items, 2, 512, 0, vp(16), ws, vp(0), infos) == -1
