@@ -36,6 +36,9 @@ namespace {
 
 constexpr uint32_t GPT = kGroupsPerThread;
 
+// Decoded output is written once: every 16-byte store is store_nt16.
+__device__ __forceinline__ void store_out16(void *p, uint4 v) { store_nt16(p, v); }
+
 // Tail group: store only the elements below n (no dynamically indexed array,
 // so nothing is placed in scratch or LDS).
 __device__ __forceinline__ void store_partial(uint16_t *out, uint64_t e0, uint64_t n, uint4 o) {
@@ -50,7 +53,7 @@ __device__ __forceinline__ void copy_group_raw(const uint16_t *__restrict__ src,
                                                uint16_t *__restrict__ out, uint64_t e0, uint64_t n,
                                                uint4 v) {
   if (e0 + 8 <= n) {
-    *reinterpret_cast<uint4 *>(out + e0) = v;
+    store_out16(out + e0, v);
   } else {
     for (uint64_t e = e0; e < n; ++e) out[e] = src[e];
   }
@@ -174,7 +177,7 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     const uint32_t hi = __builtin_amdgcn_alignbit(q2[it], q1[it], sh);
     const uint4 o = join_group(lo, hi, w, base4, sml[it], smh[it]);
     if (valid == 8)
-      *reinterpret_cast<uint4 *>(out + e0) = o;
+      store_out16(out + e0, o);
     else
       store_partial(out, e0, n, o);
   }
@@ -202,7 +205,7 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     for (uint32_t it = 0; it < CPT; ++it) {
       const uint64_t b = b0 + 16 * (uint64_t)(it * kThreads + tid);
       if (b + 16 <= bn)
-        *reinterpret_cast<uint4 *>(outb + b) = *reinterpret_cast<const uint4 *>(s + kHeaderBytes + b);
+        store_out16(outb + b, *reinterpret_cast<const uint4 *>(s + kHeaderBytes + b));
       else
         for (uint64_t k = b; k < bn; ++k) outb[k] = s[kHeaderBytes + k];
     }
@@ -262,7 +265,7 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       uint32_t *dst = reinterpret_cast<uint32_t *>(outb) + e0;
       const uint64_t rem = n - e0;
       if (rem >= 4) {
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        store_out16(dst, make_uint4(o[0], o[1], o[2], o[3]));
       } else {
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k)
@@ -327,8 +330,8 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 23) << 31) | (e[k] << 23) | (sm[k] & 0x7FFFFFu);
       uint32_t *dst = reinterpret_cast<uint32_t *>(outb) + e0;
       if (valid == 8) {
-        reinterpret_cast<uint4 *>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<uint4 *>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        store_out16(dst, make_uint4(o[0], o[1], o[2], o[3]));
+        store_out16(dst + 4, make_uint4(o[4], o[5], o[6], o[7]));
       } else {
 #pragma unroll
         for (uint32_t k = 0; k < 8; ++k)
@@ -359,8 +362,8 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 10) << 15) | ((e[k] & 0x1Fu) << 10) | (sm[k] & 0x3FFu);
       uint16_t *dst = reinterpret_cast<uint16_t *>(outb) + e0;
       if (valid == 8) {
-        *reinterpret_cast<uint4 *>(dst) =
-            make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16, o[6] | o[7] << 16);
+        store_out16(dst, make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16,
+                                    o[6] | o[7] << 16));
       } else {
 #pragma unroll
         for (uint32_t k = 0; k < 8; ++k)

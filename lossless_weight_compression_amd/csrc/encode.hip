@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_pack(EncodeArgs a, uint64_t nt
     __syncthreads();
     uint8_t *dst = a.out + a.payload_off + a.ws_segsum[seg] + tstart;
     for (uint32_t i = tid; i < tbytes / 16; i += kThreads)
-      reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(lds)[i];
+      store_nt16(dst + 16 * i, reinterpret_cast<const uint4 *>(lds)[i]);
     __syncthreads();
   }
 }
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_raw(const uint16_t *__restrict
   uint16_t *dst = reinterpret_cast<uint16_t *>(out + kHeaderBytes);
   const uint64_t nvec = n / 8;
   for (uint64_t i = tid; i < nvec; i += stride)
-    reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(in)[i];
+    store_nt16(dst + 8 * i, reinterpret_cast<const uint4 *>(in)[i]);
   for (uint64_t i = nvec * 8 + tid; i < n; i += stride) dst[i] = in[i];
 }
 

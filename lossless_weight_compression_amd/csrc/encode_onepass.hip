@@ -48,6 +48,11 @@ constexpr uint64_t kValMask = (1ull << 62) - 1;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// Cache-policy operand of the buffer stores of the sm plane and payloads:
+// the non-temporal hint (the stream is written once and not read back by
+// the encoder; the 8B-shaped set encodes 2% faster with it).
+constexpr int kStoreNT = 2;
+
 __device__ __forceinline__ uint32_t pmax16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                 __builtin_bit_cast(u16x2, b)));
@@ -324,7 +329,7 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
         lo &= bits >= 32 ? ~0u : (1u << bits) - 1;
         hi &= bits <= 32 ? 0u : (1u << (bits - 32)) - 1;
       }
-      __builtin_amdgcn_raw_buffer_store_b64((u32x2){s0, s1}, sm_rs, 8 * (sub * kTileGroups + q), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){s0, s1}, sm_rs, 8 * (sub * kTileGroups + q), 0, kStoreNT);
       const uint32_t pos = (info >> 16) + (q & ((1u << log2gpb) - 1)) * w;
       const uint32_t sh = (pos & 3) * 8, d0 = pos >> 2;
       const uint32_t w0 = lo << sh;
@@ -362,7 +367,7 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
   const __amdgpu_buffer_rsrc_t pay_rs = range_rsrc(a.out + dst, a.cap > dst ? a.cap - dst : 0);
   for (uint32_t i = tid; i < s_run / 16; i += kThreads) {
     const uint4 d = reinterpret_cast<const uint4 *>(pay)[i];
-    __builtin_amdgcn_raw_buffer_store_b128((u32x4){d.x, d.y, d.z, d.w}, pay_rs, 16 * i, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){d.x, d.y, d.z, d.w}, pay_rs, 16 * i, 0, kStoreNT);
   }
 }
 

@@ -217,14 +217,14 @@ __global__ __launch_bounds__(kThreads) void k_encw_pack(EncodeArgs a, uint64_t n
     __syncthreads();
     uint8_t *dst = a.out + a.payload_off + a.ws_segsum[seg] + tstart;
     for (uint32_t i = tid; i < tbytes / 16; i += kThreads)
-      reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(pay)[i];
+      store_nt16(dst + 16 * i, reinterpret_cast<const uint4 *>(pay)[i]);
     // kept fields: the tile's bytes start 16-byte aligned (1024 S is a
     // multiple of 16); bytes past the section's last field are not written
     const uint64_t sm0 = (uint64_t)kTileSm * tile;
     const uint32_t len = (uint32_t)(sm_total - sm0 < kTileSm ? sm_total - sm0 : kTileSm);
     uint8_t *sdst = a.out + kHeaderBytes + sm0;
     for (uint32_t i = tid; i < len / 16; i += kThreads)
-      reinterpret_cast<uint4 *>(sdst)[i] = reinterpret_cast<const uint4 *>(smi)[i];
+      store_nt16(sdst + 16 * i, reinterpret_cast<const uint4 *>(smi)[i]);
     if (tid < (len & 15)) {
       const uint32_t b = (len & ~15u) + tid;
       sdst[b] = reinterpret_cast<const uint8_t *>(smi)[b];
