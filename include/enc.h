@@ -205,14 +205,31 @@ typedef struct enc_item {
 /* Device bytes of the batch table for `count` items. */
 uint64_t enc_batch_table_bytes(int count);
 
-/* Validate the items and write the batch table into d_table (device, at least
- * enc_batch_table_bytes(count) bytes). Synchronous: returns after the table
- * has been copied. The table stays valid while the streams and outputs do. */
-enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table,
-                             uint64_t table_bytes, void *stream);
+/* Launch sizes of a prepared batch, filled by enc_batch_prepare: the decoder
+ * runs one workgroup per 8192-value tile, and the grid size has to be known
+ * on the host when the kernel is launched. */
+typedef struct enc_batch_plan {
+  uint64_t tiles;      /* tiles of the BF16 items */
+  uint64_t wide_tiles; /* tiles of the FP16 and FP32 items */
+  const void *d_table; /* the table the plan belongs to */
+  int32_t count;       /* its item count */
+  uint32_t reserved;
+} enc_batch_plan;
 
-/* Decode every item of a prepared table with one kernel launch; asynchronous. */
-enc_status enc_decompress_batch(const void *d_table, int count, void *stream);
+/* Validate the items, write the batch table into d_table (device, at least
+ * enc_batch_table_bytes(count) bytes) and fill *h_plan. Synchronous: returns
+ * after the table has been copied. The table stays valid while the streams
+ * and outputs do. */
+enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table,
+                             uint64_t table_bytes, void *stream, enc_batch_plan *h_plan);
+
+/* Decode every item of a prepared table: one kernel launch for the BF16
+ * items and one for the FP16 / FP32 items (each only if there are any;
+ * inputs past 2^23 tiles take one more launch per 2^23 tiles).
+ * Asynchronous. h_plan must be the plan enc_batch_prepare filled for this
+ * table and count (else ENC_ERR_INVALID_ARG). */
+enc_status enc_decompress_batch(const void *d_table, int count, const enc_batch_plan *h_plan,
+                                void *stream);
 
 /* Device workspace bytes for enc_decompress_gemm / enc_gemm_dense: the
  * split-K partial sums (fp32, one slice per K range). */

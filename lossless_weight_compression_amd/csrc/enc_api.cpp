@@ -749,10 +749,11 @@ enc_status enc_decompress(const void *d_comp, const enc_info *h_info, void *d_ou
 uint64_t enc_batch_table_bytes(int count) { return count < 0 ? 0 : batch_bytes(count); }
 
 enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, uint64_t table_bytes,
-                             void *stream) {
+                             void *stream, enc_batch_plan *h_plan) {
   clear_err();
   if (count < 0) return fail(ENC_ERR_INVALID_ARG, "negative count");
   if (count > 0 && !h_items) return fail(ENC_ERR_INVALID_ARG, "h_items is NULL");
+  if (!h_plan) return fail(ENC_ERR_INVALID_ARG, "h_plan is NULL");
   if (!d_table || !aligned16(d_table)) return fail(ENC_ERR_INVALID_ARG, "d_table NULL or unaligned");
   const uint64_t need = batch_bytes(count);
   if (table_bytes < need)
@@ -794,16 +795,26 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
   if (e != hipSuccess) return hip_fail(e, "table upload");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  memset(h_plan, 0, sizeof *h_plan);
+  h_plan->tiles = t;
+  h_plan->wide_tiles = tw;
+  h_plan->d_table = d_table;
+  h_plan->count = count;
   return ENC_OK;
 }
 
-enc_status enc_decompress_batch(const void *d_table, int count, void *stream) {
+enc_status enc_decompress_batch(const void *d_table, int count, const enc_batch_plan *h_plan,
+                                void *stream) {
   clear_err();
   if (count < 0) return fail(ENC_ERR_INVALID_ARG, "negative count");
   if (!d_table || !aligned16(d_table)) return fail(ENC_ERR_INVALID_ARG, "d_table NULL or unaligned");
+  if (!h_plan) return fail(ENC_ERR_INVALID_ARG, "h_plan is NULL");
+  if (h_plan->d_table != d_table || h_plan->count != count)
+    return fail(ENC_ERR_INVALID_ARG, "the plan was made for another table or count");
   if (count == 0) return ENC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return launched(launch_decode_batch(d_table, s), s, "batch decode launch");
+  return launched(launch_decode_batch(d_table, h_plan->tiles, h_plan->wide_tiles, s), s,
+                  "batch decode launch");
 }
 
 uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size) {

@@ -95,7 +95,9 @@ inline uint64_t onepass_tiles(uint64_t n) { return (tiles_for(n) + onepass_sub(n
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_decode(const DecodeDesc &d, hipStream_t s);
-hipError_t launch_decode_batch(const void *table, hipStream_t s);
+// One workgroup per tile of each list (tiles: BF16 list, wide_tiles: FP16
+// and FP32 list), as recorded in the table when it was prepared.
+hipError_t launch_decode_batch(const void *table, uint64_t tiles, uint64_t wide_tiles, hipStream_t s);
 
 struct EncodeArgs {
   const uint16_t *in;

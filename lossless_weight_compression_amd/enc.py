@@ -55,6 +55,12 @@ class EncItem(ctypes.Structure):
     _fields_ = [("d_comp", ctypes.c_void_p), ("d_out", ctypes.c_void_p), ("info", EncInfo)]
 
 
+class EncBatchPlan(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_uint64), ("wide_tiles", ctypes.c_uint64),
+                ("d_table", ctypes.c_void_p), ("count", ctypes.c_int32),
+                ("reserved", ctypes.c_uint32)]
+
+
 class EncCItem(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_void_p), ("n_elems", ctypes.c_uint64),
                 ("d_out", ctypes.c_void_p), ("out_capacity", ctypes.c_uint64)]
@@ -81,8 +87,9 @@ SIGNATURES = {
     "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
     "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
     "enc_batch_table_bytes": (_U64, [ctypes.c_int]),
-    "enc_batch_prepare": (_ST, [ctypes.POINTER(EncItem), ctypes.c_int, _VP, _U64, _VP]),
-    "enc_decompress_batch": (_ST, [_VP, ctypes.c_int, _VP]),
+    "enc_batch_prepare": (_ST, [ctypes.POINTER(EncItem), ctypes.c_int, _VP, _U64, _VP,
+                                ctypes.POINTER(EncBatchPlan)]),
+    "enc_decompress_batch": (_ST, [_VP, ctypes.c_int, ctypes.POINTER(EncBatchPlan), _VP]),
     "enc_gemm_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
     "enc_decompress_gemm": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP, _U64, _VP]),
     "enc_gemm_dense": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
@@ -303,8 +310,17 @@ def enc_batch_table_bytes(count):
     return int(lib().enc_batch_table_bytes(count))
 
 
+class BatchTable:
+    """A prepared batch: the device table (uint8 CUDA tensor) and the plan
+    (launch sizes) enc_batch_prepare filled for it."""
+
+    def __init__(self, table, plan, count):
+        self.table, self.plan, self.count = table, plan, count
+
+
 def enc_batch_prepare(items, table=None, stream=None):
-    """items: sequence of (comp tensor, EncInfo, out tensor). Returns the device table."""
+    """items: sequence of (comp tensor, EncInfo, out tensor). Returns a
+    BatchTable (table: a device buffer of at least enc_batch_table_bytes)."""
     count = len(items)
     arr = (EncItem * max(count, 1))()
     device = None
@@ -320,12 +336,18 @@ def enc_batch_prepare(items, table=None, stream=None):
     if table is None:
         import torch
         table = _empty_u8(enc_batch_table_bytes(count), device or torch.device("cuda"))
-    _check(lib().enc_batch_prepare(arr, count, _ptr(table), table.numel(), _stream(stream)))
-    return table
+    plan = EncBatchPlan()
+    _check(lib().enc_batch_prepare(arr, count, _ptr(table), table.numel(), _stream(stream),
+                                   ctypes.byref(plan)))
+    return BatchTable(table, plan, count)
 
 
-def enc_decompress_batch(table, count, stream=None):
-    _check(lib().enc_decompress_batch(_ptr(table), count, _stream(stream)))
+def enc_decompress_batch(batch, count=None, stream=None):
+    """Decode every item of a BatchTable (count, if given, must match it)."""
+    if count is None:
+        count = batch.count
+    _check(lib().enc_decompress_batch(_ptr(batch.table), count, ctypes.byref(batch.plan),
+                                      _stream(stream)))
 
 
 def enc_gemm_workspace_bytes(M, K, N, block_size=512):

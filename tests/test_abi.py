@@ -41,6 +41,7 @@ def test_struct_layouts():
     assert ctypes.sizeof(enc.EncInfo) == 96
     assert ctypes.sizeof(enc.EncItem) == 112
     assert ctypes.sizeof(enc.EncCItem) == 32
+    assert ctypes.sizeof(enc.EncBatchPlan) == 32
 
 
 def test_sizes(L):
@@ -134,9 +135,17 @@ def test_host_validation_before_any_launch(L):
     assert L.enc_decompress_gemm(vp(16), 1, 4096, vp(16), ctypes.byref(winfo), 1000, vp(16), vp(16),
                                  1 << 30, vp(0)) == -2
     # batch: negative count, missing table
-    assert L.enc_decompress_batch(vp(16), -1, vp(0)) == -1
-    assert L.enc_decompress_batch(vp(0), 3, vp(0)) == -1
-    assert L.enc_batch_prepare(None, 1, vp(16), 1 << 20, vp(0)) == -1
+    plan = enc.EncBatchPlan()
+    assert L.enc_decompress_batch(vp(16), -1, ctypes.byref(plan), vp(0)) == -1
+    assert L.enc_decompress_batch(vp(0), 3, ctypes.byref(plan), vp(0)) == -1
+    assert L.enc_decompress_batch(vp(16), 3, None, vp(0)) == -1
+    # a plan made for another table or count is refused before any launch
+    plan.d_table, plan.count, plan.tiles = 32, 3, 10
+    assert L.enc_decompress_batch(vp(16), 3, ctypes.byref(plan), vp(0)) == -1
+    assert L.enc_decompress_batch(vp(32), 2, ctypes.byref(plan), vp(0)) == -1
+    assert "another table" in enc.enc_last_error()
+    assert L.enc_batch_prepare(None, 1, vp(16), 1 << 20, vp(0), ctypes.byref(plan)) == -1
+    assert L.enc_batch_prepare(None, 0, vp(16), 1 << 20, vp(0), None) == -1
 
 
 @pytest.mark.parametrize("dtype", [2, 3])
