@@ -35,7 +35,7 @@
 namespace enc {
 namespace {
 
-constexpr uint32_t GPT = kGroupsPerThread;
+constexpr uint32_t GPT = kDecodeGroupsPerThread;
 
 // Decoded output is written once: every 16-byte store is store_nt16.
 __device__ __forceinline__ void store_out16(void *p, uint4 v) { store_nt16(p, v); }
@@ -61,23 +61,24 @@ __device__ __forceinline__ void copy_group_raw(const uint16_t *__restrict__ src,
 }
 
 // RAW stream: the values sit verbatim after the header; copy the tile with
-// all four 16-byte loads of a lane issued before the stores.
+// all of a lane's 16-byte loads issued before the stores.
 __device__ __forceinline__ void copy_tile_raw(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
   const uint16_t *__restrict__ src = reinterpret_cast<const uint16_t *>(d.stream + kHeaderBytes);
   uint16_t *__restrict__ out = static_cast<uint16_t *>(d.out);
-  const uint64_t e_a = tile * kTileElems + (uint64_t)tid * 8;
-  const uint64_t e_b = e_a + 8 * kThreads, e_c = e_b + 8 * kThreads, e_d = e_c + 8 * kThreads;
+  const uint64_t e_first = tile * kDecodeTileElems + (uint64_t)tid * 8;
   const uint4 z = make_uint4(0, 0, 0, 0);
-  const uint4 va = e_a + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_a) : z;
-  const uint4 vb = e_b + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_b) : z;
-  const uint4 vc = e_c + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_c) : z;
-  const uint4 vd = e_d + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e_d) : z;
-  if (e_a < d.n) copy_group_raw(src, out, e_a, d.n, va);
-  if (e_b < d.n) copy_group_raw(src, out, e_b, d.n, vb);
-  if (e_c < d.n) copy_group_raw(src, out, e_c, d.n, vc);
-  if (e_d < d.n) copy_group_raw(src, out, e_d, d.n, vd);
+  uint4 v[GPT];
+#pragma unroll
+  for (uint32_t it = 0; it < GPT; ++it) {
+    const uint64_t e = e_first + (uint64_t)it * 8 * kThreads;
+    v[it] = e + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e) : z;
+  }
+#pragma unroll
+  for (uint32_t it = 0; it < GPT; ++it) {
+    const uint64_t e = e_first + (uint64_t)it * 8 * kThreads;
+    if (e < d.n) copy_group_raw(src, out, e, d.n, v[it]);
+  }
 }
-static_assert(kGroupsPerThread == 4, "copy_tile_raw is written for 4 groups per lane");
 
 // Per-wave scan of the tile's segment: pk (lane j) = block j's base << 24 |
 // width << 20 | payload offset inside the segment, seg_payload = the
@@ -122,7 +123,7 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
   const uint32_t lane = tid & 63;
   const uint32_t log2gpb = d.log2b - 3;       // groups per block
   const uint32_t log2gps = log2gpb + 6;       // groups per segment
-  const uint64_t g0 = tile * kTileGroups;
+  const uint64_t g0 = tile * kDecodeTileGroups;
   const uint64_t seg = g0 >> log2gps;
   const uint32_t gs0 = (uint32_t)(g0 & ((1ull << log2gps) - 1));
 
@@ -197,12 +198,12 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
   const uint8_t *__restrict__ s = d.stream;
   uint8_t *__restrict__ outb = reinterpret_cast<uint8_t *>(d.out);
   const uint64_t n = d.n;
-  const uint64_t g0 = tile * kTileGroups;
+  const uint64_t g0 = tile * kDecodeTileGroups;
   if (d.raw) {
     // the tile's bytes as 16-byte chunks, consecutive lanes on consecutive
     // chunks (every store instruction writes whole lines)
     constexpr uint32_t CPT = GPT * ES / 2;   // chunks per thread
-    const uint64_t b0 = tile * kTileElems * ES, bn = n * ES;
+    const uint64_t b0 = tile * kDecodeTileElems * ES, bn = n * ES;
     for (uint32_t it = 0; it < CPT; ++it) {
       const uint64_t b = b0 + 16 * (uint64_t)(it * kThreads + tid);
       if (b + 16 <= bn)
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_batch_wide(const uint8_t *_
 }  // namespace
 
 hipError_t launch_decode(const DecodeDesc &d, hipStream_t s) {
-  const uint64_t ntiles = tiles_for(d.n);
+  const uint64_t ntiles = decode_tiles_for(d.n);
   for (uint64_t t0 = 0; t0 < ntiles; t0 += kMaxGrid) {
     const dim3 grid((uint32_t)(ntiles - t0 < kMaxGrid ? ntiles - t0 : kMaxGrid));
     if (d.dtype == 2)

@@ -84,6 +84,16 @@ static_assert(sizeof(BatchHeader) == 64, "table header layout");
 constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"
 
 inline uint64_t tiles_for(uint64_t n) { return (n + kTileElems - 1) / kTileElems; }
+// The decoder's work unit: one workgroup decodes kDecodeTileGroups
+// consecutive groups (kDecodeGroupsPerThread per lane). A power of two of at
+// most 1024 groups, so a tile never crosses a segment (64 blocks of at least
+// 16 groups).
+constexpr uint32_t kDecodeGroupsPerThread = 4;
+constexpr uint32_t kDecodeTileGroups = kThreads * kDecodeGroupsPerThread;
+constexpr uint64_t kDecodeTileElems = uint64_t(kDecodeTileGroups) * 8;
+static_assert(kDecodeTileGroups <= 1024 && (kDecodeTileGroups & (kDecodeTileGroups - 1)) == 0,
+              "decode tiles must not cross a segment");
+inline uint64_t decode_tiles_for(uint64_t n) { return (n + kDecodeTileElems - 1) / kDecodeTileElems; }
 
 // The single-pass encoder handles onepass_sub(n) consecutive tiles per
 // workgroup and runs one look-back per workgroup: 4 for large inputs (fewer
