@@ -37,46 +37,80 @@ namespace {
 
 constexpr uint32_t GPT = kDecodeGroupsPerThread;
 
-// Decoded output is written once: every 16-byte store is store_nt16.
-__device__ __forceinline__ void store_out16(void *p, uint4 v) { store_nt16(p, v); }
+// Every access of the stream and the output goes through these byte
+// pointers in the global address space. The batch kernels read their
+// descriptors from the table, and generic pointers loaded from memory made
+// the compiler address the stream with flat instructions; flat loads count
+// against the LDS wait counter as well, so each lane shuffle of the next
+// group waited for all of this group's loads (one group of loads in flight
+// per lane instead of four). With global loads issued on every path the
+// 8B-shaped set decodes in 4.82-4.84 ms instead of 4.89-4.94.
+#define ENC_GLOBAL __attribute__((address_space(1)))
+typedef const ENC_GLOBAL uint8_t *gsrc;
+typedef ENC_GLOBAL uint8_t *gdst;
+
+__device__ __forceinline__ gsrc stream_of(const DecodeDesc &d) { return (gsrc)d.stream; }
+__device__ __forceinline__ gdst output_of(const DecodeDesc &d) { return (gdst)d.out; }
+
+typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
+template <class T>   // scalar types
+__device__ __forceinline__ T ldg(gsrc p) {
+  return *(const ENC_GLOBAL T *)p;
+}
+__device__ __forceinline__ uint2 ldg2(gsrc p) {
+  const u32x2_g v = *(const ENC_GLOBAL u32x2_g *)p;
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ldg4(gsrc p) {
+  const u32x4_nt v = *(const ENC_GLOBAL u32x4_nt *)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <class T>
+__device__ __forceinline__ void stg(gdst p, T v) {
+  *(ENC_GLOBAL T *)p = v;
+}
+
+// Decoded output is written once: 16-byte stores with the non-temporal hint.
+__device__ __forceinline__ void store_out16(gdst p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), (ENC_GLOBAL u32x4_nt *)p);
+}
 
 // Tail group: store only the elements below n (no dynamically indexed array,
-// so nothing is placed in scratch or LDS).
-__device__ __forceinline__ void store_partial(uint16_t *out, uint64_t e0, uint64_t n, uint4 o) {
+// so nothing is placed in scratch or LDS). ob: the output's bytes.
+__device__ __forceinline__ void store_partial(gdst ob, uint64_t e0, uint64_t n, uint4 o) {
 #pragma unroll
   for (uint32_t k = 0; k < 8; ++k) {
     const uint32_t word = k < 2 ? o.x : k < 4 ? o.y : k < 6 ? o.z : o.w;
-    if (e0 + k < n) out[e0 + k] = (uint16_t)(word >> (16 * (k & 1)));
+    if (e0 + k < n) stg<uint16_t>(ob + 2 * (e0 + k), (uint16_t)(word >> (16 * (k & 1))));
   }
 }
 
-__device__ __forceinline__ void copy_group_raw(const uint16_t *__restrict__ src,
-                                               uint16_t *__restrict__ out, uint64_t e0, uint64_t n,
-                                               uint4 v) {
+// src, ob: the RAW values' bytes and the output's bytes.
+__device__ __forceinline__ void copy_group_raw(gsrc src, gdst ob, uint64_t e0, uint64_t n, uint4 v) {
   if (e0 + 8 <= n) {
-    store_out16(out + e0, v);
+    store_out16(ob + 2 * e0, v);
   } else {
-    for (uint64_t e = e0; e < n; ++e) out[e] = src[e];
+    for (uint64_t e = e0; e < n; ++e) stg<uint16_t>(ob + 2 * e, ldg<uint16_t>(src + 2 * e));
   }
 }
 
 // RAW stream: the values sit verbatim after the header; copy the tile with
 // all of a lane's 16-byte loads issued before the stores.
 __device__ __forceinline__ void copy_tile_raw(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
-  const uint16_t *__restrict__ src = reinterpret_cast<const uint16_t *>(d.stream + kHeaderBytes);
-  uint16_t *__restrict__ out = static_cast<uint16_t *>(d.out);
+  const gsrc src = stream_of(d) + kHeaderBytes;
+  const gdst ob = output_of(d);
   const uint64_t e_first = tile * kDecodeTileElems + (uint64_t)tid * 8;
   const uint4 z = make_uint4(0, 0, 0, 0);
   uint4 v[GPT];
 #pragma unroll
   for (uint32_t it = 0; it < GPT; ++it) {
     const uint64_t e = e_first + (uint64_t)it * 8 * kThreads;
-    v[it] = e + 8 <= d.n ? *reinterpret_cast<const uint4 *>(src + e) : z;
+    v[it] = e + 8 <= d.n ? ldg4(src + 2 * e) : z;
   }
 #pragma unroll
   for (uint32_t it = 0; it < GPT; ++it) {
     const uint64_t e = e_first + (uint64_t)it * 8 * kThreads;
-    if (e < d.n) copy_group_raw(src, out, e, d.n, v[it]);
+    if (e < d.n) copy_group_raw(src, ob, e, d.n, v[it]);
   }
 }
 
@@ -85,11 +119,11 @@ __device__ __forceinline__ void copy_tile_raw(const DecodeDesc &d, uint64_t tile
 // segment's payload start in the stream.
 __device__ __forceinline__ void segment_scan(const DecodeDesc &d, uint64_t seg, uint32_t lane,
                                              uint32_t &pk, uint64_t &seg_payload) {
-  const uint8_t *__restrict__ s = d.stream;
+  const gsrc s = stream_of(d);
   const uint64_t n = d.n;
   const uint64_t blk = (seg << 6) + lane;
   uint32_t m = 0;
-  if (blk < d.nb) m = *reinterpret_cast<const uint16_t *>(s + d.meta_off + 2 * blk);
+  if (blk < d.nb) m = ldg<uint16_t>(s + d.meta_off + 2 * blk);
   const uint32_t w = m >> 8;
   const bool wide = __any(w > 8);   // wave-uniform
   const uint32_t L = (blk + 1 == d.nb) ? (uint32_t)(n - ((d.nb - 1) << d.log2b)) : (1u << d.log2b);
@@ -97,7 +131,7 @@ __device__ __forceinline__ void segment_scan(const DecodeDesc &d, uint64_t seg, 
   pk = ((m & 0xFFu) << 24) | ((w & 15u) << 20);
   const uint32_t incl = wave_incl_scan(P, lane);
   pk |= incl - P;   // exclusive offset < 2^18 whenever every width is at most 8
-  const uint64_t seg_rel = *reinterpret_cast<const uint64_t *>(s + d.segoff_off + 8 * seg);
+  const uint64_t seg_rel = ldg<uint64_t>(s + d.segoff_off + 8 * seg);
   seg_payload = d.payload_off + seg_rel;
   // Guard against corrupted streams (checked once per wave, not per group):
   // a width above 8 or a segment whose payload runs past the stream end
@@ -117,8 +151,8 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     copy_tile_raw(d, tile, tid);
     return;
   }
-  const uint8_t *__restrict__ s = d.stream;
-  uint16_t *__restrict__ out = static_cast<uint16_t *>(d.out);
+  const gsrc s = stream_of(d);
+  const gdst ob = output_of(d);
   const uint64_t n = d.n;
   const uint32_t lane = tid & 63;
   const uint32_t log2gpb = d.log2b - 3;       // groups per block
@@ -154,14 +188,15 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     const uint64_t a0 = nbytes ? a : sm_addr;
     const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
     const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
-    if (valid) {
-      const uint2 smv = *reinterpret_cast<const uint2 *>(s + kHeaderBytes + e0);
-      sml[it] = smv.x;
-      smh[it] = smv.y;
-      q0[it] = ld32(s + a0);
-      q1[it] = ld32(s + a1);
-      q2[it] = ld32(s + a2);
-    }
+    // Issued on every path (a group past n reads the plane's first bytes):
+    // a load under a branch made the compiler wait for it at the join,
+    // before the next group's loads went out.
+    const uint2 smv = ldg2(s + sm_addr);
+    sml[it] = smv.x;
+    smh[it] = smv.y;
+    q0[it] = ldg<uint32_t>(s + a0);
+    q1[it] = ldg<uint32_t>(s + a1);
+    q2[it] = ldg<uint32_t>(s + a2);
     info[it] = (p & 0xFFF00000u) | (lead << 3) | (valid << 8);
   }
 
@@ -179,9 +214,9 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     const uint32_t hi = __builtin_amdgcn_alignbit(q2[it], q1[it], sh);
     const uint4 o = join_group(lo, hi, w, base4, sml[it], smh[it]);
     if (valid == 8)
-      store_out16(out + e0, o);
+      store_out16(ob + 2 * e0, o);
     else
-      store_partial(out, e0, n, o);
+      store_partial(ob, e0, n, o);
   }
 }
 
@@ -195,8 +230,8 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
 template <uint32_t DT>
 __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t tile, uint32_t tid) {
   constexpr uint32_t ES = DT == 3 ? 4 : 2;        // element bytes
-  const uint8_t *__restrict__ s = d.stream;
-  uint8_t *__restrict__ outb = reinterpret_cast<uint8_t *>(d.out);
+  const gsrc s = stream_of(d);
+  const gdst outb = output_of(d);
   const uint64_t n = d.n;
   const uint64_t g0 = tile * kDecodeTileGroups;
   if (d.raw) {
@@ -207,9 +242,9 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     for (uint32_t it = 0; it < CPT; ++it) {
       const uint64_t b = b0 + 16 * (uint64_t)(it * kThreads + tid);
       if (b + 16 <= bn)
-        store_out16(outb + b, *reinterpret_cast<const uint4 *>(s + kHeaderBytes + b));
+        store_out16(outb + b, ldg4(s + kHeaderBytes + b));
       else
-        for (uint64_t k = b; k < bn; ++k) outb[k] = s[kHeaderBytes + k];
+        for (uint64_t k = b; k < bn; ++k) stg<uint8_t>(outb + k, ldg<uint8_t>(s + kHeaderBytes + k));
     }
     return;
   }
@@ -246,9 +281,9 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       const uint32_t lead = (uint32_t)(pb & 3);
       if (nbytes) {
         const uint64_t a = pb & ~3ull;
-        q0 = ld32(s + a);
-        if (lead + nbytes > 4) q1 = ld32(s + a + 4);
-        if (lead + nbytes > 8) q2 = ld32(s + a + 8);
+        q0 = ldg<uint32_t>(s + a);
+        if (lead + nbytes > 4) q1 = ldg<uint32_t>(s + a + 4);
+        if (lead + nbytes > 8) q2 = ldg<uint32_t>(s + a + 8);
       }
       uint32_t el, eh;
       codes_to_bytes(__builtin_amdgcn_alignbit(q1, q0, lead * 8), __builtin_amdgcn_alignbit(q2, q1, lead * 8),
@@ -256,22 +291,22 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       const uint32_t eb = (h ? eh : el) + (p >> 24) * 0x01010101u;
       // 12 bytes at 24 g + 12 h (4-aligned; a tail group's read stays in the
       // stream: the metadata sections follow)
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(s + kHeaderBytes + 24 * g + 12 * h);
-      const uint32_t d0 = src[0], d1 = src[1], d2 = src[2];
+      const gsrc src = s + kHeaderBytes + 24 * g + 12 * h;
+      const uint32_t d0 = ldg<uint32_t>(src), d1 = ldg<uint32_t>(src + 4), d2 = ldg<uint32_t>(src + 8);
       const uint32_t f[4] = {d0 & 0xFFFFFFu, __builtin_amdgcn_alignbit(d1, d0, 24) & 0xFFFFFFu,
                              __builtin_amdgcn_alignbit(d2, d1, 16) & 0xFFFFFFu, d2 >> 8};
       uint32_t o[4];
 #pragma unroll
       for (uint32_t k = 0; k < 4; ++k)
         o[k] = ((f[k] >> 23) << 31) | (((eb >> (8 * k)) & 0xFFu) << 23) | (f[k] & 0x7FFFFFu);
-      uint32_t *dst = reinterpret_cast<uint32_t *>(outb) + e0;
+      const gdst dst = outb + 4 * e0;
       const uint64_t rem = n - e0;
       if (rem >= 4) {
         store_out16(dst, make_uint4(o[0], o[1], o[2], o[3]));
       } else {
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k)
-          if (k < rem) dst[k] = o[k];
+          if (k < rem) stg<uint32_t>(dst + 4 * k, o[k]);
       }
     }
     return;
@@ -295,9 +330,9 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     const uint32_t lead = (uint32_t)(pb & 3);
     if (nbytes) {
       const uint64_t a = pb & ~3ull;
-      q0 = ld32(s + a);
-      if (lead + nbytes > 4) q1 = ld32(s + a + 4);
-      if (lead + nbytes > 8) q2 = ld32(s + a + 8);
+      q0 = ldg<uint32_t>(s + a);
+      if (lead + nbytes > 4) q1 = ldg<uint32_t>(s + a + 4);
+      if (lead + nbytes > 8) q2 = ldg<uint32_t>(s + a + 8);
     }
     const uint32_t lo = __builtin_amdgcn_alignbit(q1, q0, lead * 8);
     const uint32_t hi = __builtin_amdgcn_alignbit(q2, q1, lead * 8);
@@ -316,8 +351,8 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       // 24-bit fields of 8 values: 24 bytes at 24 g (8-aligned). A tail
       // group reads past the section's last field, never past the stream:
       // the metadata and offset sections (256-byte aligned) follow.
-      const uint2 *src = reinterpret_cast<const uint2 *>(s + kHeaderBytes + 24 * g);
-      const uint2 v0 = src[0], v1 = src[1], v2 = src[2];
+      const gsrc src = s + kHeaderBytes + 24 * g;
+      const uint2 v0 = ldg2(src), v1 = ldg2(src + 8), v2 = ldg2(src + 16);
       const uint32_t dw[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
       sm[0] = dw[0] & 0xFFFFFFu;
       sm[1] = __builtin_amdgcn_alignbit(dw[1], dw[0], 24) & 0xFFFFFFu;
@@ -330,23 +365,24 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       uint32_t o[8];
 #pragma unroll
       for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 23) << 31) | (e[k] << 23) | (sm[k] & 0x7FFFFFu);
-      uint32_t *dst = reinterpret_cast<uint32_t *>(outb) + e0;
+      const gdst dst = outb + 4 * e0;
       if (valid == 8) {
         store_out16(dst, make_uint4(o[0], o[1], o[2], o[3]));
-        store_out16(dst + 4, make_uint4(o[4], o[5], o[6], o[7]));
+        store_out16(dst + 16, make_uint4(o[4], o[5], o[6], o[7]));
       } else {
 #pragma unroll
         for (uint32_t k = 0; k < 8; ++k)
-          if (k < valid) dst[k] = o[k];
+          if (k < valid) stg<uint32_t>(dst + 4 * k, o[k]);
       }
     } else {
       // 11-bit fields of 8 values: 11 bytes at 11 g (any alignment), read as
       // the 16-byte aligned-dword window that covers them (in the stream for
       // the same reason as above)
       const uint64_t b0 = kHeaderBytes + 11 * g;
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(s + (b0 & ~3ull));
+      const gsrc src = s + (b0 & ~3ull);
       const uint32_t sh = (uint32_t)(b0 & 3) * 8;
-      const uint32_t dw[4] = {src[0], src[1], src[2], src[3]};
+      const uint32_t dw[4] = {ldg<uint32_t>(src), ldg<uint32_t>(src + 4), ldg<uint32_t>(src + 8),
+                              ldg<uint32_t>(src + 12)};
       const uint32_t f0 = __builtin_amdgcn_alignbit(dw[1], dw[0], sh);
       const uint32_t f1 = __builtin_amdgcn_alignbit(dw[2], dw[1], sh);
       const uint32_t f2 = __builtin_amdgcn_alignbit(dw[3], dw[2], sh);
@@ -362,14 +398,14 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       uint32_t o[8];
 #pragma unroll
       for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 10) << 15) | ((e[k] & 0x1Fu) << 10) | (sm[k] & 0x3FFu);
-      uint16_t *dst = reinterpret_cast<uint16_t *>(outb) + e0;
+      const gdst dst = outb + 2 * e0;
       if (valid == 8) {
         store_out16(dst, make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16,
                                     o[6] | o[7] << 16));
       } else {
 #pragma unroll
         for (uint32_t k = 0; k < 8; ++k)
-          if (k < valid) dst[k] = (uint16_t)o[k];
+          if (k < valid) stg<uint16_t>(dst + 2 * k, (uint16_t)o[k]);
       }
     }
   }
