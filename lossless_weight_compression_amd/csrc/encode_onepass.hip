@@ -73,13 +73,24 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
   return v;
 }
 
-__device__ __forceinline__ void publish(uint64_t *status, uint64_t tile, uint64_t word) {
+// Status words, the size slot, the error word and the segment offsets are
+// addressed through global-address-space pointers. In the batched kernel
+// the arguments come from a table in memory, and the compiler would
+// otherwise reach them with flat instructions, which count against the LDS
+// wait counter as well: the early read of the first look-back window would
+// then hold up every LDS wait of the last sub-tile's pack instead of
+// overlapping it.
+#define ENC_GLOBAL __attribute__((address_space(1)))
+typedef ENC_GLOBAL uint64_t gu64;
+typedef ENC_GLOBAL uint32_t gu32;
+
+__device__ __forceinline__ void publish(gu64 *status, uint64_t tile, uint64_t word) {
   __hip_atomic_store(status + tile, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Lane l's status word of the window whose top is tile `top` (positions
 // below tile 0 read as a full prefix of 0).
-__device__ __forceinline__ uint64_t window_word(const uint64_t *status, int64_t top, uint32_t lane) {
+__device__ __forceinline__ uint64_t window_word(gu64 *status, int64_t top, uint32_t lane) {
   const int64_t idx = top - (int64_t)lane;
   return idx >= 0 ? __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                   : kFlagPre;
@@ -90,7 +101,7 @@ __device__ __forceinline__ uint64_t window_word(const uint64_t *status, int64_t 
 // to the nearest full prefix has published; otherwise the wave sleeps
 // briefly and reads it again. `first` is the caller's read of the first
 // window (top = tile - 1), issued early so that its latency overlaps work.
-__device__ uint64_t look_back(uint64_t *status, uint64_t tile, uint32_t lane, uint32_t *error,
+__device__ uint64_t look_back(gu64 *status, uint64_t tile, uint32_t lane, gu32 *error,
                               uint32_t spin_limit, uint64_t first) {
   uint64_t excl = 0;
   int64_t top = (int64_t)tile - 1;
@@ -103,7 +114,7 @@ __device__ uint64_t look_back(uint64_t *status, uint64_t tile, uint32_t lane, ui
     const uint64_t need = pre ? ((pre & (~pre + 1)) << 1) - 1 : ~0ull;   // lanes up to the first prefix
     if (none & need) {
       if (++spins > spin_limit) {
-        if (lane == 0) atomicOr(error, 1u);
+        if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return 0;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -227,7 +238,8 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
   // sign+mantissa plane of the tile, up to the 8-value boundary (the plane's
   // padding is zero, and so are the masked bytes of a short last group)
   const __amdgpu_buffer_rsrc_t sm_rs = range_rsrc(a.out + kHeaderBytes + start, align_up(span_vals, 8));
-  const uint32_t x_last = a.in[n - 1];
+  const uint32_t x_last = *(const ENC_GLOBAL uint16_t *)(a.in + n - 1);
+  gu64 *const status = (gu64 *)a.status;
 
   if (tid < 64) {
     smin[tid] = 255;
@@ -300,8 +312,8 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
         // the workgroup's payload total is known: publish it and read the
         // first look-back window now, so that the read is in flight while
         // the last sub-tile is packed
-        if (lane == 0) publish(a.status, tile, (tile == 0 ? kFlagPre : kFlagAgg) | (run + sub_total));
-        lb_first = window_word(a.status, (int64_t)tile - 1, lane);
+        if (lane == 0) publish(status, tile, (tile == 0 ? kFlagPre : kFlagAgg) | (run + sub_total));
+        lb_first = window_word(status, (int64_t)tile - 1, lane);
       }
     }
     lds_barrier();
@@ -350,14 +362,14 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
   // the workgroup's payload offset
   if (wave == 0) {
     const uint32_t agg = s_run;
-    const uint64_t excl = look_back(a.status, tile, lane, a.error, a.spin_limit, lb_first);
+    const uint64_t excl = look_back(status, tile, lane, (gu32 *)a.error, a.spin_limit, lb_first);
     if (lane == 0) {
-      if (tile > 0) publish(a.status, tile, kFlagPre | (excl + agg));
-      if (tile + 1 == a.ntiles) *a.ws_total = excl + agg;
+      if (tile > 0) publish(status, tile, kFlagPre | (excl + agg));
+      if (tile + 1 == a.ntiles) *(gu64 *)a.ws_total = excl + agg;
       s_excl = excl;
     }
     if (lane < nsub && (((tile * SUB + lane) * bps) & 63) == 0)   // segment starts
-      *reinterpret_cast<uint64_t *>(a.out + a.segoff_off +
+      *(gu64 *)(a.out + a.segoff_off +
                                     8 * (((tile * SUB + lane) * bps) >> 6)) = excl + s_suboff[lane];
   }
   lds_barrier();
