@@ -7,11 +7,12 @@
 // Abstract: a fixed-length format decodes in constant time and in parallel.
 //
 // Mapping onto CDNA4 (wave64, 256 CUs in 8 XCDs):
-//  * a workgroup (4 waves) decodes one tile of 1024 groups = 8192 values;
-//    lane t owns groups t, t+256, t+512, t+768 of the tile, so every wave
-//    instruction touches 64 consecutive groups: 512 contiguous bytes of the
-//    sign+mantissa plane, one contiguous run of packed codes, and 1 KiB of
-//    contiguous output (one 16-byte store per lane);
+//  * a workgroup (4 waves) decodes one tile of 512 groups = 4096 BF16
+//    values (1024 groups for FP16 / FP32); lane t owns groups t and t+256 of
+//    the tile, so every wave instruction touches 64 consecutive groups: 512
+//    contiguous bytes of the sign+mantissa plane, one contiguous run of
+//    packed codes, and 1 KiB of contiguous output (one 16-byte store per
+//    lane);
 //  * each wave re-derives the payload offsets of the tile's 64-block segment
 //    itself: lane j reads block j's {base, width}, computes the padded payload
 //    size and a wave64 inclusive scan gives every block's start -- no
@@ -23,7 +24,7 @@
 //    stream never carries out of a byte), and v_bfi/v_perm interleave them
 //    with the sign+mantissa bytes into four BF16 pairs;
 //  * every load of a tile's groups is issued before any of them is decoded,
-//    so each lane keeps 4 groups of reads in flight;
+//    so each lane keeps its groups' reads in flight together;
 //  * one workgroup per tile, in tile order (workgroup b decodes tile
 //    tile0 + b): the resident workgroups then cover one contiguous window of
 //    the stream and of the output that sweeps through memory as a single
@@ -35,7 +36,8 @@
 namespace enc {
 namespace {
 
-constexpr uint32_t GPT = kDecodeGroupsPerThread;
+constexpr uint32_t GPT = kDecodeGroupsPerThread;        // BF16 tiles
+constexpr uint32_t WGPT = kWideDecodeGroupsPerThread;   // FP16 / FP32 tiles
 
 // Every access of the stream and the output goes through these byte
 // pointers in the global address space. The batch kernels read their
@@ -233,12 +235,12 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
   const gsrc s = stream_of(d);
   const gdst outb = output_of(d);
   const uint64_t n = d.n;
-  const uint64_t g0 = tile * kDecodeTileGroups;
+  const uint64_t g0 = tile * kWideDecodeTileGroups;
   if (d.raw) {
     // the tile's bytes as 16-byte chunks, consecutive lanes on consecutive
     // chunks (every store instruction writes whole lines)
-    constexpr uint32_t CPT = GPT * ES / 2;   // chunks per thread
-    const uint64_t b0 = tile * kDecodeTileElems * ES, bn = n * ES;
+    constexpr uint32_t CPT = WGPT * ES / 2;   // chunks per thread
+    const uint64_t b0 = tile * kWideDecodeTileElems * ES, bn = n * ES;
     for (uint32_t it = 0; it < CPT; ++it) {
       const uint64_t b = b0 + 16 * (uint64_t)(it * kThreads + tid);
       if (b + 16 <= bn)
@@ -263,7 +265,7 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     // every store instruction wrote half of each line it touched (a batch
     // of 28 FP32 tensors: 1.72 ms that way, 1.48 ms this way).
 #pragma unroll 2   // fully unrolled, the loop's registers cost the FP16 path occupancy
-    for (uint32_t it = 0; it < 2 * GPT; ++it) {
+    for (uint32_t it = 0; it < 2 * WGPT; ++it) {
       const uint32_t hq = it * kThreads + tid;
       const uint32_t q = hq >> 1, h = hq & 1;
       const uint64_t g = g0 + q;
@@ -313,7 +315,7 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
   }
 
 #pragma unroll
-  for (uint32_t it = 0; it < GPT; ++it) {
+  for (uint32_t it = 0; it < WGPT; ++it) {
     const uint32_t q = it * kThreads + tid;
     const uint64_t g = g0 + q;
     const uint64_t e0 = g * 8;
@@ -415,8 +417,9 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
 // at most kMaxGrid workgroups (larger inputs take several launches). The
 // hardware dispatches workgroups in index order, round-robin over the XCDs,
 // so the resident ones decode consecutive tiles and the whole device
-// streams one contiguous region at a time. Measured on the 8B-shaped set:
-// 4.88 ms per decode, against 5.47 ms with a persistent grid of 65536
+// streams one contiguous region at a time. Measured on the 8B-shaped set
+// with 8192-value tiles: 4.88 ms per decode, against 5.47 ms with a
+// persistent grid of 65536
 // workgroups that gave each XCD a contiguous eighth of the tiles (each XCD
 // then streamed its own region, eight fronts at once), 5.26 ms for that
 // split with one tile per workgroup, and 5.9-6.5 ms with a persistent grid
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_batch_wide(const uint8_t *_
 }  // namespace
 
 hipError_t launch_decode(const DecodeDesc &d, hipStream_t s) {
-  const uint64_t ntiles = decode_tiles_for(d.n);
+  const uint64_t ntiles = decode_tiles_for(d.n, d.dtype);
   for (uint64_t t0 = 0; t0 < ntiles; t0 += kMaxGrid) {
     const dim3 grid((uint32_t)(ntiles - t0 < kMaxGrid ? ntiles - t0 : kMaxGrid));
     if (d.dtype == 2)

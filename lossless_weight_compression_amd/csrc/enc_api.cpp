@@ -783,7 +783,7 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
     descs[k] = desc_of(it.d_comp, it.info, it.d_out);
     tiles[k] = t;
     wide[k] = tw;
-    (it.info.dtype == 1 ? t : tw) += decode_tiles_for(it.info.n_elems);
+    (it.info.dtype == 1 ? t : tw) += decode_tiles_for(it.info.n_elems, it.info.dtype);
   }
   tiles[count] = t;
   wide[count] = tw;

@@ -84,16 +84,27 @@ static_assert(sizeof(BatchHeader) == 64, "table header layout");
 constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"
 
 inline uint64_t tiles_for(uint64_t n) { return (n + kTileElems - 1) / kTileElems; }
-// The decoder's work unit: one workgroup decodes kDecodeTileGroups
-// consecutive groups (kDecodeGroupsPerThread per lane). A power of two of at
-// most 1024 groups, so a tile never crosses a segment (64 blocks of at least
-// 16 groups).
-constexpr uint32_t kDecodeGroupsPerThread = 4;
+// The decoder's work unit: one workgroup decodes a tile of consecutive
+// groups, kDecodeGroupsPerThread per lane for BF16 streams (4096 values)
+// and kWideDecodeGroupsPerThread per lane for FP16 / FP32 streams (8192
+// values). Each is a power of two of at most 1024 groups, so a tile never
+// crosses a segment (64 blocks of at least 16 groups).
+constexpr uint32_t kDecodeGroupsPerThread = 2;
 constexpr uint32_t kDecodeTileGroups = kThreads * kDecodeGroupsPerThread;
 constexpr uint64_t kDecodeTileElems = uint64_t(kDecodeTileGroups) * 8;
+constexpr uint32_t kWideDecodeGroupsPerThread = 4;
+constexpr uint32_t kWideDecodeTileGroups = kThreads * kWideDecodeGroupsPerThread;
+constexpr uint64_t kWideDecodeTileElems = uint64_t(kWideDecodeTileGroups) * 8;
 static_assert(kDecodeTileGroups <= 1024 && (kDecodeTileGroups & (kDecodeTileGroups - 1)) == 0,
               "decode tiles must not cross a segment");
-inline uint64_t decode_tiles_for(uint64_t n) { return (n + kDecodeTileElems - 1) / kDecodeTileElems; }
+static_assert(kWideDecodeTileGroups <= 1024 &&
+                  (kWideDecodeTileGroups & (kWideDecodeTileGroups - 1)) == 0,
+              "decode tiles must not cross a segment");
+// Decode tiles of an n-value stream of the given dtype (1 BF16, else wide).
+inline uint64_t decode_tiles_for(uint64_t n, uint32_t dtype) {
+  const uint64_t t = dtype == 1 ? kDecodeTileElems : kWideDecodeTileElems;
+  return (n + t - 1) / t;
+}
 
 // The single-pass encoder handles onepass_sub(n) consecutive tiles per
 // workgroup and runs one look-back per workgroup: 4 for large inputs (fewer
