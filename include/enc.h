@@ -206,12 +206,12 @@ typedef struct enc_item {
 uint64_t enc_batch_table_bytes(int count);
 
 /* Launch sizes of a prepared batch, filled by enc_batch_prepare: the decoder
- * runs one workgroup per tile (4096 values of a BF16 stream, 8192 of an FP16
- * or FP32 one), and the grid size has to be known on the host when the
+ * runs one workgroup per tile (4096 values of a BF16 or FP32 stream, 8192
+ * of an FP16 one), and the grid size has to be known on the host when the
  * kernel is launched. */
 typedef struct enc_batch_plan {
-  uint64_t tiles;      /* 4096-value tiles of the BF16 items */
-  uint64_t wide_tiles; /* 8192-value tiles of the FP16 and FP32 items */
+  uint64_t tiles;      /* tiles of the BF16 items */
+  uint64_t wide_tiles; /* tiles of the FP16 and FP32 items */
   const void *d_table; /* the table the plan belongs to */
   int32_t count;       /* its item count */
   uint32_t reserved;

@@ -8,7 +8,7 @@
 //
 // Mapping onto CDNA4 (wave64, 256 CUs in 8 XCDs):
 //  * a workgroup (4 waves) decodes one tile of 512 groups = 4096 BF16
-//    values (1024 groups for FP16 / FP32); lane t owns groups t and t+256 of
+//    values (512 for FP32, 1024 for FP16); lane t owns groups t and t+256 of
 //    the tile, so every wave instruction touches 64 consecutive groups: 512
 //    contiguous bytes of the sign+mantissa plane, one contiguous run of
 //    packed codes, and 1 KiB of contiguous output (one 16-byte store per
@@ -36,8 +36,9 @@
 namespace enc {
 namespace {
 
-constexpr uint32_t GPT = kDecodeGroupsPerThread;        // BF16 tiles
-constexpr uint32_t WGPT = kWideDecodeGroupsPerThread;   // FP16 / FP32 tiles
+constexpr uint32_t GPT = decode_groups_per_thread(1);   // BF16 tiles
+constexpr uint32_t kDecodeTileGroups = decode_tile_groups(1);
+constexpr uint64_t kDecodeTileElems = 8ull * kDecodeTileGroups;
 
 // Every access of the stream and the output goes through these byte
 // pointers in the global address space. The batch kernels read their
@@ -235,12 +236,13 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
   const gsrc s = stream_of(d);
   const gdst outb = output_of(d);
   const uint64_t n = d.n;
-  const uint64_t g0 = tile * kWideDecodeTileGroups;
+  constexpr uint32_t WGPT = decode_groups_per_thread(DT);
+  const uint64_t g0 = tile * decode_tile_groups(DT);
   if (d.raw) {
     // the tile's bytes as 16-byte chunks, consecutive lanes on consecutive
     // chunks (every store instruction writes whole lines)
     constexpr uint32_t CPT = WGPT * ES / 2;   // chunks per thread
-    const uint64_t b0 = tile * kWideDecodeTileElems * ES, bn = n * ES;
+    const uint64_t b0 = tile * 8ull * decode_tile_groups(DT) * ES, bn = n * ES;
     for (uint32_t it = 0; it < CPT; ++it) {
       const uint64_t b = b0 + 16 * (uint64_t)(it * kThreads + tid);
       if (b + 16 <= bn)

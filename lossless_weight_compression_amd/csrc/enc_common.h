@@ -85,24 +85,22 @@ constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"
 
 inline uint64_t tiles_for(uint64_t n) { return (n + kTileElems - 1) / kTileElems; }
 // The decoder's work unit: one workgroup decodes a tile of consecutive
-// groups, kDecodeGroupsPerThread per lane for BF16 streams (4096 values)
-// and kWideDecodeGroupsPerThread per lane for FP16 / FP32 streams (8192
-// values). Each is a power of two of at most 1024 groups, so a tile never
-// crosses a segment (64 blocks of at least 16 groups).
-constexpr uint32_t kDecodeGroupsPerThread = 2;
-constexpr uint32_t kDecodeTileGroups = kThreads * kDecodeGroupsPerThread;
-constexpr uint64_t kDecodeTileElems = uint64_t(kDecodeTileGroups) * 8;
-constexpr uint32_t kWideDecodeGroupsPerThread = 4;
-constexpr uint32_t kWideDecodeTileGroups = kThreads * kWideDecodeGroupsPerThread;
-constexpr uint64_t kWideDecodeTileElems = uint64_t(kWideDecodeTileGroups) * 8;
-static_assert(kDecodeTileGroups <= 1024 && (kDecodeTileGroups & (kDecodeTileGroups - 1)) == 0,
+// groups, decode_groups_per_thread(dtype) per lane: 2 for BF16 and FP32
+// (4096 values), 4 for FP16 (8192). Each tile is a power of two of at most
+// 1024 groups, so it never crosses a segment (64 blocks of at least 16
+// groups).
+__host__ __device__ constexpr uint32_t decode_groups_per_thread(uint32_t dtype) {
+  return dtype == 2 ? 4u : 2u;
+}
+__host__ __device__ constexpr uint32_t decode_tile_groups(uint32_t dtype) {
+  return kThreads * decode_groups_per_thread(dtype);
+}
+static_assert(decode_tile_groups(1) <= 1024 && decode_tile_groups(2) <= 1024 &&
+                  decode_tile_groups(3) <= 1024,
               "decode tiles must not cross a segment");
-static_assert(kWideDecodeTileGroups <= 1024 &&
-                  (kWideDecodeTileGroups & (kWideDecodeTileGroups - 1)) == 0,
-              "decode tiles must not cross a segment");
-// Decode tiles of an n-value stream of the given dtype (1 BF16, else wide).
+// Decode tiles of an n-value stream of the given dtype.
 inline uint64_t decode_tiles_for(uint64_t n, uint32_t dtype) {
-  const uint64_t t = dtype == 1 ? kDecodeTileElems : kWideDecodeTileElems;
+  const uint64_t t = 8ull * decode_tile_groups(dtype);
   return (n + t - 1) / t;
 }
 
