@@ -316,6 +316,10 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     return;
   }
 
+  // FP16: every load of the lane's groups first (addresses clamped in
+  // bounds, no branch), then decode and store, as in the BF16 tile: loads
+  // under a branch made the compiler wait for them at the join.
+  uint32_t q0[WGPT], q1[WGPT], q2[WGPT], fw[WGPT][4], info[WGPT];
 #pragma unroll
   for (uint32_t it = 0; it < WGPT; ++it) {
     const uint32_t q = it * kThreads + tid;
@@ -323,94 +327,71 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     const uint64_t e0 = g * 8;
     const uint32_t gs = gs0 + q;
     const uint32_t p = __shfl(pk, (int)(gs >> log2gpb), 64);   // with every lane active
-    if (e0 >= n) continue;
     const uint32_t u = gs & ((1u << log2gpb) - 1);
     const uint32_t w = (p >> 20) & 15u;
-    const uint64_t rem = n - e0;
+    const uint64_t rem = e0 < n ? n - e0 : 0;
     const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
     const uint32_t nbytes = (valid * w + 7) >> 3;
     const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
-    uint32_t q0 = 0, q1 = 0, q2 = 0;
+    const uint64_t a = pb & ~3ull;
     const uint32_t lead = (uint32_t)(pb & 3);
-    if (nbytes) {
-      const uint64_t a = pb & ~3ull;
-      q0 = ldg<uint32_t>(s + a);
-      if (lead + nbytes > 4) q1 = ldg<uint32_t>(s + a + 4);
-      if (lead + nbytes > 8) q2 = ldg<uint32_t>(s + a + 8);
-    }
-    const uint32_t lo = __builtin_amdgcn_alignbit(q1, q0, lead * 8);
-    const uint32_t hi = __builtin_amdgcn_alignbit(q2, q1, lead * 8);
+    // 11-bit fields of 8 values: 11 bytes at 11 g (any alignment), read as
+    // the 16-byte aligned-dword window that covers them (a tail group's
+    // window stays in the stream: the metadata sections follow; a group past
+    // n reads group 0's)
+    const uint64_t b0 = kHeaderBytes + 11 * (valid ? g : 0);
+    const uint64_t fa = b0 & ~3ull;
+    const uint64_t a0 = nbytes ? a : fa;
+    const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
+    const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
+    q0[it] = ldg<uint32_t>(s + a0);
+    q1[it] = ldg<uint32_t>(s + a1);
+    q2[it] = ldg<uint32_t>(s + a2);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) fw[it][j] = ldg<uint32_t>(s + fa + 4 * j);
+    info[it] = (p & 0xFFF00000u) | ((uint32_t)(b0 & 3) << 15) | (valid << 8) | (lead << 3);
+  }
+#pragma unroll
+  for (uint32_t it = 0; it < WGPT; ++it) {
+    const uint32_t valid = (info[it] >> 8) & 15u;
+    if (!valid) continue;
+    const uint64_t e0 = (g0 + it * kThreads + tid) * 8;
+    const uint32_t w = (info[it] >> 20) & 15u;
+    const uint32_t lsh = info[it] & 31u;
+    const uint32_t fsh = (info[it] >> 12) & 31u;
+    const uint32_t base4 = (info[it] >> 24) * 0x01010101u;
     uint32_t el, eh;
-    codes_to_bytes(lo, hi, w, el, eh);
-    const uint32_t base4 = (p >> 24) * 0x01010101u;
+    codes_to_bytes(__builtin_amdgcn_alignbit(q1[it], q0[it], lsh),
+                   __builtin_amdgcn_alignbit(q2[it], q1[it], lsh), w, el, eh);
     el += base4;
     eh += base4;
-    uint32_t e[8], sm[8];
+    const uint32_t f0 = __builtin_amdgcn_alignbit(fw[it][1], fw[it][0], fsh);
+    const uint32_t f1 = __builtin_amdgcn_alignbit(fw[it][2], fw[it][1], fsh);
+    const uint32_t f2 = __builtin_amdgcn_alignbit(fw[it][3], fw[it][2], fsh);
+    // field k = bits [11 k, 11 k + 11) of f2:f1:f0
+    uint32_t sm[8];
+    sm[0] = f0 & 0x7FFu;
+    sm[1] = (f0 >> 11) & 0x7FFu;
+    sm[2] = __builtin_amdgcn_alignbit(f1, f0, 22) & 0x7FFu;
+    sm[3] = (f1 >> 1) & 0x7FFu;
+    sm[4] = (f1 >> 12) & 0x7FFu;
+    sm[5] = __builtin_amdgcn_alignbit(f2, f1, 23) & 0x7FFu;
+    sm[6] = (f2 >> 2) & 0x7FFu;
+    sm[7] = (f2 >> 13) & 0x7FFu;
+    uint32_t o[8];
 #pragma unroll
-    for (uint32_t k = 0; k < 4; ++k) {
-      e[k] = (el >> (8 * k)) & 0xFFu;
-      e[k + 4] = (eh >> (8 * k)) & 0xFFu;
+    for (uint32_t k = 0; k < 8; ++k) {
+      const uint32_t e = ((k < 4 ? el : eh) >> (8 * (k & 3))) & 0x1Fu;
+      o[k] = ((sm[k] >> 10) << 15) | (e << 10) | (sm[k] & 0x3FFu);
     }
-    if (DT == 3) {
-      // 24-bit fields of 8 values: 24 bytes at 24 g (8-aligned). A tail
-      // group reads past the section's last field, never past the stream:
-      // the metadata and offset sections (256-byte aligned) follow.
-      const gsrc src = s + kHeaderBytes + 24 * g;
-      const uint2 v0 = ldg2(src), v1 = ldg2(src + 8), v2 = ldg2(src + 16);
-      const uint32_t dw[6] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y};
-      sm[0] = dw[0] & 0xFFFFFFu;
-      sm[1] = __builtin_amdgcn_alignbit(dw[1], dw[0], 24) & 0xFFFFFFu;
-      sm[2] = __builtin_amdgcn_alignbit(dw[2], dw[1], 16) & 0xFFFFFFu;
-      sm[3] = dw[2] >> 8;
-      sm[4] = dw[3] & 0xFFFFFFu;
-      sm[5] = __builtin_amdgcn_alignbit(dw[4], dw[3], 24) & 0xFFFFFFu;
-      sm[6] = __builtin_amdgcn_alignbit(dw[5], dw[4], 16) & 0xFFFFFFu;
-      sm[7] = dw[5] >> 8;
-      uint32_t o[8];
-#pragma unroll
-      for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 23) << 31) | (e[k] << 23) | (sm[k] & 0x7FFFFFu);
-      const gdst dst = outb + 4 * e0;
-      if (valid == 8) {
-        store_out16(dst, make_uint4(o[0], o[1], o[2], o[3]));
-        store_out16(dst + 16, make_uint4(o[4], o[5], o[6], o[7]));
-      } else {
-#pragma unroll
-        for (uint32_t k = 0; k < 8; ++k)
-          if (k < valid) stg<uint32_t>(dst + 4 * k, o[k]);
-      }
+    const gdst dst = outb + 2 * e0;
+    if (valid == 8) {
+      store_out16(dst, make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16,
+                                  o[6] | o[7] << 16));
     } else {
-      // 11-bit fields of 8 values: 11 bytes at 11 g (any alignment), read as
-      // the 16-byte aligned-dword window that covers them (in the stream for
-      // the same reason as above)
-      const uint64_t b0 = kHeaderBytes + 11 * g;
-      const gsrc src = s + (b0 & ~3ull);
-      const uint32_t sh = (uint32_t)(b0 & 3) * 8;
-      const uint32_t dw[4] = {ldg<uint32_t>(src), ldg<uint32_t>(src + 4), ldg<uint32_t>(src + 8),
-                              ldg<uint32_t>(src + 12)};
-      const uint32_t f0 = __builtin_amdgcn_alignbit(dw[1], dw[0], sh);
-      const uint32_t f1 = __builtin_amdgcn_alignbit(dw[2], dw[1], sh);
-      const uint32_t f2 = __builtin_amdgcn_alignbit(dw[3], dw[2], sh);
-      // field k = bits [11 k, 11 k + 11) of f2:f1:f0
-      sm[0] = f0 & 0x7FFu;
-      sm[1] = (f0 >> 11) & 0x7FFu;
-      sm[2] = __builtin_amdgcn_alignbit(f1, f0, 22) & 0x7FFu;
-      sm[3] = (f1 >> 1) & 0x7FFu;
-      sm[4] = (f1 >> 12) & 0x7FFu;
-      sm[5] = __builtin_amdgcn_alignbit(f2, f1, 23) & 0x7FFu;
-      sm[6] = (f2 >> 2) & 0x7FFu;
-      sm[7] = (f2 >> 13) & 0x7FFu;
-      uint32_t o[8];
 #pragma unroll
-      for (uint32_t k = 0; k < 8; ++k) o[k] = ((sm[k] >> 10) << 15) | ((e[k] & 0x1Fu) << 10) | (sm[k] & 0x3FFu);
-      const gdst dst = outb + 2 * e0;
-      if (valid == 8) {
-        store_out16(dst, make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16,
-                                    o[6] | o[7] << 16));
-      } else {
-#pragma unroll
-        for (uint32_t k = 0; k < 8; ++k)
-          if (k < valid) stg<uint16_t>(dst + 2 * k, (uint16_t)o[k]);
-      }
+      for (uint32_t k = 0; k < 8; ++k)
+        if (k < valid) stg<uint16_t>(dst + 2 * k, (uint16_t)o[k]);
     }
   }
 }
