@@ -266,37 +266,54 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     // consecutive 16-byte pieces: with whole groups per lane (32 bytes each)
     // every store instruction wrote half of each line it touched (a batch
     // of 28 FP32 tensors: 1.72 ms that way, 1.48 ms this way).
-#pragma unroll 2   // fully unrolled, the loop's registers cost the FP16 path occupancy
-    for (uint32_t it = 0; it < 2 * WGPT; ++it) {
+    // Every load of the lane's half groups first (addresses clamped in
+    // bounds, no branch), then decode and store.
+    constexpr uint32_t NH = 2 * WGPT;
+    uint32_t q0[NH], q1[NH], q2[NH], fd[NH][3], info[NH];
+#pragma unroll
+    for (uint32_t it = 0; it < NH; ++it) {
       const uint32_t hq = it * kThreads + tid;
       const uint32_t q = hq >> 1, h = hq & 1;
       const uint64_t g = g0 + q;
       const uint64_t e0 = g * 8 + 4 * h;
       const uint32_t gs = gs0 + q;
       const uint32_t p = __shfl(pk, (int)(gs >> log2gpb), 64);   // with every lane active
-      if (e0 >= n) continue;
       const uint32_t u = gs & ((1u << log2gpb) - 1);
       const uint32_t w = (p >> 20) & 15u;
-      const uint64_t remg = n - g * 8;
+      const bool live = e0 < n;
+      const uint64_t remg = live ? n - g * 8 : 0;
       const uint32_t validg = remg < 8 ? (uint32_t)remg : 8u;   // values of the group
       const uint32_t nbytes = (validg * w + 7) >> 3;
       const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
-      uint32_t q0 = 0, q1 = 0, q2 = 0;
+      const uint64_t a = pb & ~3ull;
       const uint32_t lead = (uint32_t)(pb & 3);
-      if (nbytes) {
-        const uint64_t a = pb & ~3ull;
-        q0 = ldg<uint32_t>(s + a);
-        if (lead + nbytes > 4) q1 = ldg<uint32_t>(s + a + 4);
-        if (lead + nbytes > 8) q2 = ldg<uint32_t>(s + a + 8);
-      }
+      // 12 bytes of fields at 24 g + 12 h (4-aligned; a tail group's read
+      // stays in the stream: the metadata sections follow; a half group
+      // past n reads the first one's)
+      const uint64_t fa = kHeaderBytes + (live ? 24 * g + 12 * h : 0);
+      const uint64_t a0 = nbytes ? a : fa;
+      const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
+      const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
+      q0[it] = ldg<uint32_t>(s + a0);
+      q1[it] = ldg<uint32_t>(s + a1);
+      q2[it] = ldg<uint32_t>(s + a2);
+#pragma unroll
+      for (uint32_t j = 0; j < 3; ++j) fd[it][j] = ldg<uint32_t>(s + fa + 4 * j);
+      info[it] = (p & 0xFFF00000u) | ((uint32_t)live << 8) | (lead << 3);
+    }
+#pragma unroll
+    for (uint32_t it = 0; it < NH; ++it) {
+      if (!((info[it] >> 8) & 1u)) continue;
+      const uint32_t hq = it * kThreads + tid;
+      const uint32_t h = hq & 1;
+      const uint64_t e0 = (g0 + (hq >> 1)) * 8 + 4 * h;
+      const uint32_t w = (info[it] >> 20) & 15u;
+      const uint32_t lsh = info[it] & 31u;
       uint32_t el, eh;
-      codes_to_bytes(__builtin_amdgcn_alignbit(q1, q0, lead * 8), __builtin_amdgcn_alignbit(q2, q1, lead * 8),
-                     w, el, eh);
-      const uint32_t eb = (h ? eh : el) + (p >> 24) * 0x01010101u;
-      // 12 bytes at 24 g + 12 h (4-aligned; a tail group's read stays in the
-      // stream: the metadata sections follow)
-      const gsrc src = s + kHeaderBytes + 24 * g + 12 * h;
-      const uint32_t d0 = ldg<uint32_t>(src), d1 = ldg<uint32_t>(src + 4), d2 = ldg<uint32_t>(src + 8);
+      codes_to_bytes(__builtin_amdgcn_alignbit(q1[it], q0[it], lsh),
+                     __builtin_amdgcn_alignbit(q2[it], q1[it], lsh), w, el, eh);
+      const uint32_t eb = (h ? eh : el) + (info[it] >> 24) * 0x01010101u;
+      const uint32_t d0 = fd[it][0], d1 = fd[it][1], d2 = fd[it][2];
       const uint32_t f[4] = {d0 & 0xFFFFFFu, __builtin_amdgcn_alignbit(d1, d0, 24) & 0xFFFFFFu,
                              __builtin_amdgcn_alignbit(d2, d1, 16) & 0xFFFFFFu, d2 >> 8};
       uint32_t o[4];
