@@ -168,8 +168,11 @@ uint64_t enc_compress_batch_workspace_bytes(const enc_citem *h_items, int count,
  * second synchronisation (the host tables live only for the call). Items
  * whose look-back wait gave up are re-encoded with enc_compress_ex. Fills
  * h_infos[k] for each item. Errors: an item's capacity below its RAW size
- * is ENC_ERR_CAPACITY, as is a short workspace; all checks run before any
- * launch. Options as enc_compress_ex. count 0 does nothing. */
+ * is ENC_ERR_CAPACITY, as is a short workspace; all argument checks run
+ * before any launch. A HIP error after the first launch returns
+ * ENC_ERR_HIP, and then the items' outputs and h_infos are unspecified.
+ * Options as enc_compress_ex. count 0 does nothing. Items must not share
+ * output buffers, and the input and output of an item must not overlap. */
 enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t block_size,
                               uint32_t options, void *d_ws, uint64_t ws_bytes, void *stream,
                               enc_info *h_infos);

@@ -228,6 +228,12 @@ def test_batch_mixed_types(E, orc):
         wants.append((dt, x))
     say("wide batch of %d mixed items" % len(items))
     table = E.enc_batch_prepare(items)
+    # launch sizes: one workgroup per tile, 4096 values for BF16 and FP32
+    # streams, 8192 for FP16 ones
+    tile = {1: 4096, 2: 8192, 3: 4096}
+    assert table.plan.tiles == sum(-(-x.size // tile[dt]) for dt, x, _ in cases if dt == 1)
+    assert table.plan.wide_tiles == sum(-(-x.size // tile[dt]) for dt, x, _ in cases if dt != 1)
+    assert table.plan.count == len(items)
     E.enc_decompress_batch(table, len(items))
     torch.cuda.synchronize()
     for (d, info, out), (dt, x) in zip(items, wants):
