@@ -30,6 +30,8 @@
 //    the stream and of the output that sweeps through memory as a single
 //    front; the same kernel body serves the batched decode of a whole
 //    weight set in one launch.
+#include <cstdlib>
+
 #include "enc_common.h"
 #include "group_math.h"
 
@@ -426,6 +428,17 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
 // of 2048-8192 workgroups stepping through the tiles in order.
 constexpr uint32_t kMaxGrid = 1u << 23;
 
+// Workgroups per launch: kMaxGrid, or fewer when ENC_DECODE_MAX_GRID says
+// so (lets tests run the several-launch path on small inputs).
+uint32_t max_grid() {
+  const char *v = getenv("ENC_DECODE_MAX_GRID");
+  if (v && v[0]) {
+    const unsigned long g = strtoul(v, nullptr, 10);
+    if (g >= 1 && g < kMaxGrid) return (uint32_t)g;
+  }
+  return kMaxGrid;
+}
+
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeDesc d, uint64_t tile0, uint64_t ntiles) {
   const uint64_t t = tile0 + blockIdx.x;
   if (t < ntiles) decode_tile(d, t, threadIdx.x);
@@ -488,8 +501,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_batch_wide(const uint8_t *_
 
 hipError_t launch_decode(const DecodeDesc &d, hipStream_t s) {
   const uint64_t ntiles = decode_tiles_for(d.n, d.dtype);
-  for (uint64_t t0 = 0; t0 < ntiles; t0 += kMaxGrid) {
-    const dim3 grid((uint32_t)(ntiles - t0 < kMaxGrid ? ntiles - t0 : kMaxGrid));
+  const uint32_t gmax = max_grid();
+  for (uint64_t t0 = 0; t0 < ntiles; t0 += gmax) {
+    const dim3 grid((uint32_t)(ntiles - t0 < gmax ? ntiles - t0 : gmax));
     if (d.dtype == 2)
       hipLaunchKernelGGL(k_decode_wide<2>, grid, dim3(kThreads), 0, s, d, t0, ntiles);
     else if (d.dtype == 3)
@@ -504,14 +518,15 @@ hipError_t launch_decode(const DecodeDesc &d, hipStream_t s) {
 
 hipError_t launch_decode_batch(const void *table, uint64_t tiles, uint64_t wide_tiles, hipStream_t s) {
   const uint8_t *tb = reinterpret_cast<const uint8_t *>(table);
-  for (uint64_t t0 = 0; t0 < tiles; t0 += kMaxGrid) {
-    const dim3 grid((uint32_t)(tiles - t0 < kMaxGrid ? tiles - t0 : kMaxGrid));
+  const uint32_t gmax = max_grid();
+  for (uint64_t t0 = 0; t0 < tiles; t0 += gmax) {
+    const dim3 grid((uint32_t)(tiles - t0 < gmax ? tiles - t0 : gmax));
     hipLaunchKernelGGL(k_decode_batch, grid, dim3(kThreads), 0, s, tb, t0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  for (uint64_t t0 = 0; t0 < wide_tiles; t0 += kMaxGrid) {
-    const dim3 grid((uint32_t)(wide_tiles - t0 < kMaxGrid ? wide_tiles - t0 : kMaxGrid));
+  for (uint64_t t0 = 0; t0 < wide_tiles; t0 += gmax) {
+    const dim3 grid((uint32_t)(wide_tiles - t0 < gmax ? wide_tiles - t0 : gmax));
     hipLaunchKernelGGL(k_decode_batch_wide, grid, dim3(kThreads), 0, s, tb, t0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -203,10 +203,25 @@ def test_fp16_exponent_ceiling(E, orc):
     assert (chk.kind, chk.index) == want
 
 
-def test_batch_mixed_types(E, orc):
+@pytest.mark.parametrize("max_grid", [None, "7"])
+def test_batch_mixed_types(E, orc, max_grid):
     """One batched launch over BF16, FP16 and FP32 items, coded and RAW, of
     ragged sizes: every output equals the input bits (the streams are the
-    oracle's)."""
+    oracle's). With ENC_DECODE_MAX_GRID=7 every decode is split into launches
+    of at most 7 workgroups (the path inputs past 2^23 tiles take), for the
+    batch and for each item decoded alone."""
+    import os
+    if max_grid is None:
+        _mixed_batch(E, orc, False)
+        return
+    os.environ["ENC_DECODE_MAX_GRID"] = max_grid
+    try:
+        _mixed_batch(E, orc, True)
+    finally:
+        os.environ.pop("ENC_DECODE_MAX_GRID", None)
+
+
+def _mixed_batch(E, orc, also_single):
     rng = np.random.default_rng(31)
     cases = [
         (1, synth.gaussian_bits((300_001,), 0.02, 130, 1), 512),
@@ -240,3 +255,10 @@ def test_batch_mixed_types(E, orc):
         got = out.cpu().numpy()
         got = got.view(np.uint32) if dt == 3 else got.view(np.uint16)
         assert np.array_equal(got, x), (dt, x.size, info.flags)
+    if also_single:
+        for (d, info, out), (dt, x) in zip(items, wants):
+            o2 = E.enc_decompress(d, info)
+            torch.cuda.synchronize()
+            got = o2.cpu().numpy()
+            got = got.view(np.uint32) if dt == 3 else got.view(np.uint16)
+            assert np.array_equal(got, x), ("single", dt, x.size, info.flags)
