@@ -205,8 +205,11 @@ typedef struct enc_item {
   enc_info info;      /* parsed header of d_comp */
 } enc_item;
 
-/* Device bytes of the batch table for `count` items. */
-uint64_t enc_batch_table_bytes(int count);
+/* Device bytes of the batch table for these items: descriptors, tile
+ * prefixes and a 4-byte item index per decoder tile (about 0.001 byte per
+ * value). Reads only info.dtype and info.n_elems of each item. Returns 0
+ * for a negative count or NULL items with count > 0. */
+uint64_t enc_batch_table_bytes(const enc_item *h_items, int count);
 
 /* Launch sizes of a prepared batch, filled by enc_batch_prepare: the decoder
  * runs one workgroup per tile (4096 values of a BF16 or FP32 stream, 8192
@@ -221,9 +224,9 @@ typedef struct enc_batch_plan {
 } enc_batch_plan;
 
 /* Validate the items, write the batch table into d_table (device, at least
- * enc_batch_table_bytes(count) bytes) and fill *h_plan. Synchronous: returns
- * after the table has been copied. The table stays valid while the streams
- * and outputs do. */
+ * enc_batch_table_bytes(h_items, count) bytes) and fill *h_plan.
+ * Synchronous: returns after the table has been copied. The table stays
+ * valid while the streams and outputs do. */
 enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table,
                              uint64_t table_bytes, void *stream, enc_batch_plan *h_plan);
 

@@ -450,22 +450,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_wide(DecodeDesc d, uint64_t
   if (t < ntiles) decode_tile_wide<DT>(d, t, threadIdx.x);
 }
 
-// First item of a tile-prefix list that holds tile t (binary search).
-__device__ __forceinline__ uint32_t item_of(const uint64_t *tile_begin, uint32_t count, uint64_t t) {
-  uint32_t lo = 0, hi = count;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (tile_begin[mid] <= t) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // The table holds two tile-prefix lists: BF16 items' tiles, then FP16 and
 // FP32 items' tiles (an item has tiles in one list only). k_decode_batch
 // covers the first, k_decode_batch_wide the second, each with one
 // workgroup per tile; the host launches each only if its list has tiles.
-// Tiles beyond the table's own count (a launch sized from a stale plan)
-// exit at once.
+// A workgroup reads its item's index from the table's per-tile map (one
+// load; a binary search over the prefixes took eight dependent loads before
+// any stream byte was requested: 4.77-4.90 ms per set decode against
+// 4.67-4.68 with the map). Tiles beyond the table's own count (a launch
+// sized from a stale plan) exit at once.
 __global__ __launch_bounds__(kThreads) void k_decode_batch(const uint8_t *__restrict__ table,
                                                            uint64_t tile0) {
   const BatchHeader *h = reinterpret_cast<const BatchHeader *>(table);
@@ -475,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_batch(const uint8_t *__rest
   const uint32_t count = h->count;
   const uint64_t *tile_begin =
       reinterpret_cast<const uint64_t *>(table + sizeof(BatchHeader) + count * sizeof(DecodeDesc));
-  const uint32_t k = item_of(tile_begin, count, t);
+  const uint32_t k = reinterpret_cast<const uint32_t *>(table + h->map_off)[t];
   const DecodeDesc d = items[k];
   decode_tile(d, t - tile_begin[k], threadIdx.x);
 }
@@ -489,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_batch_wide(const uint8_t *_
   const uint32_t count = h->count;
   const uint64_t *wide_begin = reinterpret_cast<const uint64_t *>(
                                    table + sizeof(BatchHeader) + count * sizeof(DecodeDesc)) + count + 1;
-  const uint32_t k = item_of(wide_begin, count, t);
+  const uint32_t k = reinterpret_cast<const uint32_t *>(table + h->wide_map_off)[t];
   const DecodeDesc d = items[k];
   if (d.dtype == 2)
     decode_tile_wide<2>(d, t - wide_begin[k], threadIdx.x);

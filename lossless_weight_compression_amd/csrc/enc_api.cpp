@@ -353,10 +353,23 @@ BatchEncLayout batch_enc_layout(const enc_citem *items, int count) {
   return b;
 }
 
-uint64_t batch_bytes(int count) {
-  return align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
-                      2 * 8 * ((uint64_t)count + 1),
-                  256);
+// Device layout of a batch table for these items (see BatchHeader).
+struct BatchLayout {
+  uint64_t tiles, wide_tiles, map_off, wide_map_off, total;
+};
+
+BatchLayout batch_layout(const enc_item *items, int count) {
+  BatchLayout b;
+  b.tiles = b.wide_tiles = 0;
+  for (int k = 0; k < count; ++k)
+    (items[k].info.dtype == 1 ? b.tiles : b.wide_tiles) +=
+        decode_tiles_for(items[k].info.n_elems, items[k].info.dtype);
+  b.map_off = align_up(sizeof(BatchHeader) + (uint64_t)count * sizeof(DecodeDesc) +
+                           2 * 8 * ((uint64_t)count + 1),
+                       256);
+  b.wide_map_off = b.map_off + align_up(4 * b.tiles, 256);
+  b.total = b.wide_map_off + align_up(4 * b.wide_tiles, 256);
+  return b;
 }
 
 }  // namespace
@@ -746,7 +759,10 @@ enc_status enc_decompress(const void *d_comp, const enc_info *h_info, void *d_ou
   return launched(launch_decode(desc_of(d_comp, *h_info, d_out), s), s, "decode launch");
 }
 
-uint64_t enc_batch_table_bytes(int count) { return count < 0 ? 0 : batch_bytes(count); }
+uint64_t enc_batch_table_bytes(const enc_item *h_items, int count) {
+  if (count < 0 || (count > 0 && !h_items)) return 0;
+  return batch_layout(h_items, count).total;
+}
 
 enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, uint64_t table_bytes,
                              void *stream, enc_batch_plan *h_plan) {
@@ -755,19 +771,6 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
   if (count > 0 && !h_items) return fail(ENC_ERR_INVALID_ARG, "h_items is NULL");
   if (!h_plan) return fail(ENC_ERR_INVALID_ARG, "h_plan is NULL");
   if (!d_table || !aligned16(d_table)) return fail(ENC_ERR_INVALID_ARG, "d_table NULL or unaligned");
-  const uint64_t need = batch_bytes(count);
-  if (table_bytes < need)
-    return fail(ENC_ERR_CAPACITY, "table needs %llu bytes", (unsigned long long)need);
-  std::vector<uint8_t> host(need, 0);
-  BatchHeader hdr;
-  memset(&hdr, 0, sizeof hdr);
-  hdr.count = (uint32_t)count;
-  hdr.magic = kBatchMagic;
-  DecodeDesc *descs = reinterpret_cast<DecodeDesc *>(host.data() + sizeof(BatchHeader));
-  uint64_t *tiles = reinterpret_cast<uint64_t *>(host.data() + sizeof(BatchHeader) +
-                                                 (uint64_t)count * sizeof(DecodeDesc));
-  uint64_t *wide = tiles + count + 1;   // the FP16 / FP32 items' tile list
-  uint64_t t = 0, tw = 0;
   for (int k = 0; k < count; ++k) {
     const enc_item &it = h_items[k];
     const enc_status st = check_info(&it.info);
@@ -780,15 +783,40 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table, 
       return fail(ENC_ERR_INVALID_ARG, "item %d: NULL pointer", k);
     if (!aligned16(it.d_comp) || !aligned16(it.d_out))
       return fail(ENC_ERR_INVALID_ARG, "item %d: unaligned pointer", k);
+  }
+  const BatchLayout lay = batch_layout(h_items, count);
+  const uint64_t need = lay.total;
+  if (table_bytes < need)
+    return fail(ENC_ERR_CAPACITY, "table needs %llu bytes", (unsigned long long)need);
+  std::vector<uint8_t> host(need, 0);
+  BatchHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.count = (uint32_t)count;
+  hdr.magic = kBatchMagic;
+  DecodeDesc *descs = reinterpret_cast<DecodeDesc *>(host.data() + sizeof(BatchHeader));
+  uint64_t *tiles = reinterpret_cast<uint64_t *>(host.data() + sizeof(BatchHeader) +
+                                                 (uint64_t)count * sizeof(DecodeDesc));
+  uint64_t *wide = tiles + count + 1;   // the FP16 / FP32 items' tile list
+  uint32_t *map = reinterpret_cast<uint32_t *>(host.data() + lay.map_off);
+  uint32_t *wide_map = reinterpret_cast<uint32_t *>(host.data() + lay.wide_map_off);
+  uint64_t t = 0, tw = 0;
+  for (int k = 0; k < count; ++k) {
+    const enc_item &it = h_items[k];
     descs[k] = desc_of(it.d_comp, it.info, it.d_out);
     tiles[k] = t;
     wide[k] = tw;
-    (it.info.dtype == 1 ? t : tw) += decode_tiles_for(it.info.n_elems, it.info.dtype);
+    const uint64_t nt = decode_tiles_for(it.info.n_elems, it.info.dtype);
+    uint64_t &at = it.info.dtype == 1 ? t : tw;
+    uint32_t *m = it.info.dtype == 1 ? map : wide_map;
+    for (uint64_t x = 0; x < nt; ++x) m[at + x] = (uint32_t)k;
+    at += nt;
   }
   tiles[count] = t;
   wide[count] = tw;
   hdr.total_tiles = t;
   hdr.wide_tiles = tw;
+  hdr.map_off = lay.map_off;
+  hdr.wide_map_off = lay.wide_map_off;
   memcpy(host.data(), &hdr, sizeof hdr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(d_table, host.data(), need, hipMemcpyHostToDevice, s);

@@ -72,13 +72,17 @@ static_assert(sizeof(DecodeDesc) == 80, "table entry layout");
 // Batch table in device memory: header, then `count` DecodeDesc, then two
 // lists of `count + 1` u64 tile prefixes (first tile of each item, then the
 // total): over the BF16 items' tiles, then over the FP16 / FP32 items' tiles
-// (an item's tiles count in its own list only).
+// (an item's tiles count in its own list only); then, at map_off and
+// wide_map_off (256-byte aligned), the item index (u32) of every tile of
+// each list, so a workgroup finds its item with one load.
 struct BatchHeader {
   uint64_t total_tiles;   // tiles of BF16 items
   uint32_t count;
   uint32_t magic;
   uint64_t wide_tiles;    // tiles of FP16 and FP32 items
-  uint64_t reserved[5];
+  uint64_t map_off;       // byte offset of the BF16 tiles' item indices
+  uint64_t wide_map_off;  // byte offset of the FP16 / FP32 tiles' item indices
+  uint64_t reserved[3];
 };
 static_assert(sizeof(BatchHeader) == 64, "table header layout");
 constexpr uint32_t kBatchMagic = 0x42434E45u;  // "ENCB"

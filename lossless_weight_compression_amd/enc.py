@@ -86,7 +86,7 @@ SIGNATURES = {
     "enc_parse_header": (_ST, [_VP, _U64, _U64, _INFO_P]),
     "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
     "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
-    "enc_batch_table_bytes": (_U64, [ctypes.c_int]),
+    "enc_batch_table_bytes": (_U64, [ctypes.POINTER(EncItem), ctypes.c_int]),
     "enc_batch_prepare": (_ST, [ctypes.POINTER(EncItem), ctypes.c_int, _VP, _U64, _VP,
                                 ctypes.POINTER(EncBatchPlan)]),
     "enc_decompress_batch": (_ST, [_VP, ctypes.c_int, ctypes.POINTER(EncBatchPlan), _VP]),
@@ -306,8 +306,14 @@ def _check_out(out, info):
         raise ValueError("the output must be contiguous")
 
 
-def enc_batch_table_bytes(count):
-    return int(lib().enc_batch_table_bytes(count))
+def enc_batch_table_bytes(items):
+    """Device bytes of the batch table for items: a sequence of (comp,
+    EncInfo, out) or of EncInfo."""
+    infos = [it if isinstance(it, EncInfo) else it[1] for it in items]
+    arr = (EncItem * max(len(infos), 1))()
+    for k, info in enumerate(infos):
+        arr[k].info = info
+    return int(lib().enc_batch_table_bytes(arr, len(infos)))
 
 
 class BatchTable:
@@ -335,7 +341,7 @@ def enc_batch_prepare(items, table=None, stream=None):
         device = comp.device
     if table is None:
         import torch
-        table = _empty_u8(enc_batch_table_bytes(count), device or torch.device("cuda"))
+        table = _empty_u8(lib().enc_batch_table_bytes(arr, count), device or torch.device("cuda"))
     plan = EncBatchPlan()
     _check(lib().enc_batch_prepare(arr, count, _ptr(table), table.numel(), _stream(stream),
                                    ctypes.byref(plan)))

@@ -54,8 +54,24 @@ def test_sizes(L):
     # A(8 * 128) + slot = 1280
     assert enc.enc_compress_workspace_bytes(1 << 20, 4096) == 1024 + 256
     assert enc.enc_compress_workspace_bytes(1 << 20, 24) == 0
-    assert enc.enc_batch_table_bytes(0) % 256 == 0
-    assert enc.enc_batch_table_bytes(226) >= 64 + 226 * 80 + 227 * 8
+    # batch table: header, descriptors and two prefix lists (256-aligned),
+    # then a u32 item index per decoder tile of each list (4096-value tiles
+    # for BF16 and FP32, 8192 for FP16), each run 256-aligned
+    assert enc.enc_batch_table_bytes([]) == 256
+    infos = []
+    for dt, n in [(1, 10000), (2, 20000), (3, 5000), (1, 1)]:
+        i = enc.EncInfo()
+        i.dtype, i.n_elems = dt, n
+        infos.append(i)
+    head = -(-(64 + 4 * 80 + 2 * 8 * 5) // 256) * 256
+    bf16_tiles = 3 + 1
+    wide_tiles = 3 + 2
+    assert enc.enc_batch_table_bytes(infos) == head + 256 + 256
+    assert enc.enc_batch_table_bytes(infos * 100) == (-(-(64 + 400 * 80 + 2 * 8 * 401) // 256) * 256
+                                                      + -(-4 * 100 * bf16_tiles // 256) * 256
+                                                      + -(-4 * 100 * wide_tiles // 256) * 256)
+    assert enc.lib().enc_batch_table_bytes(None, 1) == 0
+    assert enc.lib().enc_batch_table_bytes(None, -1) == 0
     assert enc.enc_status_string(-4) == "bad stream"
 
 
