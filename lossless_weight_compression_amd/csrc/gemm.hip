@@ -1371,10 +1371,168 @@ hipError_t launch_splitk_reduce(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// M = 1 in the linear-layer layout (W [N, K], y = W . x): a workgroup owns
+// R consecutive rows of W, whose K values give y[n] in full -- no split over
+// K, no partial sums, no second launch. (Written for M up to 4, but from
+// M = 2 on the staged-row MFMA kernel below was faster: on a 14336 x 4096 W,
+// GPU time per call, this kernel 26.2-26.6 / 33.3 / 34.8 / 40.2 us at M = 1
+// / 2 / 3 / 4 against 27.1-30.9 / 27.4 / 27.3 / 27.5 us; 2, 8 or 16 rows per
+// workgroup were no faster than 4 at M = 1.)
+//
+// First the rows' block table: thread j describes block b_first + j (the
+// absolute payload offset through row_block, {base, width}) in LDS; one
+// barrier. Then the R rows' groups are taken as one run: lane t of the
+// workgroup owns groups t, t + 256, ..., so every wave instruction reads 512
+// contiguous sign+mantissa bytes and one contiguous run of codes, and (K
+// being a multiple of 512) all of its 64 groups lie in one row. The loads of
+// kGemvBatch groups per lane are issued before any of them is decoded (raw
+// buffer loads over the stream: out-of-range dwords read 0). A lane
+// multiplies its values with X (fp32 products of BF16 values, fp32 sums, in
+// a fixed order); whenever a wave moves on to the next row, it adds up its
+// lanes' sums (a fixed butterfly) into LDS, and the workgroup adds the four
+// waves' sums in wave order: the result is deterministic.
+// --------------------------------------------------------------------------
+namespace {
+
+constexpr uint32_t kGemvMaxM = 1;
+constexpr uint32_t kGemvMaxK = 65536;
+constexpr uint32_t kGemvRows = 4;                        // rows of W per workgroup
+// groups per lane in flight: their W and X loads all go out before any of
+// them is decoded
+__host__ __device__ constexpr uint32_t gemv_batch(int mm) { return mm <= 2 ? 4 : 2; }
+constexpr uint32_t kGemvMaxBlocks = kGemvRows * (kGemvMaxK / 128) + 1;
+
+template <int MM, bool DENSE>
+__global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
+  constexpr uint32_t R = kGemvRows;
+  __shared__ uint32_t t_off[DENSE ? 1 : kGemvMaxBlocks], t_meta[DENSE ? 1 : kGemvMaxBlocks];
+  __shared__ float red[R][4][MM];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t K = a.K, N = a.N, log2b = a.log2b;
+  const uint32_t n0 = blockIdx.x * R;
+  const uint32_t nrows = N - n0 < R ? N - n0 : R;
+  const uint32_t gpr = K >> 3;                        // groups per row
+  const uint32_t ng = nrows * gpr;                    // groups of the workgroup
+  const uint64_t e0 = (uint64_t)n0 * K;               // first value
+  const uint64_t b_first = e0 >> log2b;
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
+  for (uint32_t i = tid; i < R * 4 * MM; i += 256) (&red[0][0][0])[i] = 0.f;
+  if (!DENSE) {
+    const uint32_t nblk = (uint32_t)(((e0 + (uint64_t)nrows * K - 1) >> log2b) - b_first + 1);
+    for (uint32_t j = tid; j < nblk; j += 256) {
+      uint64_t off, mw;
+      row_block<false>(a, b_first + j, off, mw);
+      uint32_t w = (uint32_t)(mw >> 8) & 0xFFu;
+      if (w > 8) w = 0;   // corrupted stream: decode as width 0 (reads stay bounds-checked)
+      t_off[j] = (uint32_t)off;
+      t_meta[j] = ((uint32_t)mw & 0xFFu) | (w << 8);
+    }
+  }
+  __syncthreads();
+  float acc[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) acc[m] = 0.f;
+  uint32_t cur = (64 * wave) / gpr;                   // this wave's row (uniform)
+  auto flush = [&](uint32_t row) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      float v = acc[m];
+#pragma unroll
+      for (uint32_t d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+      if (lane == 0 && row < R) red[row][wave][m] = v;
+      acc[m] = 0.f;
+    }
+  };
+  constexpr uint32_t NB = gemv_batch(MM);
+  for (uint32_t f0 = 0; f0 < ng; f0 += 256 * NB) {
+    uint4 wv[NB], xs[NB][MM];
+    u32x2 sm[NB];
+    u32x3 qd[NB];
+    uint32_t info[NB];
+#pragma unroll
+    for (uint32_t i = 0; i < NB; ++i) {
+      const uint32_t f = f0 + i * 256 + tid;
+      const uint32_t fc = f < ng ? f : ng - 1;         // loads stay on the rows
+      const uint64_t e = e0 + 8ull * fc;
+      const uint32_t kc = 8 * (fc % gpr);
+#pragma unroll
+      for (int m = 0; m < MM; ++m) xs[i][m] = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)m * K + kc);
+      if (DENSE) {
+        wv[i] = *reinterpret_cast<const uint4 *>(a.wdense + e);
+      } else {
+        const uint32_t j = (uint32_t)((e >> log2b) - b_first);
+        const uint32_t meta = t_meta[j];
+        const uint32_t w = meta >> 8;
+        const uint32_t u = (uint32_t)((e & ((1ull << log2b) - 1)) >> 3);
+        const uint32_t pb = t_off[j] + u * w;
+        sm[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, kHeaderBytes + (uint32_t)e, 0, 0);
+        qd[i] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
+        info[i] = (meta & 0xFFu) | (w << 8) | ((pb & 3u) << 16);
+      }
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < NB; ++i) {
+      const uint32_t fw = f0 + i * 256 + 64 * wave;   // the wave's first group (uniform)
+      if (fw >= ng) break;
+      const uint32_t row = fw / gpr;
+      if (row != cur) {
+        flush(cur);
+        cur = row;
+      }
+      if (!DENSE) {
+        const uint32_t w = (info[i] >> 8) & 15u;
+        const uint32_t sh = ((info[i] >> 16) & 3u) * 8;
+        const uint32_t lo = __builtin_amdgcn_alignbit(qd[i].y, qd[i].x, sh);
+        const uint32_t hi = __builtin_amdgcn_alignbit(qd[i].z, qd[i].y, sh);
+        wv[i] = join_group(lo, hi, w, (info[i] & 0xFFu) * 0x01010101u, sm[i].x, sm[i].y);
+      }
+      const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        const uint32_t xd[4] = {xs[i][m].x, xs[i][m].y, xs[i][m].z, xs[i][m].w};
+        float sum = acc[m];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          sum = fmaf(bf_lo(wd[h]), bf_lo(xd[h]), sum);
+          sum = fmaf(bf_hi(wd[h]), bf_hi(xd[h]), sum);
+        }
+        acc[m] = sum;
+      }
+    }
+  }
+  flush(cur);
+  __syncthreads();
+  if (tid < nrows * MM) {
+    const uint32_t r = tid / MM, m = tid % MM;
+    a.y[(uint64_t)m * N + n0 + r] = ((red[r][0][m] + red[r][1][m]) + red[r][2][m]) + red[r][3][m];
+  }
+}
+
+template <bool DENSE>
+hipError_t launch_gemv_nt(const GemmArgs &a, hipStream_t s) {
+  const dim3 grid((a.N + kGemvRows - 1) / kGemvRows), block(256);
+  static_assert(kGemvMaxM == 1, "one instantiation per M");
+  hipLaunchKernelGGL((k_gemv_nt<1, DENSE>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The GEMV serves M = 1 when K is a multiple of 512 (a wave's 64 groups
+// then lie in one block for every block size), K <= kGemvMaxK, and the
+// stream's offsets fit the 32-bit buffer offsets.
+bool gemv_ok(bool dense, uint32_t M, uint32_t K, uint64_t total) {
+  return M <= kGemvMaxM && K % 512 == 0 && K <= kGemvMaxK && (dense || total < (1ull << 31));
+}
+
 hipError_t launch_gemm_nt(const GemmArgs &a_in, hipStream_t s) {
   GemmArgs a = a_in;
   const bool dense = a.wstream == nullptr;
   hipError_t e;
+  if (gemv_ok(dense, a.M, a.K, a.total))
+    return dense ? launch_gemv_nt<true>(a, s) : launch_gemv_nt<false>(a, s);
   if (ntu_ok(dense, a.K, a.log2b)) {
     gemm_ntu_plan(dense, a.M, a.K, a.N, a.log2b, &a.ksplit, &a.krows);
     e = dense ? launch_ntu<true>(a, s) : launch_ntu<false>(a, s);

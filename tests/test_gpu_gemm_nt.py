@@ -207,3 +207,46 @@ def test_largest_m(E, orc):
     want = bf16_f64(W)[:, ks].T
     assert np.array_equal(run_fused(E, X, comp, info, N), want)
     assert np.array_equal(run_dense(E, X, W), want)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("K,B", [(512, 128), (512, 512), (2048, 256), (4608, 512), (8192, 4096),
+                                 (4096, 1024)])
+def test_gemv_rows(E, orc, M, K, B):
+    """K a multiple of 512, small N: M = 1 runs the workgroup-per-rows GEMV,
+    M = 2..4 the staged-row kernel. Every output within the bound, one-hot
+    rows of X exact, and the dense twin (same kernels, plain loads) within
+    the bound too."""
+    N = 192
+    W = synth.gaussian_bits((N, K), 0.02, 140, K + B, outliers=True)
+    X = synth.gemm_activations(M, K)
+    comp, info = oracle_stream(E, orc, W, B)
+    say("gemv M=%d K=%d B=%d" % (M, K, B))
+    Y, A = oracle_nt(orc, X, W)
+    assert_within(run_fused(E, X, comp, info, N), Y, A, "gemv fused")
+    assert_within(run_dense(E, X, W), Y, A, "gemv dense")
+    # one-hot rows: Y[m, n] = W[n, k_m] exactly
+    ks = [(37 * m + 5) % K for m in range(M)]
+    Xh = np.zeros((M, K), np.uint16)
+    for m, k in enumerate(ks):
+        Xh[m, k] = 0x3F80
+    y = run_fused(E, Xh, comp, info, N)
+    for m, k in enumerate(ks):
+        assert np.array_equal(y[m], bf16_f64(W[:, k])), (m, k)
+
+
+def test_gemv_raw_and_pow2(E, orc):
+    """The M = 1 GEMV on a RAW stream (multiplied from its verbatim values)
+    and on a power-of-two-width stream."""
+    N, K, M = 64, 1024, 1
+    W = synth.random_bits(N * K, 141, 0, 0x4100).reshape(N, K)   # exponents 0..130: width 8, RAW
+    X = synth.gemm_activations(M, K)
+    comp, info = oracle_stream(E, orc, W, 512)
+    assert info.flags == 1
+    Y, A = oracle_nt(orc, X, W)
+    assert_within(run_fused(E, X, comp, info, N), Y, A, "gemv raw")
+    W2 = synth.gaussian_bits((N, K), 0.03, 142, 0)
+    comp2, info2 = oracle_stream(E, orc, W2, 512, pow2=True)
+    assert info2.flags == 2
+    Y2, A2 = oracle_nt(orc, X, W2)
+    assert_within(run_fused(E, X, comp2, info2, N), Y2, A2, "gemv pow2")
