@@ -68,6 +68,12 @@
  *    "0"), the asynchronous entry points synchronise their stream after
  *    launching (except while it is being captured into a graph), so a kernel
  *    fault is returned as ENC_ERR_HIP by the call that caused it.
+ *  - Two more variables exist for tests: ENC_LOOKBACK_SPINS (polls of an
+ *    unpublished tile before the single-pass encoder gives up and the
+ *    two-pass encoder takes over; 0 forces that path) and
+ *    ENC_DECODE_MAX_GRID (workgroups per decode launch, below the default
+ *    2^23, to run the several-launch path on small inputs). Results do not
+ *    depend on either.
  */
 #ifndef ENC_H
 #define ENC_H
