@@ -19,18 +19,10 @@
 // The bytes are exactly those the format definition prescribes (the stream
 // is unique for a given input and block size).
 #include "enc_common.h"
+#include "group_math.h"
 
 namespace enc {
 namespace {
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t d = 1; d < 64; d <<= 1) {
-    uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
 
 __device__ __forceinline__ unsigned long long wave_incl_scan64(unsigned long long v, uint32_t lane) {
 #pragma unroll
@@ -66,11 +58,15 @@ __global__ __launch_bounds__(kThreads) void k_enc_params(EncodeArgs a) {
   const uint32_t log2gpb = a.log2b - 3;
   const uint32_t gps = 1u << (log2gpb + 6);
   const uint64_t gseg = seg * gps;
-  for (uint32_t q = tid; q < gps; q += kThreads) {
+  // Every lane of a wave runs every round (the lane exchanges of span_max16
+  // need them all); lanes past the end hold no value (key 0). The lanes of
+  // one block reduce ((255 - min) << 16 | max) first, so one lane per block
+  // and wave updates LDS (a per-lane atomic on one address serialises).
+  const uint32_t span = log2gpb < 6 ? (1u << log2gpb) : 64u;
+  for (uint32_t q0 = 0; q0 < gps && (gseg + q0) * 8 < a.n; q0 += kThreads) {
+    const uint32_t q = q0 + tid;
     const uint64_t e0 = (gseg + q) * 8;
-    if (e0 >= a.n) break;
-    const uint64_t rem = a.n - e0;
-    const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
+    const uint32_t valid = e0 < a.n ? (a.n - e0 < 8 ? (uint32_t)(a.n - e0) : 8u) : 0u;
     const uint4 g = load_group(a.in, e0, valid);
     const uint32_t words[4] = {g.x, g.y, g.z, g.w};
     uint32_t mn = 255, mx = 0;
@@ -79,8 +75,11 @@ __global__ __launch_bounds__(kThreads) void k_enc_params(EncodeArgs a) {
       mn = e < mn ? e : mn;
       mx = e > mx ? e : mx;
     }
-    atomicMin(&smin[q >> log2gpb], mn);
-    atomicMax(&smax[q >> log2gpb], mx);
+    const uint32_t key = span_max16(((255u - mn) << 16) | mx, span);
+    if ((tid & (span - 1)) == span - 1 && key != 0) {
+      atomicMin(&smin[q >> log2gpb], 255u - (key >> 16));
+      atomicMax(&smax[q >> log2gpb], key & 0xFFFFu);
+    }
   }
   __syncthreads();
   if (tid < kSegBlocks) {
@@ -94,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_params(EncodeArgs a) {
       P = (((w * L + 7) >> 3) + 15) & ~15u;
       *reinterpret_cast<uint16_t *>(a.ws_meta + 2 * blk) = (uint16_t)(base | (w << 8));
     }
-    const uint32_t tot = wave_incl_scan(P, tid);
+    const uint32_t tot = wave_incl_scan(P);
     if (tid == kSegBlocks - 1) a.ws_segsum[seg] = tot;
   }
 }
@@ -140,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_enc_pack(EncodeArgs a, uint64_t nt
       P = (((w * L + 7) >> 3) + 15) & ~15u;
       pk = ((m & 0xFFu) << 24) | (w << 20);
     }
-    const uint32_t incl = wave_incl_scan(P, lane);
+    const uint32_t incl = wave_incl_scan(P);
     pk |= incl - P;
     const uint64_t glast = (g0 + kTileGroups < ngroups ? g0 + kTileGroups : ngroups) - 1;
     const uint32_t jb0 = gs0 >> log2gpb;

@@ -20,7 +20,8 @@
 // result and runs the two-pass encoder.
 // For each 8192-value sub-tile, in turn (the next one's loads in flight):
 //  1. per-block exponent min/max: lanes of one block reduce with packed
-//     16-bit max over shuffles, then one LDS atomic per block and wave;
+//     16-bit max over DPP lane exchanges, then one LDS atomic per block and
+//     wave;
 //  2. wave 0: base, width, padded payload size and offset (inside the
 //     workgroup's payload) of each block; writes the block metas;
 //  3. all lanes: sign+mantissa bytes to the stream, codes into a zeroed LDS
@@ -38,6 +39,7 @@
 // agent-scope relaxed atomics, so no fence is needed; every wait is bounded
 // (on give-up the kernel flags an error and the host falls back).
 #include "encode_batch.h"
+#include "group_math.h"
 
 namespace enc {
 namespace {
@@ -53,19 +55,6 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // the encoder; the 8B-shaped set encodes 2% faster with it).
 constexpr int kStoreNT = 2;
 
-__device__ __forceinline__ uint32_t pmax16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                __builtin_bit_cast(u16x2, b)));
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
 
 __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 #pragma unroll
@@ -220,7 +209,7 @@ __device__ __forceinline__ uint32_t pack4(uint32_t d, uint32_t w) {
 template <uint32_t SUB>
 __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile) {
   constexpr uint32_t kPayBytes = SUB * kTileGroups * 8 + 16;   // a tile's payload, at most
-  __shared__ uint32_t pay[kPayBytes / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t pay[kPayBytes / 4];
   __shared__ uint32_t smin[64], smax[64], sblk[64], s_suboff[SUB];
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_run;
@@ -246,7 +235,8 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
     smax[tid] = 0;
   }
   if (tid == 0) s_run = 0;
-  for (uint32_t i = tid; i < kPayBytes / 4; i += kThreads) pay[i] = 0;
+  for (uint32_t i = tid; i < kPayBytes / 16; i += kThreads)
+    reinterpret_cast<uint4 *>(pay)[i] = make_uint4(0u, 0u, 0u, 0u);
 
   uint64_t lb_first = kFlagPre;   // wave 0: first look-back window, read early
   uint4 g[kGroupsPerThread], gn[kGroupsPerThread];
@@ -270,9 +260,9 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
       uint32_t el, eh;
       exp_bytes(g[it], el, eh);
       uint32_t key = valid[it] ? minmax_key(el, eh) : 0u;   // 0: no valid value here
-      for (uint32_t d = 1; d < span; d <<= 1) key = pmax16(key, __shfl_xor(key, d, 64));
+      key = span_max16(key, span);
       const uint32_t q = it * kThreads + tid;
-      if ((lane & (span - 1)) == 0 && key != 0) {
+      if ((lane & (span - 1)) == span - 1 && key != 0) {
         atomicMin(&smin[q >> log2gpb], 255u - (key >> 16));
         atomicMax(&smax[q >> log2gpb], key & 0xFFFFu);
       }
@@ -301,8 +291,8 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
       smin[lane] = 255;
       smax[lane] = 0;
       const uint32_t run = s_run;
-      const uint32_t incl = wave_incl_scan(P, lane);
-      const uint32_t sub_total = __shfl(incl, 63, 64);
+      const uint32_t incl = wave_incl_scan(P);
+      const uint32_t sub_total = __builtin_amdgcn_readlane(incl, 63);
       sblk[lane] = base | (w << 8) | ((run + incl - P) << 16);
       if (lane == 0) {
         s_suboff[sub] = run;

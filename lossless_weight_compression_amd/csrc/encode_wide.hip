@@ -16,6 +16,7 @@
 // assembled in zeroed LDS images and written out with 16-byte stores) and
 // k_encw_finish (header, metas, offsets, section padding).
 #include "enc_common.h"
+#include "group_math.h"
 
 namespace enc {
 namespace {
@@ -30,15 +31,6 @@ template <>
 struct Wide<3> {   // FP32: s eeeeeeee m x 23
   static constexpr uint32_t kBytes = 4, kSmBits = 24, kShift = 23, kExpMask = 0xFFu;
 };
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
 
 // The `valid` values of the group starting at element e0 (the rest read as 0
 // and are never used).
@@ -95,23 +87,27 @@ __global__ __launch_bounds__(kThreads) void k_encw_params(EncodeArgs a) {
   const uint32_t log2gpb = a.log2b - 3;
   const uint32_t gps = 1u << (log2gpb + 6);
   const uint64_t gseg = seg * gps;
-  for (uint32_t q = tid; q < gps; q += kThreads) {
+  // As in the BF16 parameter pass: whole waves run every round, the lanes of
+  // a block reduce with span_max16, one lane per block and wave updates LDS.
+  const uint32_t span = log2gpb < 6 ? (1u << log2gpb) : 64u;
+  for (uint32_t q0 = 0; q0 < gps && (gseg + q0) * 8 < a.n; q0 += kThreads) {
+    const uint32_t q = q0 + tid;
     const uint64_t e0 = (gseg + q) * 8;
-    if (e0 >= a.n) break;
-    const uint64_t rem = a.n - e0;
-    const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
+    const uint32_t valid = e0 < a.n ? (a.n - e0 < 8 ? (uint32_t)(a.n - e0) : 8u) : 0u;
     uint32_t x[8];
     load_values<DT>(in, e0, valid, x);
     uint32_t mn = 255, mx = 0;
 #pragma unroll
     for (uint32_t k = 0; k < 8; ++k) {
-      if (k >= valid) break;
       const uint32_t e = exponent_of<DT>(x[k]);
-      mn = e < mn ? e : mn;
-      mx = e > mx ? e : mx;
+      mn = k < valid && e < mn ? e : mn;
+      mx = k < valid && e > mx ? e : mx;
     }
-    atomicMin(&smin[q >> log2gpb], mn);
-    atomicMax(&smax[q >> log2gpb], mx);
+    const uint32_t key = span_max16(((255u - mn) << 16) | mx, span);
+    if ((tid & (span - 1)) == span - 1 && key != 0) {
+      atomicMin(&smin[q >> log2gpb], 255u - (key >> 16));
+      atomicMax(&smax[q >> log2gpb], key & 0xFFFFu);
+    }
   }
   __syncthreads();
   if (tid < kSegBlocks) {
@@ -124,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_encw_params(EncodeArgs a) {
       P = (((w * L + 7) >> 3) + 15) & ~15u;
       *reinterpret_cast<uint16_t *>(a.ws_meta + 2 * blk) = (uint16_t)(base | (w << 8));
     }
-    const uint32_t tot = wave_incl_scan(P, tid);
+    const uint32_t tot = wave_incl_scan(P);
     if (tid == kSegBlocks - 1) a.ws_segsum[seg] = tot;
   }
 }
@@ -154,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_encw_pack(EncodeArgs a, uint64_t n
       P = (((w * L + 7) >> 3) + 15) & ~15u;
       pk = ((m & 0xFFu) << 24) | (w << 20);
     }
-    const uint32_t incl = wave_incl_scan(P, lane);
+    const uint32_t incl = wave_incl_scan(P);
     pk |= incl - P;
     const uint64_t glast = (g0 + kTileGroups < ngroups ? g0 + kTileGroups : ngroups) - 1;
     const uint32_t jb0 = gs0 >> log2gpb;

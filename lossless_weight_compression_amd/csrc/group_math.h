@@ -1,5 +1,6 @@
 // group_math.h -- per-lane decode arithmetic of one 8-element group, shared
-// by the decoder and the fused decompress-GEMM (device code only).
+// by the decoder and the fused decompress-GEMM, and the wave scan the
+// decoder, the encoders and the deep check use (device code only).
 //
 // A group's 8 codes of w bits occupy exactly w bytes of its block payload,
 // starting on a byte boundary (8 codes x w bits = w bytes). Packing is LSB
@@ -14,13 +15,46 @@ namespace enc {
 
 constexpr uint32_t kH8 = 0x80808080u;
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
-#pragma unroll
-  for (uint32_t d = 1; d < 64; d <<= 1) {
-    uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active). The
+// lane exchanges are DPP operand modifiers of the adds: shifts by 1, 2, 4
+// and 8 inside each 16-lane row (a lane with no source adds 0), then row
+// 0's total into row 1 and row 2's into row 3 (row broadcast of lane 15),
+// then rows 0-1's total into rows 2 and 3 (row broadcast of lane 31). Six
+// dependent VALU adds; the lane-shuffle form was six dependent LDS permutes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
   return v;
+}
+
+// Lane-wise max of two pairs of 16-bit integers.
+__device__ __forceinline__ uint32_t pmax16(uint32_t a, uint32_t b) {
+  typedef unsigned short h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(h2, a),
+                                                                __builtin_bit_cast(h2, b)));
+}
+
+// Packed 16-bit max of `key` over each aligned run of `span` lanes (16, 32
+// or 64; all lanes active), complete in the run's last lane. The lane
+// exchanges are DPP operand modifiers: quad permutes (pairs, then quads),
+// the half-row and row mirrors (8, then 16 lanes), then the row broadcasts
+// of lane 15 into rows 1 and 3 (32 lanes) and of lane 31 into rows 2 and 3
+// (64). With lane shuffles (LDS permutes) this reduction took 12% of the
+// single-pass encoder's time.
+__device__ __forceinline__ uint32_t span_max16(uint32_t key, uint32_t span) {
+  key = pmax16(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0xB1, 0xF, 0xF, false));
+  key = pmax16(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x4E, 0xF, 0xF, false));
+  key = pmax16(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x141, 0xF, 0xF, false));
+  key = pmax16(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x140, 0xF, 0xF, false));
+  if (span >= 32)
+    key = pmax16(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x142, 0xA, 0xF, false));
+  if (span >= 64)
+    key = pmax16(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x143, 0xC, 0xF, false));
+  return key;
 }
 
 __device__ __forceinline__ uint32_t ld32(const uint8_t *p) {

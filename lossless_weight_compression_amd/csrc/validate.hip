@@ -49,8 +49,8 @@ __global__ __launch_bounds__(kThreads) void k_validate(ValidateArgs a) {
     if (valid && (w > 8 || (a.pow2 && (w & (w - 1)))))
       atomicMin(&a.result[0], (unsigned long long)blk);
 
-    const uint32_t incl = wave_incl_scan(P, lane);
-    const uint32_t seg_sum = __shfl(incl, 63, 64);
+    const uint32_t incl = wave_incl_scan(P);
+    const uint32_t seg_sum = __builtin_amdgcn_readlane(incl, 63);
     const uint64_t so = *reinterpret_cast<const uint64_t *>(s + a.segoff_off + 8 * seg);
     const uint64_t next = seg + 1 < a.nseg
                               ? *reinterpret_cast<const uint64_t *>(s + a.segoff_off + 8 * (seg + 1))
