@@ -204,13 +204,14 @@ enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t p
   return i;
 }
 
-// Polls of an unpublished tile before the single pass gives up (about 0.1 s;
-// never reached when workgroups are dispatched in order). ENC_LOOKBACK_SPINS
+// Polls of an unpublished tile before the single pass gives up (about 0.1 s
+// at one poll per ~3.4 us of sleep; never reached when workgroups are
+// dispatched in order). ENC_LOOKBACK_SPINS
 // overrides it, which lets tests force the fallback path.
 uint32_t lookback_spin_limit() {
   const char *v = getenv("ENC_LOOKBACK_SPINS");
   if (v && v[0]) return (uint32_t)strtoul(v, nullptr, 10);
-  return 1u << 22;
+  return 1u << 15;
 }
 
 // Single pass (reads the input once): used when the output can hold the
