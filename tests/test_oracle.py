@@ -693,3 +693,29 @@ def test_fp16_exponent_ceiling_validate(orc):
     pay = int.from_bytes(bytes(s[72:80]), "little")
     b = s.copy(); b[pay] |= 0b11                          # element 0's code -> 3
     assert orc.validate(b) == (3, 0) == brute.validate(bytes(b))
+
+
+# ------------------------------------------------ fixtures in tests/golden
+def test_golden_hand_streams(orc):
+    """The hand-derived streams of tests/golden/hand_streams.json: the
+    oracle's bytes at every listed offset, its total size, and the round
+    trip."""
+    import json
+    import pathlib
+    spec = json.loads((pathlib.Path(__file__).parent / "golden" / "hand_streams.json").read_text())
+    for case in spec["cases"]:
+        exps = []
+        for pattern, reps in case["exponents"]:
+            exps += list(pattern) * reps
+        n = case["n"]
+        assert len(exps) == n, case["name"]
+        sms = (np.arange(n) * 37 + 11) % 256 if case["sign_mantissa"] != "0" else np.zeros(n, np.int64)
+        x = _bits_from_exps(exps, sms)
+        s = orc.encode(x, case["block"])
+        assert s.size == case["total"], case["name"]
+        for item in case["expect"]:
+            off, hexbytes = item[0], bytes.fromhex(item[1])
+            reps = item[2] if len(item) > 2 else 1
+            want = list(hexbytes) * reps
+            assert list(s[off:off + len(want)]) == want, (case["name"], off)
+        assert np.array_equal(orc.decode(s), x), case["name"]
