@@ -30,6 +30,9 @@ METRIC = "decompress GB/s (BF16 out) + % of HBM roofline; compression ratio"
 CSRC = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc")
 DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "group_math.h", "enc_common.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_batch_set8b_pmc.json")
+# rotating weight copies in the GEMM timing: 8 x 88.5 MB compressed (8 x 117 MB
+# dense) is well past the 256 MB last-level cache, so every call reads HBM
+GEMM_COPIES = 8
 
 
 def log(*a):
@@ -45,6 +48,11 @@ def parse():
     p.add_argument("--layers", type=int, default=32,
                    help="decoder layers in the set (32 = the full 8B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="only the fused-GEMM measurement (for profiling runs): both layouts, "
+                        "then a 1 GiB device copy of known size for counter calibration")
+    p.add_argument("--gemm-m", default="1,2,4,8,16,32,64,128,256",
+                   help="comma-separated M values of the [K, N] GEMM sweep")
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other configurations (tiny, layer sweep, stress)")
@@ -54,8 +62,11 @@ def parse():
                    help="layers of the set measured as FP16 and FP32")
     p.add_argument("--no-pow2", action="store_true",
                    help="skip the power-of-two-width variant of the decode step")
-    p.add_argument("--cpu-sample-tensors", type=int, default=21,
-                   help="first tensors of the set the CPU oracle decodes (bounded sample)")
+    p.add_argument("--cpu-layers", type=int, default=4,
+                   help="layers of the set the CPU oracle encodes and decodes on all host "
+                        "threads (bounded sample)")
+    p.add_argument("--cpu-layers-1t", type=int, default=1,
+                   help="layers of the set the CPU oracle encodes and decodes on one thread")
     return p.parse_args()
 
 
@@ -93,6 +104,18 @@ def main():
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
     B = args.block_size
+
+    if args.gemm_only:
+        g = bench_gemm(enc, synth, torch, np, dev, stream, args.gemm_m)
+        gnt = bench_gemm_nt(enc, synth, torch, np, dev)
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)                       # calibration: 1 GiB read, 1 GiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"metric": "fused decompress-GEMM us per call", "fused_gemm": g,
+                          "fused_gemm_nt": gnt, "gemm_roofline": gemm_roofline(g, gnt)}),
+              flush=True)
+        return
 
     shapes = synth.set8b_shapes()
     if args.layers != 32:
@@ -187,7 +210,22 @@ def main():
     log("decode: %.3f ms/step (launch avg %.3f, min %.3f), %.1f GB/s out, %.1f GB/s HBM"
         % (step_ms, avg_launch_ms, min(launch_ms), value, achieved))
 
+    # ---- correctness of what was timed, before anything else writes `outs` --
+    def check_outs(what):
+        for k, i in enumerate(idx):
+            if not torch.equal(outs[k], xs[k].reshape(-1)):
+                log("MISMATCH in tensor %s (%s)" % (shapes[i][0], what))
+                sys.exit(1)
+
+    def poison_outs():
+        for o in outs:
+            o.fill_(0x5A5A)
+
+    check_outs("timed batched decode")
+    log("timed batched decode: all %d outputs bit-exact" % len(outs))
+
     # ---- the same step as one launch per tensor (context, not the headline) ----
+    poison_outs()
     pt_ms = []
     for _ in range(max(args.steps // 4, 2)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -198,7 +236,8 @@ def main():
         torch.cuda.synchronize()
         pt_ms.append(e0.elapsed_time(e1))
     per_tensor_ms = float(np.median(pt_ms))
-    log("per-tensor launches: %.3f ms/step" % per_tensor_ms)
+    check_outs("per-tensor decode")
+    log("per-tensor launches: %.3f ms/step, bit-exact" % per_tensor_ms)
 
     # ---- variant: power-of-two widths (stream flag 2), same tensors ---------
     pow2 = None
@@ -213,6 +252,7 @@ def main():
                        inf.n_elems + 2 * inf.n_blocks + 8 * inf.n_segments + inf.payload_bytes)
                       for _, inf in p2_streams)
         p2_table = enc.enc_batch_prepare([(c, inf, o) for (c, inf), o in zip(p2_streams, outs)])
+        poison_outs()
         for _ in range(args.warmup):
             enc.enc_decompress_batch(p2_table, count)
         ms = []
@@ -224,6 +264,7 @@ def main():
             ms.append((e0, e1))
         torch.cuda.synchronize()
         p2_ms = float(np.mean([a.elapsed_time(b) for a, b in ms]))
+        check_outs("power-of-two-width decode")
         pow2 = {
             "compression_ratio": round(2 * n_total / p2_total, 5),
             "decode_ms_per_step": round(p2_ms, 4),
@@ -235,29 +276,12 @@ def main():
         del p2_streams, p2_table
         torch.cuda.empty_cache()
 
-    # ---- correctness of what was timed (outside the timed region) ------------
-    for k, i in enumerate(idx):
-        if not torch.equal(outs[k], xs[k].reshape(-1)):
-            log("MISMATCH in tensor", shapes[i][0])
-            sys.exit(1)
-    log("all decoded tensors bit-exact")
     del outs, xs
     torch.cuda.empty_cache()
 
-    # ---- device copy ceiling (same sizes as one step, 2 x 4 GiB) -------------
-    a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        b.copy_(a)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * a.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del a, b
-    torch.cuda.empty_cache()
+    # ---- HBM ceiling for the decoder's access shape ---------------------------
+    ceiling = stream_ceiling(enc, torch, np, dev, stream, algo_read, out_bytes)
+    copy_gbs = ceiling["copy_ceiling_gbs"]
 
     result = {
         "metric": METRIC,
@@ -286,6 +310,7 @@ def main():
         "hbm_frac_of_8tbs": round(achieved / HBM_PEAK_GBS, 4),
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "hbm_frac_of_copy": round(achieved / copy_gbs, 4),
+        "copy_ceiling": ceiling,
         "encode_gbs": round((2 * n_total + comp_total) / (enc_ms * 1e-3) / 1e9, 1),
         "encode_ms_per_tensor_calls": round(enc_ms, 2),
         "encode_batch_ms": round(enc_batch_ms, 2),
@@ -314,11 +339,13 @@ def main():
         result["other_configs"] = bench_configs(enc, synth, torch, np, dev, stream, args)
 
     if not args.no_gemm:
-        result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream)
+        result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream, args.gemm_m)
         result["fused_gemm_nt"] = bench_gemm_nt(enc, synth, torch, np, dev)
+        result["gemm_roofline"] = gemm_roofline(result["fused_gemm"], result["fused_gemm_nt"])
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(synth, np, torch, dev, args.cpu_sample_tensors, B)
+        result["cpu_baseline"] = cpu_baseline(synth, np, torch, dev, args.cpu_layers,
+                                              args.cpu_layers_1t, B)
 
     print(json.dumps(result), flush=True)
 
@@ -494,21 +521,22 @@ def _graph_time_us(fn, torch, calls=8, replays=20):
     return e0.elapsed_time(e1) * 1e3 / (replays * calls), g
 
 
-def bench_gemm(enc, synth, torch, np, dev, stream):
+def bench_gemm(enc, synth, torch, np, dev, stream, ms):
     """Y = X W with W 4096x14336 compressed (B=512) vs the same GEMM on the
-    uncompressed W, M from 1 to 256. Four rotating weight copies keep the
-    working set above the 256 MB last-level cache; times are GPU time per
+    uncompressed W, M from 1 to 256. Eight rotating weight copies keep the
+    working set well above the 256 MB last-level cache; times are GPU time per
     call from HIP-graph replays, and every replayed result is checked
     bit-exactly against an eager call (the fused path is deterministic)."""
     K, N = 4096, 14336
     W = torch.from_numpy(synth.gemm_weight(K, N).view(np.int16)).to(dev)
-    copies = 4
+    copies = GEMM_COPIES
     Ws = [W.clone() for _ in range(copies)]
     comps = [enc.enc_compress(w, 512) for w in Ws]
     out = {"shape": "X[M,4096] x W[4096,14336], W compressed at B=512",
+           "rotating_copies": copies,
            "timing": "GPU time per call, HIP-graph replay of 8 calls x 20",
            "w_bytes_compressed": comps[0][1].total_bytes, "w_bytes_dense": 2 * K * N}
-    for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+    for M in [int(v) for v in ms.split(",")]:
         X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
         Xb = X.view(torch.bfloat16)
         Ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(copies)]
@@ -556,14 +584,15 @@ def bench_gemm(enc, synth, torch, np, dev, stream):
 def bench_gemm_nt(enc, synth, torch, np, dev):
     """Y = X W^T with W in linear-layer layout [14336, 4096], compressed at
     B=512, against the same kernel on the dense W and torch's F.linear
-    (hipBLASLt); four rotating weight copies, HIP-graph replay timing."""
+    (hipBLASLt); eight rotating weight copies, HIP-graph replay timing."""
     import torch.nn.functional as F
     K, N = 4096, 14336
     W = torch.from_numpy(synth.gaussian_bits((N, K), 0.02, 4, 1, outliers=False).view(np.int16)).to(dev)
-    copies = 4
+    copies = GEMM_COPIES
     Ws = [W.clone() for _ in range(copies)]
     comps = [enc.enc_compress(w.reshape(-1), 512) for w in Ws]
     out = {"shape": "X[M,4096] x W^T, W [14336,4096] compressed at B=512",
+           "rotating_copies": copies,
            "w_bytes_compressed": comps[0][1].total_bytes}
     for M in (1, 16, 128):
         X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
@@ -597,35 +626,178 @@ def bench_gemm_nt(enc, synth, torch, np, dev):
     return out
 
 
-def cpu_baseline(synth, np, torch, dev, ntensors, B):
-    """The CPU oracle, as it is (plain C, one thread), decoding the oracle's
-    own streams of the first `ntensors` tensors of the set (21 = layers 0-2)."""
+def host_threads():
+    """Threads the CPU leg uses: the CPUs this process may run on, at most 16
+    (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(synth, np, torch, dev, layers_T, layers_1, B):
+    """The CPU oracle as it is (plain single-threaded C), on this host: its
+    encode of the set's first layers and its decode of its own streams, once
+    on one thread (layers 0..layers_1-1) and once on T threads, one tensor
+    per thread (layers 0..layers_T-1). The values are the same tensors the
+    GPU path measures; every decode is checked against its input."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as orc
     orc.build()
-    n_total = 0
-    enc_s = dec_s = 0.0
-    for i in range(ntensors):
-        x = synth.set8b_tensor_gpu(i, device=dev).cpu().numpy().view(np.uint16).reshape(-1)
-        t0 = time.perf_counter()
-        s = orc.encode(x, B)
-        enc_s += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        y = orc.decode(s)
-        dec_s += time.perf_counter() - t0
-        assert np.array_equal(y, x)
-        n_total += x.size
-    names = [synth.set8b_shapes()[i][0] for i in range(ntensors)]
+    shapes = synth.set8b_shapes()
+    T = host_threads()
+
+    def sample(layers):
+        keep = ["L%d." % l for l in range(layers)]
+        idx = [i for i, (nm, _, _) in enumerate(shapes) if any(nm.startswith(k) for k in keep)]
+        return idx, [synth.set8b_tensor_gpu(i, device=dev).cpu().numpy().view(np.uint16).reshape(-1)
+                     for i in idx]
+
+    def run(xs, threads):
+        with ThreadPoolExecutor(threads) as ex:
+            t0 = time.perf_counter()
+            streams = list(ex.map(lambda x: orc.encode(x, B), xs))
+            enc_s = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            ys = list(ex.map(orc.decode, streams))
+            dec_s = time.perf_counter() - t0
+        for x, y in zip(xs, ys):
+            assert np.array_equal(x, y), "oracle round trip failed"
+        return enc_s, dec_s
+
+    idx1, xs1 = sample(layers_1)
+    n1 = sum(x.size for x in xs1)
+    enc1, dec1 = run(xs1, 1)
+    del xs1
+    idxT, xsT = sample(layers_T)
+    nT = sum(x.size for x in xsT)
+    encT, decT = run(xsT, T)
+    del xsT
     return {
-        "value": round(2 * n_total / dec_s / 1e9, 4),
+        "value": round(2 * nT / decT / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": T,
         "kind": "oracle",
-        "sample": "oracle decode of its own streams of %s (%d values, %.2f GB BF16 out), B=%d; "
-                  "oracle encode %.2f GB/s" % ("+".join(names), n_total, 2 * n_total / 1e9, B,
-                                               2 * n_total / enc_s / 1e9),
-        "decode_s": round(dec_s, 3),
-        "encode_s": round(enc_s, 3),
+        "sample": "oracle decode of its own B=%d streams of set8b layers 0-%d (%d tensors, %d "
+                  "values, %.2f GB BF16 out), one tensor per thread on %d threads of a %s"
+                  % (B, layers_T - 1, len(idxT), nT, 2 * nT / 1e9, T, cpu_model()),
+        "cpu_model": cpu_model(),
+        "threads": T,
+        "decode_s": round(decT, 3),
+        "encode_s": round(encT, 3),
+        "encode_gbs": round(2 * nT / encT / 1e9, 4),
+        "one_thread": {
+            "sample": "set8b layers 0-%d (%d tensors, %d values)" % (layers_1 - 1, len(idx1), n1),
+            "decode_gbs": round(2 * n1 / dec1 / 1e9, 4),
+            "encode_gbs": round(2 * n1 / enc1 / 1e9, 4),
+            "decode_s": round(dec1, 3),
+            "encode_s": round(enc1, 3),
+        },
     }
+
+
+def stream_ceiling(enc, torch, np, dev, stream, read_bytes, write_bytes):
+    """HBM rate of the library's streaming kernel with the decoder's access
+    shape (16-byte loads, non-temporal 16-byte stores, one contiguous run per
+    workgroup, workgroups in order) over exactly one decode step's bytes:
+    read_bytes read, write_bytes written. 1, 2 and 4 items per thread (4, 8
+    and 16 KB written per workgroup; the decoder writes 8 KB). The ceiling
+    is the fastest of the three. A 4 GiB torch copy_ is kept for context."""
+    rb = (read_bytes + 15) // 16 * 16
+    wb = (write_bytes + 15) // 16 * 16
+    src = torch.empty(rb, dtype=torch.uint8, device=dev)
+    dst = torch.empty(wb, dtype=torch.uint8, device=dev)
+    src.fill_(0x3C)
+    res = {"read_bytes": rb, "write_bytes": wb}
+    best = 0.0
+    for items in (1, 2, 4):
+        enc.enc_stream_probe(src, dst, items)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            enc.enc_stream_probe(src, dst, items)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = (rb + wb) / (ms * 1e-3) / 1e9
+        res["items%d" % items] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                                  "kb_written_per_workgroup": 4 * items}
+        best = max(best, gbs)
+        log("stream probe, %d item(s) per thread: %.3f ms, %.1f GB/s" % (items, ms, gbs))
+    del src, dst
+    torch.cuda.empty_cache()
+    a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["torch_copy_4gib_gbs"] = round(2 * a.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    res["copy_ceiling_gbs"] = round(best, 1)
+    return res
+
+
+GEMM_PMC = os.path.join(ROOT, "profiles", "gemm_w4096x14336_b512_pmc.json")
+GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "group_math.h", "enc_common.h")]
+
+
+def gemm_roofline(g, gnt):
+    """Roofline of the fused decompress-GEMM at M = 1, 16, 128 (both
+    layouts): algorithmic bytes per call (the compressed stream, X and Y) over
+    the GPU time per call, against 8 TB/s, and the MFMA share of the 2.5
+    PFLOP/s dense BF16 peak; the HBM traffic per call comes from the
+    committed rocprofv3 PMC summary when it was taken on the current source."""
+    pmc = None
+    try:
+        d = json.load(open(GEMM_PMC))
+        if d.get("gemm_source_sha256_16") == source_hash(GEMM_SRCS):
+            pmc = d
+    except (OSError, ValueError):
+        pass
+    out = {"bound": "hbm", "peak_gbs": HBM_PEAK_GBS, "mfma_peak_tflops": BF16_DENSE_PEAK_TFLOPS}
+    for name, res in (("kn", g), ("nk", gnt)):
+        for M in (1, 16, 128):
+            r = res.get("M%d" % M, {})
+            if "fused_us" not in r:
+                continue
+            K, N = 4096, 14336
+            alg = res["w_bytes_compressed"] + 2 * M * K + 4 * M * N
+            t = r["fused_us"] * 1e-6
+            ent = {
+                "algorithmic_bytes": alg,
+                "us_per_call": r["fused_us"],
+                "achieved_gbs": round(alg / t / 1e9, 1),
+                "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(2.0 * M * K * N / t / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+                "traffic": None,
+            }
+            if pmc and name == "kn" and ("M%d" % M) in pmc.get("per_call", {}):
+                tr = pmc["per_call"]["M%d" % M]
+                ent["traffic"] = tr["hbm_bytes"]
+                ent["traffic_ratio"] = round(tr["hbm_bytes"] / alg, 4)
+            out["%s.M%d" % (name, M)] = ent
+    return out
 
 
 if __name__ == "__main__":

@@ -70,7 +70,8 @@
  *    fault is returned as ENC_ERR_HIP by the call that caused it.
  *  - Two more variables exist for tests: ENC_LOOKBACK_SPINS (polls of an
  *    unpublished tile before the single-pass encoder gives up and the
- *    two-pass encoder takes over; 0 forces that path) and
+ *    two-pass encoder takes over; 0 makes every tile after the first give
+ *    up at once, so that path always runs) and
  *    ENC_DECODE_MAX_GRID (workgroups per decode launch, below the default
  *    2^23, to run the several-launch path on small inputs). Results do not
  *    depend on either.
@@ -325,6 +326,22 @@ typedef struct enc_check {
 uint64_t enc_validate_workspace_bytes(void);
 enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, uint64_t ws_bytes,
                         void *stream, enc_check *h_check);
+
+/* Measurement helper, not part of the codec: a streaming kernel with the
+ * decoder's access shape and no decoding, so a benchmark can state the HBM
+ * rate the device reaches for that shape beside the decoder's (the
+ * decoder's roofline is memory bandwidth: every stream byte is read once and
+ * every output byte written once, as the MINE Abstract describes for
+ * single-stream inference). Reads src_bytes from d_src and writes dst_bytes
+ * to d_dst (16-byte items, non-temporal stores): workgroup b writes the b-th
+ * run of 256 x items_per_thread output items and reads the b-th
+ * proportional run of the source; the output holds copies of source items
+ * (which ones is unspecified). Sizes: nonzero multiples of 16;
+ * items_per_thread 1, 2 or 4; buffers 16-byte aligned, not overlapping.
+ * Asynchronous; allocates nothing. Errors: ENC_ERR_INVALID_ARG,
+ * ENC_ERR_UNSUPPORTED (sizes past the index arithmetic), ENC_ERR_HIP. */
+enc_status enc_stream_probe(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
+                            uint32_t items_per_thread, void *stream);
 
 /* Static text for a status code. */
 const char *enc_status_string(enc_status s);

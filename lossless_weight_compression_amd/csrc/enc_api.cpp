@@ -206,8 +206,9 @@ enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t p
 
 // Polls of an unpublished tile before the single pass gives up (about 0.1 s
 // at one poll per ~3.4 us of sleep; never reached when workgroups are
-// dispatched in order). ENC_LOOKBACK_SPINS
-// overrides it, which lets tests force the fallback path.
+// dispatched in order). ENC_LOOKBACK_SPINS overrides it; 0 makes every
+// tile after the first give up at once, so tests take the fallback path
+// deterministically.
 uint32_t lookback_spin_limit() {
   const char *v = getenv("ENC_LOOKBACK_SPINS");
   if (v && v[0]) return (uint32_t)strtoul(v, nullptr, 10);
@@ -995,6 +996,27 @@ enc_status enc_gemm_dense_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const 
   a.wdense = d_w;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launched(launch_gemm_nt(a, s), s, "GEMM launch");
+}
+
+enc_status enc_stream_probe(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
+                            uint32_t items_per_thread, void *stream) {
+  clear_err();
+  if (!d_src || !d_dst) return fail(ENC_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(d_src) || !aligned16(d_dst)) return fail(ENC_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (src_bytes == 0 || dst_bytes == 0 || src_bytes % 16 || dst_bytes % 16)
+    return fail(ENC_ERR_INVALID_ARG, "sizes must be nonzero multiples of 16 bytes");
+  if (items_per_thread != 1 && items_per_thread != 2 && items_per_thread != 4)
+    return fail(ENC_ERR_INVALID_ARG, "items_per_thread must be 1, 2 or 4");
+  const uintptr_t s0 = (uintptr_t)d_src, d0 = (uintptr_t)d_dst;
+  if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return fail(ENC_ERR_INVALID_ARG, "buffers overlap");
+  const uint64_t nwg = (dst_bytes / 16 + 256ull * items_per_thread - 1) / (256ull * items_per_thread);
+  const uint64_t si = src_bytes / 16;
+  // 32.32 fixed-point source run per workgroup: (workgroups x ratio) < 2^64
+  if (nwg > (1ull << 30) || si >= (1ull << 31) || si / nwg + 1 >= (1ull << 31))
+    return fail(ENC_ERR_UNSUPPORTED, "sizes too large for the probe's index arithmetic");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(launch_stream_probe(d_src, src_bytes, d_dst, dst_bytes, items_per_thread, s), s,
+                  "probe launch");
 }
 
 uint64_t enc_validate_workspace_bytes(void) { return 256; }

@@ -157,6 +157,10 @@ hipError_t launch_encode_wide_pack(const EncodeArgs &a, uint32_t dtype, hipStrea
 hipError_t launch_encode_wide_finish(const EncodeArgs &a, uint32_t dtype, const HeaderImage &h,
                                      hipStream_t s);
 
+// ---- measurement: streaming kernel with the decoder's access shape --------
+hipError_t launch_stream_probe(const void *src, uint64_t src_bytes, void *dst, uint64_t dst_bytes,
+                               uint32_t items, hipStream_t s);
+
 // ---- deep stream check ------------------------------------------------------
 struct ValidateArgs {
   const uint8_t *stream;

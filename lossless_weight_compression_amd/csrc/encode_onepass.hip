@@ -96,6 +96,12 @@ __device__ uint64_t look_back(gu64 *status, uint64_t tile, uint32_t lane, gu32 *
   int64_t top = (int64_t)tile - 1;
   uint32_t spins = 0;
   uint64_t v = first;
+  // spin limit 0 (a test setting): every tile with a predecessor gives up at
+  // once, whatever its window holds, so the host's fallback always runs
+  if (spin_limit == 0 && top >= 0) {
+    if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 0;
+  }
   while (top >= 0) {
     const uint64_t flag = v >> 62;
     const uint64_t pre = __ballot(flag == 2);
