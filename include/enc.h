@@ -245,8 +245,9 @@ enc_status enc_batch_prepare(const enc_item *h_items, int count, void *d_table,
 enc_status enc_decompress_batch(const void *d_table, int count, const enc_batch_plan *h_plan,
                                 void *stream);
 
-/* Device workspace bytes for enc_decompress_gemm / enc_gemm_dense: the
- * split-K partial sums (fp32, one slice per K range). */
+/* Device workspace bytes for enc_decompress_gemm / enc_gemm_dense: a small
+ * area of per-strip arrival counters, then the split-K partial sums (fp32,
+ * one slice per K range). */
 uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size);
 
 /* Fused decompress-GEMM (ZipServ Abstract: decompress on the fly into the
@@ -256,11 +257,14 @@ uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t b
  * Requirements: K*N == n_elems, N % 512 == 0 and N % block_size == 0,
  * K % 8 == 0, 1 <= M <= 4096, else ENC_ERR_SHAPE / ENC_ERR_UNSUPPORTED. A RAW
  * stream is multiplied directly from its verbatim values. The workspace must
- * be at least enc_gemm_workspace_bytes(M, K, N, block_size) bytes; its
- * contents need no initialisation. When the K dimension is split, a second
- * kernel on the same stream adds the fp32 partial slices in K order, so the
- * result is deterministic; calls sharing one workspace must not overlap.
- * Accumulation is fp32. Asynchronous; allocates nothing. */
+ * be at least enc_gemm_workspace_bytes(M, K, N, block_size) bytes and must be
+ * zero-filled before its first use with these two entry points: it starts
+ * with per-strip arrival counters, which every call leaves at zero again
+ * (the rest is scratch). When the K dimension is split, the fp32 partial
+ * slices are added in K order -- by the last workgroup of each strip to
+ * finish (M <= 2, coded W with B >= 512) or by a second kernel on the same
+ * stream -- so the result is deterministic; calls sharing one workspace must
+ * not overlap. Accumulation is fp32. Asynchronous; allocates nothing. */
 enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
                                const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
                                uint64_t ws_bytes, void *stream);

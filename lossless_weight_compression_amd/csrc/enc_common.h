@@ -187,7 +187,11 @@ struct GemmArgs {
   uint64_t total;          // stream bytes (reads never go past it)
   uint32_t ksplit;         // number of K ranges
   uint32_t krows;          // rows per K range
+  uint32_t *counters;      // per-strip arrival counts (zero between calls), or nullptr
 };
+// [K, N] GEMM workspace: gemm_counter_bytes(N) of strip arrival counters
+// (zero between calls), then the split-K partial slices.
+uint64_t gemm_counter_bytes(uint32_t N);
 uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
 // W stored [N, K] (linear-layer layout), Y = X . W^T; needs N % 64 == 0 and

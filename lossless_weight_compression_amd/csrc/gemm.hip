@@ -36,6 +36,23 @@
 #include "enc_common.h"
 #include "group_math.h"
 
+// 1: split-K arrivals ordered by agent-scope release / acquire fences;
+// 0: by waiting for the slice's agent-scope stores to complete.
+#ifndef ENC_FIXUP_FENCE
+#define ENC_FIXUP_FENCE 0
+#endif
+// Load pipelining: rows per batch and batches in the ring of the small-M
+// kernel; K steps in the ring of the MFMA kernel.
+#ifndef ENC_ROWU_RB
+#define ENC_ROWU_RB 4
+#endif
+#ifndef ENC_ROWU_NB
+#define ENC_ROWU_NB 2
+#endif
+#ifndef ENC_MFMAU_NB
+#define ENC_MFMAU_NB 2
+#endif
+
 namespace enc {
 namespace {
 
@@ -193,6 +210,75 @@ __device__ __forceinline__ void strip_finish(const GemmArgs &a, uint32_t c, uint
   });
 }
 
+// Strip and K range of workgroup b (1-D grid of nstrips x ksplit). The
+// hardware hands workgroups to the eight XCDs round-robin, b mod 8; when
+// ksplit is a multiple of 8, K range ks runs entirely on XCD ks mod 8, so
+// the strips of one row -- whose code payloads share the cache lines at
+// their ends, and whose rows share segment metadata -- meet in one L2.
+__device__ __forceinline__ void xcd_strip_range(uint32_t b, uint32_t nstrips, uint32_t ksplit,
+                                                uint32_t &c, uint32_t &ks) {
+  if ((ksplit & 7) == 0) {
+    const uint32_t j = b >> 3;
+    ks = (b & 7) + 8 * (j / nstrips);
+    c = j % nstrips;
+  } else {
+    c = b % nstrips;
+    ks = b / nstrips;
+  }
+}
+
+// In-kernel split-K reduction of a strip (no second launch): each K range
+// publishes its slice with agent-scope stores, waits until they have
+// completed (they are performed at the device's coherence point, past the
+// XCD-private L2s), and counts its arrival on the strip's counter; the last
+// workgroup to arrive adds the slices in K order (its own from LDS), writes
+// Y and resets the counter to zero for the next call. The order of the sum
+// is fixed, so the result does not depend on which workgroup is last (and
+// equals k_splitk_reduce's).
+template <int MM>
+__device__ __forceinline__ void strip_fixup(const GemmArgs &a, uint32_t c, uint32_t ks,
+                                            const float *red) {
+  __shared__ uint32_t last;
+  const uint64_t col0 = (uint64_t)c * kStrip, mn = (uint64_t)a.M * a.N;
+  float *mine = a.partial + (uint64_t)ks * mn;
+  for (uint32_t i = threadIdx.x; i < MM * kStrip; i += blockDim.x)
+    __hip_atomic_store(mine + (i / kStrip) * a.N + col0 + (i % kStrip), red[i], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+#if ENC_FIXUP_FENCE
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#else
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(a.counters + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           a.ksplit - 1;
+  __syncthreads();
+  if (!last) return;
+#if ENC_FIXUP_FENCE
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+  // every slice (this one's too: it reads back what this workgroup stored),
+  // kCh loads in flight per output before any is added
+  constexpr uint32_t kCh = 16;
+  for (uint32_t i = threadIdx.x; i < MM * kStrip; i += blockDim.x) {
+    const uint64_t yi = (i / kStrip) * a.N + col0 + (i % kStrip);
+    float sum = 0.f;
+    for (uint32_t k0 = 0; k0 < a.ksplit; k0 += kCh) {
+      float v[kCh];
+#pragma unroll
+      for (uint32_t j = 0; j < kCh; ++j)
+        v[j] = __hip_atomic_load(a.partial + (uint64_t)min(k0 + j, a.ksplit - 1) * mn + yi,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (uint32_t j = 0; j < kCh; ++j) sum += k0 + j < a.ksplit ? v[j] : 0.f;
+    }
+    a.y[yi] = sum;
+  }
+  (void)ks;
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // --------------------------------------------------------------------------
 // M < kMfmaMinM: VALU FMA path.
 // --------------------------------------------------------------------------
@@ -324,11 +410,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t *s, 
 template <int MM>
 __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
   constexpr uint32_t RW = kRowsPerWaveU;
-  constexpr uint32_t RB = 4;                      // rows per batch; two batches in flight
+  constexpr uint32_t RB = ENC_ROWU_RB;            // rows per batch
+  constexpr uint32_t NB = ENC_ROWU_NB;            // batches in the load ring
   __shared__ float red[MM * kStrip];
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const uint32_t c = blockIdx.x, ks = blockIdx.y;
+  uint32_t c, ks;
+  xcd_strip_range(blockIdx.x, a.N / kStrip, a.ksplit, c, ks);
   const uint32_t N = a.N, K = a.K, log2b = a.log2b;
   const uint32_t kw0 = ks * a.krows + wave * RW;
   const uint32_t nrows = kw0 < K ? min(RW, K - kw0) : 0u;
@@ -429,13 +517,17 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
       }
     }
   };
-  Batch bA, bB;
-  load_batch(0, bA);
-  for (uint32_t r0 = 0; r0 < nrows; r0 += 2 * RB) {
-    load_batch(r0 + RB, bB);
-    compute_batch(r0, bA);
-    load_batch(r0 + 2 * RB, bA);
-    compute_batch(r0 + RB, bB);   // rows past nrows are skipped inside
+  // NB batches in a ring: batch j + NB - 1 is loaded while batch j is
+  // computed (rows past nrows are skipped inside compute_batch)
+  Batch bt[NB];
+#pragma unroll
+  for (uint32_t p = 0; p + 1 < NB; ++p) load_batch(p * RB, bt[p]);
+  for (uint32_t r0 = 0; r0 < nrows; r0 += NB * RB) {
+#pragma unroll
+    for (uint32_t j = 0; j < NB; ++j) {
+      load_batch(r0 + (j + NB - 1) * RB, bt[(j + NB - 1) % NB]);
+      compute_batch(r0 + j * RB, bt[j]);
+    }
   }
   for (uint32_t w = 0; w < 4; ++w) {
     if (wave == w) {
@@ -449,7 +541,10 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
     }
     __syncthreads();
   }
-  strip_finish<MM>(a, c, ks, red);
+  if (a.counters && a.ksplit > 1)
+    strip_fixup<MM>(a, c, ks, red);
+  else
+    strip_finish<MM>(a, c, ks, red);
 }
 
 // --------------------------------------------------------------------------
@@ -631,7 +726,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   __shared__ uint32_t tbl_off[1024], tbl_meta[1024];
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const uint32_t c = blockIdx.x, ks = blockIdx.y, mt = blockIdx.z;
+  const uint32_t mt = blockIdx.y;
+  uint32_t c, ks;
+  xcd_strip_range(blockIdx.x, a.N / kStrip, a.ksplit, c, ks);
   const uint32_t N = a.N, K = a.K, M = a.M, log2b = a.log2b;
   const uint32_t k0 = ks * a.krows;
   const uint32_t k1 = min(k0 + a.krows, K);
@@ -805,7 +902,7 @@ hipError_t launch_valu(const GemmArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
-  const dim3 grid(a.N / kStrip, a.ksplit);
+  const dim3 grid(a.N / kStrip * a.ksplit);
   switch (a.M) {
 #define CASE(m) \
   case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(256), 0, s, a); break;
@@ -818,7 +915,7 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
 
 // Step buffers per M tile size (ring depth of the prefetch). Measured at
 // M = 16 / 32 / 128: two beat three (register pressure).
-constexpr int kMfmauNB = 2;       // K steps in the load ring
+constexpr int kMfmauNB = ENC_MFMAU_NB;   // K steps in the load ring
 // 16 waves per workgroup for every M tile: more waves share one decoded LDS
 // tile and need fewer registers each (2 rows per wave per step), so the
 // device holds more rows in flight with fewer split-K slices (measured on a
@@ -837,7 +934,7 @@ template <bool DENSE>
 hipError_t launch_mfmau(const GemmArgs &a, hipStream_t s) {
   constexpr int W = kMfmauWaves, NB = kMfmauNB;
   const uint32_t MT = mfmau_tile_m(a.M);
-  const dim3 grid(a.N / kStrip, a.ksplit, (a.M + MT - 1) / MT), block(W * 64);
+  const dim3 grid(a.N / kStrip * a.ksplit, (a.M + MT - 1) / MT), block(W * 64);
   switch (MT) {
     case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, W, DENSE, NB>), grid, block, 0, s, a); break;
     case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, W, DENSE, NB>), grid, block, 0, s, a); break;
@@ -1287,6 +1384,7 @@ void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t 
     // second round doubles the time.
     const uint64_t slots = MT == 128 ? kSlots128 : MT == 64 ? kSlots64 : (MT == 16 ? kSlots16 : kSlots32);
     ks = tiles >= slots ? 1 : slots / tiles;
+    if (ks >= 8) ks &= ~7ull;   // whole XCD groups (xcd_strip_range)
   } else {
     const uint64_t target = M <= 32 ? 512 : 256;
     ks = (target + tiles - 1) / tiles;
@@ -1305,8 +1403,11 @@ void gemm_plan(uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit, uint32_t *k
   gemm_plan_kind(M >= kMfmaMinM ? 2 : 0, M, K, N, ksplit, krows);
 }
 
+uint64_t gemm_counter_bytes(uint32_t N) { return align_up(4ull * (N / kStrip), kSectionAlign); }
+
 uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
-  // the split-K partial slices of whichever kernel the call selects
+  // the strips' arrival counters, then the split-K partial slices of
+  // whichever kernel the call selects
   uint64_t most = 256;
   for (uint32_t kind = 0; kind < 4; ++kind) {
     if ((kind >= 2) != (M >= kMfmaMinM)) continue;
@@ -1315,7 +1416,7 @@ uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
     const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
     if (partial > most) most = partial;
   }
-  return most;
+  return gemm_counter_bytes(N) + most;
 }
 
 // [N, K]-layout GEMM plan: K ranges of whole blocks (at most kNtBlocks), as
@@ -1558,7 +1659,7 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
     e = dense ? launch_mfmau<true>(a, s) : launch_mfmau<false>(a, s);
   else
     e = dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
-  if (e != hipSuccess || a.ksplit == 1) return e;
+  if (e != hipSuccess || a.ksplit == 1 || (kind == 1 && a.counters)) return e;
   return launch_splitk_reduce(a, s);
 }
 

@@ -362,9 +362,11 @@ def enc_gemm_workspace_bytes(M, K, N, block_size=512):
 
 
 def gemm_workspace(M, K, N, block_size=512, device="cuda"):
-    """A workspace for the GEMM entry points (contents need no initialisation)."""
+    """A zero-filled workspace for enc_decompress_gemm / enc_gemm_dense (it
+    starts with arrival counters that must be zero before the first call;
+    every call leaves them zero)."""
     import torch
-    return torch.empty(max(enc_gemm_workspace_bytes(M, K, N, block_size), 16), dtype=torch.uint8,
+    return torch.zeros(max(enc_gemm_workspace_bytes(M, K, N, block_size), 16), dtype=torch.uint8,
                        device=device)
 
 

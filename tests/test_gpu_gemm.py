@@ -140,13 +140,14 @@ def test_gpu_stream_and_workspace_reuse(E, orc):
     comp, info = E.enc_compress(dev(W), 512)
     ws = E.gemm_workspace(64, K, N, 512)
     ys = []
-    for M in (64, 64, 24, 2, 64):
+    for M in (64, 64, 24, 2, 1, 1, 2, 64):
         X = synth.gemm_activations(M, K)
         Y, A = orc.gemm_f64(X, W)
         y = run_fused(E, X, comp, info, N, ws=ws)
         assert_within(y, Y, A, "reuse M=%d" % M)
         ys.append(y)
-    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[4])
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[7])
+    assert np.array_equal(ys[4], ys[5]) and np.array_equal(ys[3], ys[6])
 
 
 @pytest.mark.parametrize("M", [1, 16])
