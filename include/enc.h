@@ -269,6 +269,21 @@ enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, cons
                                const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,
                                uint64_t ws_bytes, void *stream);
 
+/* enc_decompress_gemm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, requirements and results, without the
+ * workspace: it comes from a fixed-size device array inside the library,
+ * enc_gemm_noalloc_scratch_bytes() bytes on every device the library runs on,
+ * zero-filled at load and held until the process ends. A shape whose
+ * workspace (enc_gemm_workspace_bytes) exceeds it returns ENC_ERR_CAPACITY
+ * before anything is launched. Calls on one device share the array: calls
+ * that overlap in time on one device race. Uses the current device.
+ * Asynchronous; allocates nothing. */
+uint64_t enc_gemm_noalloc_scratch_bytes(void);
+enc_status enc_decompress_gemm_noalloc(const uint16_t *d_x, uint32_t M, uint32_t K,
+                                       const void *d_wcomp, const enc_info *h_winfo, uint32_t N,
+                                       float *d_y, void *stream);
+
 /* The same GEMM on an uncompressed BF16 W[K,N] (same kernels with the decode
  * stage replaced by plain loads): the baseline the fused path is compared
  * with. Same workspace rules, with block_size 512. */

@@ -376,6 +376,14 @@ BatchLayout batch_layout(const enc_item *items, int count) {
 
 }  // namespace
 
+enc_status enc::set_error(enc_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
 extern "C" {
 
 uint64_t enc_compress_bound(uint64_t n_elems) { return kHeaderBytes + 2 * n_elems; }

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "enc.h"
+
 namespace enc {
 
 constexpr uint32_t kHeaderBytes = 256;
@@ -156,6 +158,9 @@ hipError_t launch_encode_wide_params(const EncodeArgs &a, uint32_t dtype, hipStr
 hipError_t launch_encode_wide_pack(const EncodeArgs &a, uint32_t dtype, hipStream_t s);
 hipError_t launch_encode_wide_finish(const EncodeArgs &a, uint32_t dtype, const HeaderImage &h,
                                      hipStream_t s);
+
+// Sets the library's thread-local last-error text (enc_api.cpp) and returns st.
+enc_status set_error(enc_status st, const char *fmt, ...);
 
 // ---- measurement: streaming kernel with the decoder's access shape --------
 hipError_t launch_stream_probe(const void *src, uint64_t src_bytes, void *dst, uint64_t dst_bytes,

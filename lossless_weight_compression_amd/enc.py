@@ -93,6 +93,8 @@ SIGNATURES = {
     "enc_gemm_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
     "enc_decompress_gemm": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP, _U64, _VP]),
     "enc_gemm_dense": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
+    "enc_gemm_noalloc_scratch_bytes": (_U64, []),
+    "enc_decompress_gemm_noalloc": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP]),
     "enc_validate_workspace_bytes": (_U64, []),
     "enc_validate": (_ST, [_VP, _INFO_P, _VP, _U64, _VP, ctypes.POINTER(EncCheck)]),
     "enc_gemm_nt_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
@@ -381,6 +383,22 @@ def enc_decompress_gemm(x, comp, info, N, y=None, ws=None, stream=None):
         ws = gemm_workspace(M, K, N, info.block_size, x.device)
     _check(lib().enc_decompress_gemm(_ptr(x), M, K, _ptr(comp), ctypes.byref(info), N, _ptr(y),
                                      _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def enc_gemm_noalloc_scratch_bytes():
+    return int(lib().enc_gemm_noalloc_scratch_bytes())
+
+
+def enc_decompress_gemm_noalloc(x, comp, info, N, y=None, stream=None):
+    """enc_decompress_gemm with the library's static scratch as workspace."""
+    import torch
+    x = _bits(x)
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().enc_decompress_gemm_noalloc(_ptr(x), M, K, _ptr(comp), ctypes.byref(info), N,
+                                             _ptr(y), _stream(stream)))
     return y
 
 
