@@ -247,7 +247,8 @@ enc_status enc_decompress_batch(const void *d_table, int count, const enc_batch_
 
 /* Device workspace bytes for enc_decompress_gemm / enc_gemm_dense: a small
  * area of per-strip arrival counters, then the split-K partial sums (fp32,
- * one slice per K range). */
+ * one slice per K range). Returns 0 for an unsupported block size or a
+ * shape those calls reject (M outside 1..4096, N % 512, K % 8, a zero). */
 uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size);
 
 /* Fused decompress-GEMM (ZipServ Abstract: decompress on the fly into the
@@ -305,6 +306,8 @@ enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uin
  * same stream adds the partial slices in K order (deterministic); calls
  * sharing a workspace must not overlap. Accumulation is fp32. Asynchronous;
  * allocates nothing. */
+/* (Returns 0 for an unsupported block size or a shape the call rejects: M
+ * outside 1..4096, N % 64, K % 32, a zero.) */
 uint64_t enc_gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size);
 enc_status enc_decompress_gemm_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,
                                   const enc_info *h_winfo, uint32_t N, float *d_y, void *d_ws,

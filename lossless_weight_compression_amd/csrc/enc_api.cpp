@@ -856,7 +856,10 @@ enc_status enc_decompress_batch(const void *d_table, int count, const enc_batch_
 }
 
 uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size) {
-  if (log2_block(block_size) < 0 || M == 0 || K == 0 || N == 0) return 0;
+  // 0 for a shape enc_decompress_gemm rejects (the plan divides by the
+  // number of 512-column strips)
+  if (log2_block(block_size) < 0 || M == 0 || M > 4096 || K == 0 || N == 0 || N % 512 || K % 8)
+    return 0;
   return gemm_workspace_bytes(M, K, N);
 }
 
@@ -931,7 +934,9 @@ enc_status enc_gemm_dense(const uint16_t *d_x, uint32_t M, uint32_t K, const uin
 
 uint64_t enc_gemm_nt_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t block_size) {
   const int lb = log2_block(block_size);
-  if (lb < 0 || M == 0 || K == 0 || N == 0) return 0;
+  // 0 for a shape enc_decompress_gemm_nt rejects (the plan divides by the
+  // number of 64-column tiles)
+  if (lb < 0 || M == 0 || M > 4096 || K == 0 || N == 0 || N % 64 || K % 32) return 0;
   return gemm_nt_workspace_bytes(M, K, N, (uint32_t)lb);
 }
 

@@ -138,10 +138,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Raw buffer descriptor over [base, base + bytes): the hardware drops stores
-// and zero-fills loads of dwords that do not lie wholly inside, so every lane
-// issues its loads and stores unconditionally (a load or store under a branch
-// would make the compiler wait for all outstanding memory operations).
+// Raw buffer descriptor over [base, base + bytes). The CDNA3 ISA reference
+// guide's range checking for buffer instructions (stride 0: out of range at
+// or past num_records, checked per dword of a multi-dword access; CDNA4 keeps
+// the rule) makes the hardware drop stores and zero-fill loads of dwords that
+// do not lie wholly inside, so every lane issues its loads and stores
+// unconditionally (a load or store under a branch would make the compiler
+// wait for all outstanding memory operations).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void *base, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
                                            (int)(uint32_t)(bytes < 0xFFFFFFF0ull ? bytes : 0xFFFFFFF0ull),

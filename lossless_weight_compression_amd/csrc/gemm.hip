@@ -399,9 +399,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Raw buffer descriptor over a whole stream (< 4 GiB): loads take a 32-bit
-// offset, and the hardware checks every dword against num_records = stream
-// size (out-of-range dwords read as 0, per dword), so a group's three code
-// dwords are one buffer_load_dwordx3 even at the very end of the stream.
+// offset. Range checking as the CDNA3 ISA reference guide defines it for
+// buffer instructions (section on buffer addressing, range checking; CDNA4
+// keeps the rule): with stride 0 an access is out of range when its byte
+// offset is at or past num_records (here the stream size), the check is made
+// for each dword of a multi-dword access, out-of-range dwords load as zero
+// and out-of-range stores are not performed. So a group's three code dwords
+// are one buffer_load_dwordx3 even at the very end of the stream.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t *s, uint64_t total) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(s), 0, (int)(uint32_t)total,
                                            0x00020000);
