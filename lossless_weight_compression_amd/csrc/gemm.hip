@@ -52,6 +52,13 @@
 #ifndef ENC_MFMAU_NB
 #define ENC_MFMAU_NB 2
 #endif
+#ifndef ENC_MFMAU_NB_BIG
+#define ENC_MFMAU_NB_BIG 2
+#endif
+#ifndef ENC_MFMAU_KS
+#define ENC_MFMAU_KS 32
+#endif
+
 
 namespace enc {
 namespace {
@@ -235,15 +242,18 @@ __device__ __forceinline__ void xcd_strip_range(uint32_t b, uint32_t nstrips, ui
 // Y and resets the counter to zero for the next call. The order of the sum
 // is fixed, so the result does not depend on which workgroup is last (and
 // equals k_splitk_reduce's).
-template <int MM>
-__device__ __forceinline__ void strip_fixup(const GemmArgs &a, uint32_t c, uint32_t ks,
-                                            const float *red) {
+// Publishes this K range's slice of a strip (for_each as in splitk_finish)
+// with agent-scope stores, waits until they have completed, and counts the
+// arrival on the strip's counter. Returns true in the last workgroup to
+// arrive (all slices are then in place).
+template <class ForEach>
+__device__ __forceinline__ bool strip_arrive(const GemmArgs &a, uint32_t c, uint32_t ks,
+                                             ForEach for_each) {
   __shared__ uint32_t last;
-  const uint64_t col0 = (uint64_t)c * kStrip, mn = (uint64_t)a.M * a.N;
-  float *mine = a.partial + (uint64_t)ks * mn;
-  for (uint32_t i = threadIdx.x; i < MM * kStrip; i += blockDim.x)
-    __hip_atomic_store(mine + (i / kStrip) * a.N + col0 + (i % kStrip), red[i], __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  float *mine = a.partial + (uint64_t)ks * a.M * a.N;
+  for_each([&](int64_t y, float v) {
+    if (y >= 0) __hip_atomic_store(mine + y, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
 #if ENC_FIXUP_FENCE
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 #else
@@ -254,14 +264,21 @@ __device__ __forceinline__ void strip_fixup(const GemmArgs &a, uint32_t c, uint3
     last = __hip_atomic_fetch_add(a.counters + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            a.ksplit - 1;
   __syncthreads();
-  if (!last) return;
 #if ENC_FIXUP_FENCE
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #endif
-  // every slice (this one's too: it reads back what this workgroup stored),
+  return last;
+}
+
+// In the last workgroup of strip c: Y[m, strip] = sum of the slices in K
+// order (the order is fixed, so the result does not depend on which
+// workgroup is last, and equals k_splitk_reduce's); then the strip's counter
+// goes back to zero for the next call.
+__device__ __forceinline__ void strip_reduce(const GemmArgs &a, uint32_t c) {
+  const uint64_t col0 = (uint64_t)c * kStrip, mn = (uint64_t)a.M * a.N;
   // kCh loads in flight per output before any is added
   constexpr uint32_t kCh = 16;
-  for (uint32_t i = threadIdx.x; i < MM * kStrip; i += blockDim.x) {
+  for (uint32_t i = threadIdx.x; i < a.M * kStrip; i += blockDim.x) {
     const uint64_t yi = (i / kStrip) * a.N + col0 + (i % kStrip);
     float sum = 0.f;
     for (uint32_t k0 = 0; k0 < a.ksplit; k0 += kCh) {
@@ -275,8 +292,21 @@ __device__ __forceinline__ void strip_fixup(const GemmArgs &a, uint32_t c, uint3
     }
     a.y[yi] = sum;
   }
-  (void)ks;
   if (threadIdx.x == 0) __hip_atomic_store(a.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// In-kernel split-K reduction of a strip (no second launch): each K range
+// publishes its slice and counts its arrival; the last workgroup to arrive
+// adds the slices (its own included, read back) and writes Y.
+template <int MM>
+__device__ __forceinline__ void strip_fixup(const GemmArgs &a, uint32_t c, uint32_t ks,
+                                            const float *red) {
+  const uint64_t col0 = (uint64_t)c * kStrip;
+  const bool last = strip_arrive(a, c, ks, [&](auto fn) {
+    for (uint32_t i = threadIdx.x; i < MM * kStrip; i += blockDim.x)
+      fn((int64_t)(i / kStrip) * a.N + (int64_t)col0 + (i % kStrip), red[i]);
+  });
+  if (last) strip_reduce(a, c);
 }
 
 // --------------------------------------------------------------------------
@@ -392,8 +422,11 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
 // so at most 64. Measured on a 4096 x 14336 W, GPU time per call at M = 1 /
 // M = 2: 32 rows 25.7 / 27.3 us, 64 rows 24.1 / 26.0 (half the split-K
 // slices); 8 waves x 64 rows 23.9 / 26.1, 16 waves x 64 36.4 / 39.9.
-constexpr uint32_t kRowsPerWaveU = 64;
+constexpr uint32_t kRowuWaves = 4;
+constexpr uint32_t kRowuRange = 256;            // rows per K range (workgroup)
+constexpr uint32_t kRowsPerWaveU = kRowuRange / kRowuWaves;
 static_assert(kRowsPerWaveU <= 64, "k_gemm_rowu keeps one row per lane");
+static_assert(kRowuRange % kRowuWaves == 0, "whole rows per wave");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
@@ -412,8 +445,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t *s, 
 }
 
 template <int MM>
-__global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
-  constexpr uint32_t RW = kRowsPerWaveU;
+__global__ __launch_bounds__(kRowuWaves * 64) void k_gemm_rowu(GemmArgs a) {
+  const uint32_t RW = a.krows / kRowuWaves;      // <= 64 (the plan's choice)
   constexpr uint32_t RB = ENC_ROWU_RB;            // rows per batch
   constexpr uint32_t NB = ENC_ROWU_NB;            // batches in the load ring
   __shared__ float red[MM * kStrip];
@@ -533,7 +566,7 @@ __global__ __launch_bounds__(256) void k_gemm_rowu(GemmArgs a) {
       compute_batch(r0 + j * RB, bt[j]);
     }
   }
-  for (uint32_t w = 0; w < 4; ++w) {
+  for (uint32_t w = 0; w < kRowuWaves; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int m = 0; m < MM; ++m)
@@ -707,7 +740,7 @@ __device__ __forceinline__ void lds_barrier() {
 // M tile of k_gemm_mfmau; larger M runs several 128-row tiles.
 uint32_t mfmau_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
-constexpr uint32_t kXsPitch = 40;   // bf16 per LDS row of the staged X slice (32 + 8)
+constexpr uint32_t xs_pitch(uint32_t ks) { return ks + 8; }   // bf16 per LDS row of the X slice
 
 // Each K step, the workgroup's threads load the step's X slice (MT rows x 32
 // k, one 16-byte piece per thread) and store it in LDS next to the decoded W
@@ -716,18 +749,18 @@ constexpr uint32_t kXsPitch = 40;   // bf16 per LDS row of the staged X slice (3
 // two-step ring within 128 registers at 16 waves for every M tile, so W is
 // decoded once for M up to 128 (measured on a 4096 x 14336 W: M = 32 38.7 ->
 // 34.1 us, M = 64 50.5 -> 39.7, M = 128 57.8 -> 52.7).
-template <int MT, int WAVES, bool DENSE, int NB>
+template <int MT, int WAVES, bool DENSE, int NB, int KS>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
-  constexpr uint32_t RPW = 32 / WAVES;          // rows decoded per wave per step
+  constexpr uint32_t RPW = KS / WAVES;          // rows decoded per wave per step
   constexpr uint32_t NSUB = 32 / WAVES;         // 16-column subtiles per wave
   constexpr uint32_t MSUB = MT / 16;
   constexpr uint32_t NTHR = WAVES * 64;
-  constexpr uint32_t XP = MT * 4;               // 16-byte pieces of a step's X slice
-  static_assert(RPW % 2 == 0, "rows are decoded in pairs");
+  constexpr uint32_t XP = MT * KS / 8;          // 16-byte pieces of a step's X slice
+  constexpr uint32_t XPITCH = xs_pitch(KS);
+  static_assert(WAVES == 16 && (KS == 32 || KS == 64), "16 waves, steps of 32 or 64 rows");
   static_assert(XP <= NTHR, "at most one X piece per thread");
-  __shared__ __attribute__((aligned(16))) uint32_t tile[2][16 * kPitchU];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * kXsPitch];
-  __shared__ uint32_t tbl_off[1024], tbl_meta[1024];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[2][KS / 2 * kPitchU];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * XPITCH];
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const uint32_t mt = blockIdx.y;
@@ -736,99 +769,161 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   const uint32_t N = a.N, K = a.K, M = a.M, log2b = a.log2b;
   const uint32_t k0 = ks * a.krows;
   const uint32_t k1 = min(k0 + a.krows, K);
-  const uint32_t nsteps = (k1 - k0 + 31) / 32;
+  const uint32_t nsteps = (k1 - k0 + KS - 1) / KS;   // RPW * nsteps <= 64: at most 1024 rows
   const uint32_t col0 = c * kStrip, m0 = mt * MT;
   const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
 
-  if (!DENSE) {
-    for (uint32_t r = tid; r < k1 - k0; r += NTHR) {
-      const uint64_t e = (uint64_t)(k0 + r) * N + col0;
+  // Row table of this wave (coded W): lane l describes row KS (l / RPW) +
+  // RPW wave + l % RPW of the K range -- a row the wave decodes in step
+  // l / RPW -- by its block offset and a meta word (base, width, first group
+  // of the strip inside its block). Steps read their rows with v_readlane
+  // into SGPRs: no LDS table and no barrier before the first loads. Rows
+  // past the K range keep offset and meta word 0 (width 0, base 0).
+  uint32_t t_off = 0, t_meta = 0;
+  auto build_table = [&]() {
+    if (!DENSE && k0 + KS * (lane / RPW) + RPW * wave + (lane % RPW) < k1) {
+      const uint32_t kr = k0 + KS * (lane / RPW) + RPW * wave + (lane % RPW);
+      const uint64_t e = (uint64_t)kr * N + col0;
       uint64_t off, mw;
       row_block<false>(a, e >> log2b, off, mw);
       uint32_t w = (uint32_t)(mw >> 8) & 0xFFu;
       if (w > 8) w = 0;   // corrupted stream: decode as width 0
-      tbl_off[r] = (uint32_t)off;
-      tbl_meta[r] = ((uint32_t)mw & 0xFFu) | (w << 8) |
-                    ((uint32_t)((e & ((1ull << log2b) - 1)) >> 3) << 16);
+      t_off = (uint32_t)off;
+      t_meta = ((uint32_t)mw & 0xFFu) | (w << 8) | ((uint32_t)((e & ((1ull << log2b) - 1)) >> 3) << 16);
     }
-    __syncthreads();
-  }
+  };
 
   struct Step {
     u32x2 sm[RPW];
     u32x3 q[RPW];
     uint4 dv[RPW];
-    uint4 x;                    // this thread's piece of the X slice
+    uint32_t off[RPW], meta[RPW];   // rows' block offset and meta word (uniform)
+    uint4 x;                    // this thread's piece of the X slice, as loaded
+    uint32_t xm;                // all ones if that piece lies inside the K range
   };
   // Every load is issued unconditionally, from a clamped (always valid) row
   // or X element; out-of-range data is discarded after the load. Loads under
   // branches would make the compiler wait for all outstanding loads (vmcnt 0)
   // before the decode, i.e. also for the next step's prefetch.
-  // st >= nsteps (ring slots past the end): the stream loads get an offset
-  // past the descriptor's range (zeros, no memory access), the others a
-  // clamped row.
-  auto load_step = [&](uint32_t st, Step &S) {
-    const uint32_t kb = k0 + 32 * min(st, nsteps - 1);
-    const uint32_t dead = st < nsteps ? 0u : 0x80000000u;
+  // Ring slots past the last step, and rows past the K range: the stream
+  // loads get an offset past the descriptor's range (zeros, no memory
+  // access) -- with width and base 0 such a row decodes to zeros -- the
+  // others a clamped row.
+  // The loads of a step in two parts: rows' sign+mantissa bytes (or dense
+  // values) and the X piece, which need no row table, then the code bytes,
+  // which do (so the first steps' byte planes are in flight while the table
+  // is built).
+  auto load_codes = [&](uint32_t st, Step &S) {
+    if (DENSE) return;
+    const uint32_t sc = min(st, nsteps - 1);
+    const uint32_t kb = k0 + KS * sc;
 #pragma unroll
     for (uint32_t j = 0; j < RPW; ++j) {
-      const uint32_t kr = min(kb + wave * RPW + j, k1 - 1);
-      if (DENSE) {
-        S.dv[j] = *reinterpret_cast<const uint4 *>(a.wdense + (uint64_t)kr * N + col0 + 8 * lane);
-      } else {
-        const uint32_t off = __builtin_amdgcn_readfirstlane(tbl_off[kr - k0]);
-        const uint32_t meta = __builtin_amdgcn_readfirstlane(tbl_meta[kr - k0]);
-        const uint32_t w = (meta >> 8) & 15u;
-        const uint32_t pb = off + ((meta >> 16) + lane) * w;
-        S.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (8 * lane) | dead, kHeaderBytes + kr * N + col0, 0);
-        S.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
-      }
+      const uint32_t dead = (st < nsteps && kb + wave * RPW + j < k1) ? 0u : 0x80000000u;
+      const uint32_t off = __builtin_amdgcn_readlane(t_off, RPW * sc + j);
+      const uint32_t meta = __builtin_amdgcn_readlane(t_meta, RPW * sc + j);
+      const uint32_t w = (meta >> 8) & 15u;
+      const uint32_t pb = off + ((meta >> 16) + lane) * w;
+      S.off[j] = off;
+      S.meta[j] = meta;
+      S.q[j] = __builtin_amdgcn_raw_buffer_load_b96(rs, (pb & ~3u) | dead, 0, 0);
     }
-    // piece p = tid mod XP: row p / 4, k = kb + 8 (p % 4) .. + 7 (threads
-    // past XP load a duplicate and do not store it)
-    const uint32_t p = tid % XP;
-    const uint32_t m = m0 + (p >> 2), kx = kb + 8 * (p & 3);
-    const uint4 v = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K +
-                                                     min(kx, k1 - 8));
-    const bool in = m < M && kx < k1;
-    S.x = make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
   };
-  auto decode_row = [&](uint32_t st, const Step &S, uint32_t j) -> uint4 {
-    const uint32_t kr = k0 + 32 * st + wave * RPW + j;   // uniform
-    if (kr >= k1) return make_uint4(0, 0, 0, 0);
-    if (DENSE) return S.dv[j];
-    const uint32_t off = __builtin_amdgcn_readfirstlane(tbl_off[kr - k0]);
-    const uint32_t meta = __builtin_amdgcn_readfirstlane(tbl_meta[kr - k0]);
-    const uint32_t w = (meta >> 8) & 15u;           // wave-uniform
-    uint32_t el, eh;
+  auto load_planes = [&](uint32_t st, Step &S) {
+    const uint32_t sc = min(st, nsteps - 1);
+    const uint32_t kb = k0 + KS * sc;
+#pragma unroll
+    for (uint32_t j = 0; j < RPW; ++j) {
+      const uint32_t dead = (st < nsteps && kb + wave * RPW + j < k1) ? 0u : 0x80000000u;
+      const uint32_t kr = min(kb + wave * RPW + j, k1 - 1);
+      if (DENSE)
+        S.dv[j] = *reinterpret_cast<const uint4 *>(a.wdense + (uint64_t)kr * N + col0 + 8 * lane);
+      else
+        S.sm[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (8 * lane) | dead, kHeaderBytes + kr * N + col0, 0);
+    }
+    // piece p = tid mod XP: row p / (KS / 8), k = kb + 8 (p % (KS / 8)) .. + 7 (threads
+    // past XP load a duplicate and do not store it). Rows past M are clamped
+    // copies of row M - 1 and only reach output rows that are not stored;
+    // pieces past the K range are zeroed when the last step stores them (a
+    // select right after the load would make the compiler wait for it, i.e.
+    // for every load just issued).
+    const uint32_t p = tid % XP;
+    const uint32_t m = m0 + p / (KS / 8), kx = kb + 8 * (p % (KS / 8));
+    S.x = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K + min(kx, k1 - 8));
+    S.xm = (st < nsteps && kx < k1) ? ~0u : 0u;
+  };
+  // Dense W: rows as loaded (zero past the K range).
+  auto dense_row = [&](uint32_t st, const Step &S, uint32_t j) -> uint4 {
+    const uint32_t kr = k0 + KS * st + wave * RPW + j;   // uniform
+    return kr < k1 ? S.dv[j] : make_uint4(0, 0, 0, 0);
+  };
+  // Coded W: the w-bit codes of row j's eight values as bytes, E0 = values
+  // 0, 2, 4, 6 and E1 = values 1, 3, 5, 7 (the order the 4-bit split gives).
+  auto code_bytes = [&](const Step &S, uint32_t j, uint32_t &E0, uint32_t &E1) {
+    const uint32_t w = (S.meta[j] >> 8) & 15u;   // wave-uniform
     if (w == 4) {
-      codes_to_bytes_w4(S.q[j].x, el, eh);          // dword-aligned, see k_gemm_rowu
+      // block payloads start on 16-byte boundaries, so a 4-byte group is
+      // dword-aligned: its codes are exactly q.x
+      E0 = S.q[j].x & 0x0F0F0F0Fu;
+      E1 = (S.q[j].x >> 4) & 0x0F0F0F0Fu;
     } else {
-      const uint32_t sh = ((off + ((meta >> 16) + lane) * w) & 3u) * 8;
+      const uint32_t sh = ((S.off[j] + ((S.meta[j] >> 16) + lane) * w) & 3u) * 8;
       const uint32_t lo = __builtin_amdgcn_alignbit(S.q[j].y, S.q[j].x, sh);
       const uint32_t hi = __builtin_amdgcn_alignbit(S.q[j].z, S.q[j].y, sh);
+      uint32_t el, eh;
       codes_to_bytes(lo, hi, w, el, eh);
+      E0 = __builtin_amdgcn_perm(eh, el, 0x06040200u);
+      E1 = __builtin_amdgcn_perm(eh, el, 0x07050301u);
     }
-    return bytes_to_bf16(el, eh, (meta & 0xFFu) * 0x01010101u, S.sm[j].x, S.sm[j].y);
   };
+  // Row pair (a = k even, b = k + 1) of this lane's eight columns as k-pair
+  // dwords, BF16 of row a in the low half: per column, the two code bytes
+  // side by side as 16-bit lanes (v_perm), shifted to the exponent field
+  // with both bases added (v_lshl_add), and merged with the sign+mantissa
+  // bytes placed at bits 0..6 and 15 of each half (v_perm, v_bfi) --
+  // sign | exponent << 7 | mantissa, four operations per two values.
   auto decode_step = [&](uint32_t st, const Step &S, uint32_t buf) {
+    const uint32_t kb = k0 + KS * st;
+    const bool tail = kb + KS > k1;               // uniform: the last, partial step
 #pragma unroll
-    for (uint32_t j = 0; j < RPW; j += 2) {
-      const uint4 ra = decode_row(st, S, j), rb = decode_row(st, S, j + 1);
-      uint4 lo4, hi4;   // k-pairs of columns 0..3 and 4..7 of this lane
-      lo4.x = __builtin_amdgcn_perm(rb.x, ra.x, 0x05040100u);
-      lo4.y = __builtin_amdgcn_perm(rb.x, ra.x, 0x07060302u);
-      lo4.z = __builtin_amdgcn_perm(rb.y, ra.y, 0x05040100u);
-      lo4.w = __builtin_amdgcn_perm(rb.y, ra.y, 0x07060302u);
-      hi4.x = __builtin_amdgcn_perm(rb.z, ra.z, 0x05040100u);
-      hi4.y = __builtin_amdgcn_perm(rb.z, ra.z, 0x07060302u);
-      hi4.z = __builtin_amdgcn_perm(rb.w, ra.w, 0x05040100u);
-      hi4.w = __builtin_amdgcn_perm(rb.w, ra.w, 0x07060302u);
-      uint32_t *dst = &tile[buf][(wave * RPW + j) / 2 * kPitchU + 8 * lane];
-      *reinterpret_cast<uint4 *>(dst) = lo4;
-      *reinterpret_cast<uint4 *>(dst + 4) = hi4;
+    for (uint32_t pr = 0; pr < RPW / 2; ++pr) {   // row pairs 2 pr, 2 pr + 1 of this wave
+      uint32_t *dst = &tile[buf][(wave * (RPW / 2) + pr) * kPitchU + 8 * lane];
+      if (DENSE) {
+        const uint4 ra = dense_row(st, S, 2 * pr), rb = dense_row(st, S, 2 * pr + 1);
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(
+            __builtin_amdgcn_perm(rb.x, ra.x, 0x05040100u), __builtin_amdgcn_perm(rb.x, ra.x, 0x07060302u),
+            __builtin_amdgcn_perm(rb.y, ra.y, 0x05040100u), __builtin_amdgcn_perm(rb.y, ra.y, 0x07060302u));
+        *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(
+            __builtin_amdgcn_perm(rb.z, ra.z, 0x05040100u), __builtin_amdgcn_perm(rb.z, ra.z, 0x07060302u),
+            __builtin_amdgcn_perm(rb.w, ra.w, 0x05040100u), __builtin_amdgcn_perm(rb.w, ra.w, 0x07060302u));
+      } else {
+        uint32_t E0a, E1a, E0b, E1b;
+        code_bytes(S, 2 * pr, E0a, E1a);
+        code_bytes(S, 2 * pr + 1, E0b, E1b);
+        const uint32_t b7 = ((S.meta[2 * pr] & 0xFFu) << 7) | ((S.meta[2 * pr + 1] & 0xFFu) << 23);
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {   // columns 4h .. 4h + 3
+          const uint32_t sa = h ? S.sm[2 * pr].y : S.sm[2 * pr].x;
+          const uint32_t sb = h ? S.sm[2 * pr + 1].y : S.sm[2 * pr + 1].x;
+          uint32_t kp[4];
+#pragma unroll
+          for (uint32_t q = 0; q < 4; ++q) {
+            const uint32_t col = 4 * h + q, i = col >> 1;
+            const uint32_t ea = (col & 1) ? E1a : E0a, eb = (col & 1) ? E1b : E0b;
+            const uint32_t e16 = __builtin_amdgcn_perm(eb, ea, 0x0C000C00u | ((4u + i) << 16) | i);
+            const uint32_t x16 = (e16 << 7) + b7;
+            const uint32_t s2 = __builtin_amdgcn_perm(sb, sa, q | (q << 8) | ((4u + q) << 16) | ((4u + q) << 24));
+            kp[q] = (s2 & 0x807F807Fu) | (x16 & ~0x807F807Fu);
+          }
+          *reinterpret_cast<uint4 *>(dst + 4 * h) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
+        }
+      }
     }
-    if (tid < XP) *reinterpret_cast<uint4 *>(&xs[buf][(tid >> 2) * kXsPitch + 8 * (tid & 3)]) = S.x;
+    if (tid < XP) {
+      uint4 x = S.x;
+      if (tail) x = make_uint4(x.x & S.xm, x.y & S.xm, x.z & S.xm, x.w & S.xm);
+      *reinterpret_cast<uint4 *>(&xs[buf][(tid / (KS / 8)) * XPITCH + 8 * (tid % (KS / 8))]) = x;
+    }
   };
   f32x4 acc[MSUB][NSUB];
 #pragma unroll
@@ -836,49 +931,57 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
 #pragma unroll
     for (uint32_t ns = 0; ns < NSUB; ++ns) acc[mi][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto mfma_step = [&](uint32_t buf) {
-    const uint32_t kq = 4 * (lane >> 4);
-    bf16x8 b[NSUB];
 #pragma unroll
-    for (uint32_t ns = 0; ns < NSUB; ++ns) {
-      const uint32_t n = wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
-      uint4 bw;
-      bw.x = tile[buf][(kq + 0) * kPitchU + n];
-      bw.y = tile[buf][(kq + 1) * kPitchU + n];
-      bw.z = tile[buf][(kq + 2) * kPitchU + n];
-      bw.w = tile[buf][(kq + 3) * kPitchU + n];
-      b[ns] = __builtin_bit_cast(bf16x8, bw);
-    }
+    for (uint32_t kc = 0; kc < KS / 32; ++kc) {   // 32-k chunks of the step
+      const uint32_t kq = 16 * kc + 4 * (lane >> 4);
+      bf16x8 b[NSUB];
 #pragma unroll
-    for (uint32_t mi = 0; mi < MSUB; ++mi) {
-      const uint4 av =
-          *reinterpret_cast<const uint4 *>(&xs[buf][(16 * mi + (lane & 15)) * kXsPitch + 8 * (lane >> 4)]);
-      const bf16x8 af = __builtin_bit_cast(bf16x8, av);
+      for (uint32_t ns = 0; ns < NSUB; ++ns) {
+        const uint32_t n = wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
+        uint4 bw;
+        bw.x = tile[buf][(kq + 0) * kPitchU + n];
+        bw.y = tile[buf][(kq + 1) * kPitchU + n];
+        bw.z = tile[buf][(kq + 2) * kPitchU + n];
+        bw.w = tile[buf][(kq + 3) * kPitchU + n];
+        b[ns] = __builtin_bit_cast(bf16x8, bw);
+      }
 #pragma unroll
-      for (uint32_t ns = 0; ns < NSUB; ++ns)
-        acc[mi][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[ns], acc[mi][ns], 0, 0, 0);
+      for (uint32_t mi = 0; mi < MSUB; ++mi) {
+        const uint4 av = *reinterpret_cast<const uint4 *>(
+            &xs[buf][(16 * mi + (lane & 15)) * XPITCH + 32 * kc + 8 * (lane >> 4)]);
+        const bf16x8 af = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (uint32_t ns = 0; ns < NSUB; ++ns)
+          acc[mi][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[ns], acc[mi][ns], 0, 0, 0);
+      }
     }
   };
 
   // NB step buffers in a ring: step s + NB - 1 is loaded while step s is
-  // decoded and multiplied. Loads are issued unconditionally (see load_step
-  // for slots past the last step), so the number of loads in flight is the
-  // same on every path and the compiler waits for exactly the step it needs.
+  // decoded and multiplied. Loads are issued unconditionally (see
+  // load_codes for slots past the last step), and the step count is rounded up to a
+  // multiple of NB (steps past the K range decode to zeros), so every path
+  // through the loop body is the same and the compiler waits for exactly the
+  // step it needs.
+  const uint32_t nst = (nsteps + NB - 1) / NB * NB;
   Step S[NB];
 #pragma unroll
-  for (uint32_t p = 0; p + 1 < NB; ++p) load_step(p, S[p]);
-  for (uint32_t st = 0; st < nsteps; st += NB) {
+  for (uint32_t p = 0; p + 1 < NB; ++p) load_planes(p, S[p]);
+  build_table();
+#pragma unroll
+  for (uint32_t p = 0; p + 1 < NB; ++p) load_codes(p, S[p]);
+  for (uint32_t st = 0; st < nst; st += NB) {
 #pragma unroll
     for (uint32_t j = 0; j < NB; ++j) {
-      load_step(st + j + NB - 1, S[(j + NB - 1) % NB]);
-      if (st + j < nsteps) {
-        decode_step(st + j, S[j], (st + j) & 1);
-        lds_barrier();
-        mfma_step((st + j) & 1);
-      }
+      load_planes(st + j + NB - 1, S[(j + NB - 1) % NB]);
+      load_codes(st + j + NB - 1, S[(j + NB - 1) % NB]);
+      decode_step(st + j, S[j], (st + j) & 1);
+      lds_barrier();
+      mfma_step((st + j) & 1);
     }
   }
 
-  splitk_finish(a, ks, [&](auto fn) {
+  auto outputs = [&](auto fn) {
 #pragma unroll
     for (uint32_t mi = 0; mi < MSUB; ++mi)
 #pragma unroll
@@ -889,7 +992,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
           const uint32_t n = col0 + wave * (kStrip / WAVES) + 16 * ns + (lane & 15);
           fn(m < M ? (int64_t)m * N + n : (int64_t)-1, acc[mi][ns][j]);
         }
-  });
+  };
+  splitk_finish(a, ks, outputs);
 }
 
 template <bool DENSE>
@@ -909,7 +1013,7 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
   const dim3 grid(a.N / kStrip * a.ksplit);
   switch (a.M) {
 #define CASE(m) \
-  case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(256), 0, s, a); break;
+  case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(kRowuWaves * 64), 0, s, a); break;
     CASE(1) CASE(2)
 #undef CASE
     default: return hipErrorInvalidValue;
@@ -919,31 +1023,37 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
 
 // Step buffers per M tile size (ring depth of the prefetch). Measured at
 // M = 16 / 32 / 128: two beat three (register pressure).
-constexpr int kMfmauNB = ENC_MFMAU_NB;   // K steps in the load ring
+// K steps in the load ring (16- and 32-row tiles; 64 and 128)
+constexpr int mfmau_nb(int MT) { return MT <= 32 ? ENC_MFMAU_NB : ENC_MFMAU_NB_BIG; }
+// Rows per K step (16- and 32-row tiles; 64 and 128, whose X slice would not
+// fit twice in LDS with 64-row steps)
+constexpr int mfmau_ks(int MT) { return MT <= 32 ? ENC_MFMAU_KS : 32; }
 // 16 waves per workgroup for every M tile: more waves share one decoded LDS
 // tile and need fewer registers each (2 rows per wave per step), so the
 // device holds more rows in flight with fewer split-K slices (measured on a
 // 4096 x 14336 W, 16 waves over 4: M = 8 35.9 -> 29.8 us, M = 16 36.6 ->
 // 31.6, M = 32 42.3 -> 38.9; with the X slice in LDS the 64- and 128-row
-// tiles gained from 16 waves over 8 too). The split-K plan fills the
-// resident workgroups: two per CU for the 16-row tile (LDS and registers
-// allow it), one for the others.
+// tiles gained from 16 waves over 8 too). The split-K plan aims at one
+// workgroup per CU for every M tile: two resident 16-row workgroups per CU
+// (their registers and LDS allow it) were slower on a 4096 x 14336 W at
+// M = 4 / 16 (29.3 / 31.8 us per call against 27.5 / 29.2): the CU's
+// decode, LDS and barrier work per K step is the limit, not memory.
 constexpr int kMfmauWaves = 16;
-constexpr uint64_t kSlots16 = 512;
+constexpr uint64_t kSlots16 = 256;
 constexpr uint64_t kSlots32 = 256;
 constexpr uint64_t kSlots64 = 256;
 constexpr uint64_t kSlots128 = 256;
 
 template <bool DENSE>
 hipError_t launch_mfmau(const GemmArgs &a, hipStream_t s) {
-  constexpr int W = kMfmauWaves, NB = kMfmauNB;
+  constexpr int W = kMfmauWaves;
   const uint32_t MT = mfmau_tile_m(a.M);
   const dim3 grid(a.N / kStrip * a.ksplit, (a.M + MT - 1) / MT), block(W * 64);
   switch (MT) {
-    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, W, DENSE, NB>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, W, DENSE, NB>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_gemm_mfmau<64, W, DENSE, NB>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfmau<128, W, DENSE, NB>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_gemm_mfmau<16, W, DENSE, mfmau_nb(16), mfmau_ks(16)>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_gemm_mfmau<32, W, DENSE, mfmau_nb(32), mfmau_ks(32)>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_gemm_mfmau<64, W, DENSE, mfmau_nb(64), mfmau_ks(64)>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfmau<128, W, DENSE, mfmau_nb(128), mfmau_ks(128)>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -1371,7 +1481,7 @@ uint32_t gemm_kind(uint32_t M, bool dense, uint32_t log2b, uint64_t total) {
 void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t *ksplit,
                     uint32_t *krows) {
   if (kind == 0 || kind == 1) {
-    const uint32_t rows = kind == 0 ? kValuRows : 4 * kRowsPerWaveU;
+    const uint32_t rows = kind == 0 ? kValuRows : kRowuRange;
     *krows = rows;
     *ksplit = (K + rows - 1) / rows;
     return;
@@ -1383,9 +1493,8 @@ void gemm_plan_kind(uint32_t kind, uint32_t M, uint32_t K, uint32_t N, uint32_t 
   const uint64_t tiles = (uint64_t)(N / ncol) * ((M + MT - 1) / MT);
   uint64_t ks;
   if (kind == 3) {
-    // Resident k_gemm_mfmau workgroups (kSlots*: two per CU for the 16-row
-    // tile, one for the others). Fill the slots in one round: a partial
-    // second round doubles the time.
+    // Resident k_gemm_mfmau workgroups (kSlots*: one per CU). Fill the
+    // slots in one round: a partial second round doubles the time.
     const uint64_t slots = MT == 128 ? kSlots128 : MT == 64 ? kSlots64 : (MT == 16 ? kSlots16 : kSlots32);
     ks = tiles >= slots ? 1 : slots / tiles;
     if (ks >= 8) ks &= ~7ull;   // whole XCD groups (xcd_strip_range)
@@ -1655,6 +1764,10 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
   const uint32_t kind = gemm_kind(a.M, dense, a.log2b, a.total);
   gemm_plan_kind(kind, a.M, a.K, a.N, &a.ksplit, &a.krows);
   hipError_t e;
+  // arrival counters (in-kernel split-K reduction): the small-M kernel only.
+  // (The MFMA kernels' last workgroup of a strip would add up to 256 KB of
+  // slices alone; measured slower than the reduction kernel at every M.)
+  if (kind != 1 || a.ksplit == 1) a.counters = nullptr;
   if (kind == 1)
     e = launch_rowu(a, s);
   else if (kind == 0)
@@ -1663,7 +1776,7 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
     e = dense ? launch_mfmau<true>(a, s) : launch_mfmau<false>(a, s);
   else
     e = dense ? launch_mfma<true>(a, s) : launch_mfma<false>(a, s);
-  if (e != hipSuccess || a.ksplit == 1 || (kind == 1 && a.counters)) return e;
+  if (e != hipSuccess || a.ksplit == 1 || a.counters) return e;
   return launch_splitk_reduce(a, s);
 }
 
