@@ -209,6 +209,11 @@ enc_info coded_info(uint64_t n, uint32_t block_size, const Layout &L, uint64_t p
 // dispatched in order). ENC_LOOKBACK_SPINS overrides it; 0 makes every
 // tile after the first give up at once, so tests take the fallback path
 // deterministically.
+#ifndef ENC_SHORT_SLEEP_TILES
+#define ENC_SHORT_SLEEP_TILES 4096
+#endif
+constexpr uint64_t kShortSleepTiles = ENC_SHORT_SLEEP_TILES;
+
 uint32_t lookback_spin_limit() {
   const char *v = getenv("ENC_LOOKBACK_SPINS");
   if (v && v[0]) return (uint32_t)strtoul(v, nullptr, 10);
@@ -243,6 +248,10 @@ enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_si
   a.ws_total = reinterpret_cast<uint64_t *>(d_ws + status_bytes);
   a.error = reinterpret_cast<uint32_t *>(d_ws + status_bytes + 12);
   a.spin_limit = lookback_spin_limit();
+  // one tensor of at most kShortSleepTiles workgroups: poll after a short
+  // sleep (the spin limit scaled so a wait still gives up after ~0.1 s)
+  a.short_sleep = a.ntiles <= kShortSleepTiles;
+  if (a.short_sleep && a.spin_limit < (1u << 27)) a.spin_limit *= 16;
   hipError_t e = hipMemsetAsync(d_ws, 0, status_bytes + 16, s);
   if (e != hipSuccess) return hip_fail(e, "look-back state initialisation");
   e = launch_encode_onepass(a, s);

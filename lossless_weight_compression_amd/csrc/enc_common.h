@@ -138,6 +138,7 @@ struct EncodeArgs {
   uint64_t *status;      // one word per tile: flag (bits 63..62) | payload bytes
   uint32_t *error;       // nonzero: a look-back wait gave up
   uint32_t spin_limit;   // polls of a not-yet-published tile before giving up
+  uint32_t short_sleep;  // 1: poll the look-back window after a short sleep (small launches)
   uint64_t cap;          // output capacity: payload stores beyond it are dropped
   uint64_t ntiles;
 };

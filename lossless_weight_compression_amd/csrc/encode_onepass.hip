@@ -71,6 +71,9 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 // overlapping it.
 #define ENC_GLOBAL __attribute__((address_space(1)))
 typedef ENC_GLOBAL uint64_t gu64;
+#ifndef ENC_SHORT_SLEEP
+#define ENC_SHORT_SLEEP 8
+#endif
 typedef ENC_GLOBAL uint32_t gu32;
 
 __device__ __forceinline__ void publish(gu64 *status, uint64_t tile, uint64_t word) {
@@ -91,7 +94,7 @@ __device__ __forceinline__ uint64_t window_word(gu64 *status, int64_t top, uint3
 // (about 3 microseconds) and reads it again. `first` is the caller's read of the first
 // window (top = tile - 1), issued early so that its latency overlaps work.
 __device__ uint64_t look_back(gu64 *status, uint64_t tile, uint32_t lane, gu32 *error,
-                              uint32_t spin_limit, uint64_t first) {
+                              uint32_t spin_limit, uint32_t short_sleep, uint64_t first) {
   uint64_t excl = 0;
   int64_t top = (int64_t)tile - 1;
   uint32_t spins = 0;
@@ -112,11 +115,20 @@ __device__ uint64_t look_back(gu64 *status, uint64_t tile, uint32_t lane, gu32 *
         if (lane == 0) __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return 0;
       }
-      // the longest sleep (127 x 64 clocks): waiting workgroups re-read
-      // their window rarely, so their polls do not crowd the memory system
+      // Large launches: the longest sleep (127 x 64 clocks), so that the
+      // polls of many waiting workgroups do not crowd the memory system
       // (measured on the 8B-shaped set, batched: sleep 1 6.77 ms, 32 6.41,
-      // 64 6.20, 127 5.95, two of 127 6.13)
-      __builtin_amdgcn_s_sleep(127);
+      // 64 6.20, 127 5.95, two of 127 6.13). Small launches (one tensor of
+      // a few thousand tiles) poll after a short one: their few waiting
+      // workgroups cost the memory system little, and each long sleep sat on
+      // the tensor's critical path (4.2M-value tensor, 512 tiles: kernel
+      // 12.2 -> 9.0 us; sleeps of 2, 8 and 32 x 64 clocks measured alike).
+      // (Walking back with the whole workgroup, 256 tiles per round trip,
+      // was slower: 11.3 us.)
+      if (short_sleep)
+        __builtin_amdgcn_s_sleep(ENC_SHORT_SLEEP);
+      else
+        __builtin_amdgcn_s_sleep(127);
       v = window_word(status, top, lane);
       continue;
     }
@@ -365,7 +377,8 @@ __device__ __forceinline__ void onepass_tile(const EncodeArgs &a, uint64_t tile)
   // the workgroup's payload offset
   if (wave == 0) {
     const uint32_t agg = s_run;
-    const uint64_t excl = look_back(status, tile, lane, (gu32 *)a.error, a.spin_limit, lb_first);
+    const uint64_t excl = look_back(status, tile, lane, (gu32 *)a.error, a.spin_limit, a.short_sleep,
+                                    lb_first);
     if (lane == 0) {
       if (tile > 0) publish(status, tile, kFlagPre | (excl + agg));
       if (tile + 1 == a.ntiles) *(gu64 *)a.ws_total = excl + agg;
