@@ -380,6 +380,32 @@ def bench_wide(enc, synth, torch, np, dev, stream, args):
                      (S * info.n_elems + 7) // 8 + 2 * info.n_blocks + 8 * info.n_segments
                      + info.payload_bytes)
             del x, comp
+        # the same tensors in one batched single-pass launch (inputs
+        # regenerated, outputs and workspace allocated once): wall clock per
+        # call, host synchronisations included; every stream must equal the
+        # per-tensor one
+        xs = [synth.set8b_tensor_gpu_dt(i, dt, device=dev).reshape(-1) for i in idx]
+        bouts = [torch.empty(enc.enc_compress_bound_dt(x.numel(), dt), dtype=torch.uint8, device=dev)
+                 for x in xs]
+        bws = None
+        batch_ms = []
+        for rep in range(4):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            bres = enc.enc_compress_batch_dt(xs, dt, B, outs=bouts, ws=bws)
+            torch.cuda.synchronize()
+            if rep:
+                batch_ms.append((time.perf_counter() - t0) * 1e3)
+            if bws is None:
+                bws = torch.empty(max(int(enc.lib().enc_compress_batch_workspace_bytes(
+                    enc._citems(xs, bouts), len(xs), B)), 16), dtype=torch.uint8, device=dev)
+        for (bc, binf), (c, inf) in zip(bres, streams):
+            if binf.total_bytes != inf.total_bytes or not torch.equal(bc, c):
+                log("MISMATCH: batched %s stream differs from the per-tensor one" % name)
+                sys.exit(1)
+        bms = sorted(batch_ms)[len(batch_ms) // 2]
+        del xs, bouts, bws, bres
+        torch.cuda.empty_cache()
         outs = [torch.empty(inf.n_elems, dtype=torch.int16 if dt == 2 else torch.int32,
                             device=dev) for _, inf in streams]
         table = enc.enc_batch_prepare([(c, inf, o) for (c, inf), o in zip(streams, outs)])
@@ -413,14 +439,17 @@ def bench_wide(enc, synth, torch, np, dev, stream, args):
             "elements": n_total,
             "compression_ratio": round(out_bytes / comp_total, 5),
             "encode_gbs": round((out_bytes + comp_total) / (enc_ms * 1e-3) / 1e9, 1),
+            "encode_batch_ms": round(bms, 4),
+            "encode_batch_gbs": round((out_bytes + comp_total) / (bms * 1e-3) / 1e9, 1),
             "decode_ms_per_step": round(ms, 4),
             "out_gbs": round(out_bytes / (ms * 1e-3) / 1e9, 1),
             "hbm_gbs": round((read + out_bytes) / (ms * 1e-3) / 1e9, 1),
             "per_tensor_launch_ms_per_step": round(pt_ms, 4),
         }
-        log("%s: ratio %.4f, encode %.1f ms, decode %.3f ms/step (%.1f GB/s HBM; per-tensor "
-            "launches %.3f ms), bit-exact" % (name, res[name]["compression_ratio"], enc_ms, ms,
-                                             res[name]["hbm_gbs"], pt_ms))
+        log("%s: ratio %.4f, encode %.1f ms per tensor call / %.2f ms batched (%.1f GB/s), "
+            "decode %.3f ms/step (%.1f GB/s HBM; per-tensor launches %.3f ms), bit-exact"
+            % (name, res[name]["compression_ratio"], enc_ms, bms, res[name]["encode_batch_gbs"], ms,
+               res[name]["hbm_gbs"], pt_ms))
         del streams, outs, table
         torch.cuda.empty_cache()
     return res

@@ -138,10 +138,13 @@ uint64_t enc_compress_bound_dt(uint64_t n_elems, uint32_t dtype);
 
 /* Compress n values of the given dtype (bit patterns, 2 bytes each for BF16
  * and FP16, 4 for FP32) -- the block code above with the element type's
- * exponent and kept fields. dtype 1 is enc_compress_ex. For FP16 and FP32:
- * a width kernel, the scan of segment sizes, one synchronisation of
- * `stream` to read back the size, then the pack kernel (the input is read
- * twice). Same block sizes, options, workspace size
+ * exponent and kept fields. dtype 1 is enc_compress_ex. FP16 and FP32 take
+ * the same single pass (decoupled look-back) as BF16 when out_capacity holds
+ * the RAW size (enc_compress_bound_dt), with one synchronisation of `stream`
+ * to read back the size; otherwise, or should a look-back wait give up, a
+ * width kernel, the scan of segment sizes, the synchronisation, then the
+ * pack kernel (the input read twice). Either way the bytes are the ones the
+ * format prescribes. Same block sizes, options, workspace size
  * (enc_compress_workspace_bytes) and capacity rule (the final stream size;
  * enc_compress_bound_dt always suffices). Unknown dtype:
  * ENC_ERR_UNSUPPORTED. */
@@ -183,6 +186,18 @@ uint64_t enc_compress_batch_workspace_bytes(const enc_citem *h_items, int count,
 enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t block_size,
                               uint32_t options, void *d_ws, uint64_t ws_bytes, void *stream,
                               enc_info *h_infos);
+
+/* enc_compress_batch for items of one dtype (1 BF16 -- enc_compress_batch
+ * --, 2 FP16, 3 FP32; ENEC Abstract, as enc_compress_dt): each item's d_in
+ * holds n_elems values of that dtype and its out_capacity at least
+ * enc_compress_bound_dt(n_elems, dtype); the workspace is
+ * enc_compress_batch_workspace_bytes of the same items. Each item's stream
+ * is byte-identical to what enc_compress_dt writes for it; items whose
+ * look-back wait gave up are re-encoded with enc_compress_dt. Unknown dtype:
+ * ENC_ERR_UNSUPPORTED. */
+enc_status enc_compress_batch_dt(const enc_citem *h_items, int count, uint32_t dtype,
+                                 uint32_t block_size, uint32_t options, void *d_ws, uint64_t ws_bytes,
+                                 void *stream, enc_info *h_infos);
 
 /* Parse and check a stream header held in host memory (header_bytes >= 256)
  * for a stream of comp_bytes bytes. Checks magic, version, dtype, flags,

@@ -225,14 +225,15 @@ uint32_t lookback_spin_limit() {
 // land outside the buffer and the RAW fallback can simply overwrite it.
 // Returns ENC_ERR_HIP with *gave_up set if a look-back wait gave up; the
 // caller then runs the two-pass encoder, which rewrites every byte.
-enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_size, uint32_t pow2,
-                             const Layout &L, uint8_t *d_out, uint64_t cap, uint8_t *d_ws,
-                             hipStream_t s, enc_info *h_info, bool *gave_up) {
+enc_status compress_one_pass(const void *d_in, uint64_t n, uint32_t dtype, uint32_t block_size,
+                             uint32_t pow2, const Layout &L, uint8_t *d_out, uint64_t cap,
+                             uint8_t *d_ws, hipStream_t s, enc_info *h_info, bool *gave_up) {
   *gave_up = false;
   EncodeArgs a;
   memset(&a, 0, sizeof a);
   a.pow2 = pow2;
-  a.in = d_in;
+  a.dtype = dtype;
+  a.in = static_cast<const uint16_t *>(d_in);
   a.out = d_out;
   a.n = n;
   a.nb = L.nb;
@@ -254,7 +255,7 @@ enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_si
   if (a.short_sleep && a.spin_limit < (1u << 27)) a.spin_limit *= 16;
   hipError_t e = hipMemsetAsync(d_ws, 0, status_bytes + 16, s);
   if (e != hipSuccess) return hip_fail(e, "look-back state initialisation");
-  e = launch_encode_onepass(a, s);
+  e = dtype == 1 ? launch_encode_onepass(a, s) : launch_encode_wide_onepass(a, s);
   if (e != hipSuccess) return hip_fail(e, "single-pass kernel launch");
   uint64_t back[2] = {0, 0};   // payload bytes; (unused) | error << 32
   e = hipMemcpyAsync(back, a.ws_total, sizeof back, hipMemcpyDeviceToHost, s);
@@ -266,14 +267,16 @@ enc_status compress_one_pass(const uint16_t *d_in, uint64_t n, uint32_t block_si
     return fail(ENC_ERR_HIP, "single-pass encoder: a look-back wait gave up");
   }
   const uint64_t payload = back[0];
-  const uint64_t raw_total = kHeaderBytes + 2 * n;
+  const uint64_t raw_total = kHeaderBytes + elem_bytes(dtype) * n;
   enc_info i;
   enc_status st;
   if (L.payload_off + payload >= raw_total) {
-    i = raw_info(n, block_size);
-    st = launched(launch_encode_raw(d_in, d_out, n, header_of(i), s), s, "raw copy launch");
+    i = raw_info(n, block_size, dtype);
+    // the verbatim copy moves 16-bit units
+    st = launched(launch_encode_raw(a.in, d_out, n * (elem_bytes(dtype) / 2), header_of(i), s), s,
+                  "raw copy launch");
   } else {
-    i = coded_info(n, block_size, L, payload, a.pow2);
+    i = coded_info(n, block_size, L, payload, a.pow2, dtype);
     st = launched(launch_encode_pads(a, header_of(i), s), s, "header kernel launch");
   }
   if (st != ENC_OK) return st;
@@ -452,7 +455,7 @@ enc_status enc_compress_ex(const uint16_t *d_in, uint64_t n, uint32_t block_size
   const Layout L = layout_of(n, block_size);
   if (out_capacity >= raw_total && L.payload_off <= raw_total) {
     bool gave_up = false;
-    const enc_status st = compress_one_pass(d_in, n, block_size, pow2, L,
+    const enc_status st = compress_one_pass(d_in, n, 1, block_size, pow2, L,
                                             static_cast<uint8_t *>(d_out), out_capacity,
                                             static_cast<uint8_t *>(d_ws), s, h_info, &gave_up);
     if (!gave_up) return st;
@@ -544,6 +547,18 @@ enc_status enc_compress_dt(const void *d_in, uint64_t n, uint32_t dtype, uint32_
   const uint64_t need_ws = enc_compress_workspace_bytes(n, block_size);
   if (!d_ws || ws_bytes < need_ws)
     return fail(ENC_ERR_CAPACITY, "workspace of %llu bytes needed", (unsigned long long)need_ws);
+  // single pass when the output can hold the RAW size (as for BF16); the
+  // two-pass encoder when it cannot, or when a look-back wait gave up
+  const Layout L = layout_of(n, block_size, dtype);
+  const uint64_t raw_total = kHeaderBytes + elem_bytes(dtype) * n;
+  if (out_capacity >= raw_total && L.payload_off <= raw_total) {
+    bool gave_up = false;
+    const enc_status st = compress_one_pass(d_in, n, dtype, block_size, pow2, L,
+                                            static_cast<uint8_t *>(d_out), out_capacity,
+                                            static_cast<uint8_t *>(d_ws), s, h_info, &gave_up);
+    if (!gave_up) return st;
+    clear_err();
+  }
   return compress_wide(d_in, n, dtype, block_size, pow2, static_cast<uint8_t *>(d_out),
                        out_capacity, static_cast<uint8_t *>(d_ws), s, h_info);
 }
@@ -559,10 +574,12 @@ uint64_t enc_compress_batch_workspace_bytes(const enc_citem *h_items, int count,
   return need;
 }
 
-enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t block_size,
-                              uint32_t options, void *d_ws, uint64_t ws_bytes, void *stream,
-                              enc_info *h_infos) {
+enc_status enc_compress_batch_dt(const enc_citem *h_items, int count, uint32_t dtype,
+                                 uint32_t block_size, uint32_t options, void *d_ws, uint64_t ws_bytes,
+                                 void *stream, enc_info *h_infos) {
   clear_err();
+  if (!dtype_known(dtype)) return fail(ENC_ERR_UNSUPPORTED, "dtype %u (1 BF16, 2 FP16, 3 FP32)", dtype);
+  const uint64_t eb = elem_bytes(dtype);
   if (options & ~(uint32_t)ENC_OPT_POW2_WIDTHS)
     return fail(ENC_ERR_INVALID_ARG, "unknown options 0x%x", options);
   const uint32_t pow2 = (options & ENC_OPT_POW2_WIDTHS) ? 1u : 0u;
@@ -582,10 +599,10 @@ enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t bloc
     if (it.n_elems > kMaxElems) return fail(ENC_ERR_UNSUPPORTED, "item %d: n above 2^40", k);
     if (!aligned16(it.d_in) || !aligned16(it.d_out))
       return fail(ENC_ERR_INVALID_ARG, "item %d: device buffers must be 16-byte aligned", k);
-    if (it.out_capacity < kHeaderBytes + 2 * it.n_elems)
+    if (it.out_capacity < kHeaderBytes + eb * it.n_elems)
       return fail(ENC_ERR_CAPACITY, "item %d: output capacity %llu below the RAW size %llu", k,
                   (unsigned long long)it.out_capacity,
-                  (unsigned long long)(kHeaderBytes + 2 * it.n_elems));
+                  (unsigned long long)(kHeaderBytes + eb * it.n_elems));
     total_wgs += onepass_batch_tiles(it.n_elems);
   }
   // one launch: the grid's work-item count (256 per workgroup) is a u32
@@ -613,14 +630,15 @@ enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t bloc
       raw_items.push_back(k);
       continue;
     }
-    const Layout L = layout_of(n, block_size);
-    if (L.payload_off > kHeaderBytes + 2 * n) {
+    const Layout L = layout_of(n, block_size, dtype);
+    if (L.payload_off > kHeaderBytes + eb * n) {
       raw_items.push_back(k);
       continue;
     }
     EncodeArgs &a = targs[coded_items.size()];
     memset(&a, 0, sizeof a);
     a.pow2 = pow2;
+    a.dtype = dtype;
     a.in = it.d_in;
     a.out = static_cast<uint8_t *>(it.d_out);
     a.n = n;
@@ -657,7 +675,8 @@ enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t bloc
     if (e != hipSuccess) return hip_fail(e, "look-back state initialisation");
     e = hipMemcpyAsync(ws + W.table, table.data(), table.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "batch table upload");
-    e = launch_encode_onepass_batch(ws + W.table, wgs, s);
+    e = dtype == 1 ? launch_encode_onepass_batch(ws + W.table, wgs, s)
+                   : launch_encode_wide_onepass_batch(ws + W.table, wgs, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "batched single-pass kernel launch");
     e = hipMemcpyAsync(back.data(), ws + W.results, 16 * (uint64_t)nc, hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return hip_fail(e, "size read-back");
@@ -677,12 +696,12 @@ enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t bloc
       continue;
     }
     const uint64_t payload = back[2 * c];
-    const Layout L = layout_of(n, block_size);
-    if (L.payload_off + payload >= kHeaderBytes + 2 * n) {
+    const Layout L = layout_of(n, block_size, dtype);
+    if (L.payload_off + payload >= kHeaderBytes + eb * n) {
       raw_items.push_back(k);
       continue;
     }
-    h_infos[k] = coded_info(n, block_size, L, payload, pow2);
+    h_infos[k] = coded_info(n, block_size, L, payload, pow2, dtype);
     PadsItem p;
     p.a = targs[c];
     p.h = header_of(h_infos[k]);
@@ -698,9 +717,10 @@ enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t bloc
   }
   for (const int k : raw_items) {
     const enc_citem &it = h_items[k];
-    const enc_info i = raw_info(it.n_elems, block_size);
+    const enc_info i = raw_info(it.n_elems, block_size, dtype);
+    // the verbatim copy moves 16-bit units
     const enc_status st = launched(launch_encode_raw(it.d_in, static_cast<uint8_t *>(it.d_out),
-                                                     it.n_elems, header_of(i), s),
+                                                     it.n_elems * (eb / 2), header_of(i), s),
                                    s, "raw copy launch");
     if (st != ENC_OK) return st;
     h_infos[k] = i;
@@ -710,11 +730,18 @@ enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t bloc
   if (e != hipSuccess) return hip_fail(e, "stream synchronize");
   for (const int k : retry) {
     const enc_citem &it = h_items[k];
-    const enc_status st = enc_compress_ex(it.d_in, it.n_elems, block_size, options, it.d_out,
+    const enc_status st = enc_compress_dt(it.d_in, it.n_elems, dtype, block_size, options, it.d_out,
                                           it.out_capacity, d_ws, ws_bytes, stream, &h_infos[k]);
     if (st != ENC_OK) return st;
   }
   return ENC_OK;
+}
+
+enc_status enc_compress_batch(const enc_citem *h_items, int count, uint32_t block_size,
+                              uint32_t options, void *d_ws, uint64_t ws_bytes, void *stream,
+                              enc_info *h_infos) {
+  return enc_compress_batch_dt(h_items, count, 1, block_size, options, d_ws, ws_bytes, stream,
+                               h_infos);
 }
 
 enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_t comp_bytes,

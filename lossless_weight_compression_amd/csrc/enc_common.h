@@ -134,6 +134,7 @@ struct EncodeArgs {
   uint64_t meta_off, segoff_off, payload_off;
   uint32_t log2b;
   uint32_t pow2;         // 1: widths rounded up to 0, 1, 2, 4 or 8
+  uint32_t dtype;        // 1 (or 0) BF16, 2 FP16, 3 FP32: the single pass and its pads
   // single pass only
   uint64_t *status;      // one word per tile: flag (bits 63..62) | payload bytes
   uint32_t *error;       // nonzero: a look-back wait gave up
@@ -144,6 +145,10 @@ struct EncodeArgs {
 };
 hipError_t launch_encode_params(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_encode_onepass(const EncodeArgs &a, hipStream_t s);
+// FP16 / FP32 single pass (a.dtype 2 or 3), one stream or a batch of one dtype
+hipError_t launch_encode_wide_onepass(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_encode_wide_onepass_batch(const void *table, uint64_t total_wgs, uint32_t dtype,
+                                            hipStream_t s);
 hipError_t launch_encode_scan(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_encode_pack(const EncodeArgs &a, hipStream_t s);
 

@@ -426,12 +426,300 @@ __global__ __launch_bounds__(kThreads) void k_enc_onepass_batch(const uint8_t *_
   onepass_tile<kOnePassMaxSub>(a, b - begin[lo]);
 }
 
+// ---------------------------------------------------------------------------
+// FP16 (DT 2) and FP32 (DT 3) input in one pass: the same tile schedule,
+// block parameters and decoupled look-back as the BF16 tile above, with the
+// other float layouts' fields (FP16: 5 exponent bits, the sign and 10
+// mantissa bits kept as an 11-bit field; FP32: 8 exponent bits, a 24-bit
+// kept field). A group of 8 values owns exactly 11 or 24 bytes of the kept
+// section, so each sub-tile's kept fields are assembled in a zeroed LDS image
+// (fixed position in the stream: no look-back needed) and leave with 16-byte
+// stores while the codes collect in the workgroup's payload image.
+// ---------------------------------------------------------------------------
+template <uint32_t DT>
+struct WideField {
+  static constexpr uint32_t kBytes = DT == 3 ? 4 : 2;     // input bytes per value
+  static constexpr uint32_t kSmBits = DT == 3 ? 24 : 11;  // kept bits per value
+  static constexpr uint32_t kShift = DT == 3 ? 23 : 10;   // exponent position
+  static constexpr uint32_t kExpMask = DT == 3 ? 0xFFu : 0x1Fu;
+  static constexpr uint32_t kChunks = DT == 3 ? 2 : 1;    // 16-byte loads per group
+};
+
+// Value k of a group loaded as WideField<DT>::kChunks 16-byte pieces.
+template <uint32_t DT>
+__device__ __forceinline__ uint32_t wide_value(const uint4 (&r)[WideField<DT>::kChunks], uint32_t k) {
+  if (DT == 3) {
+    const uint4 &c = r[(k >> 2) & (WideField<DT>::kChunks - 1)];
+    const uint32_t j = k & 3;
+    return j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
+  }
+  const uint32_t j = k >> 1;
+  const uint32_t d = j == 0 ? r[0].x : j == 1 ? r[0].y : j == 2 ? r[0].z : r[0].w;
+  return (d >> (16 * (k & 1))) & 0xFFFFu;
+}
+
+template <uint32_t DT, uint32_t SUB>
+__device__ __forceinline__ void onepass_tile_wide(const EncodeArgs &a, uint64_t tile) {
+  typedef WideField<DT> F;
+  constexpr uint32_t CH = F::kChunks;
+  constexpr uint32_t kPayBytes = SUB * kTileGroups * 8 + 16;   // a tile's payload, at most
+  constexpr uint32_t kTileSm = kTileGroups * F::kSmBits;       // kept bytes of a sub-tile (x16)
+  __shared__ __attribute__((aligned(16))) uint32_t pay[kPayBytes / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t smi[kTileSm / 4 + 4];
+  __shared__ uint32_t smin[64], smax[64], sblk[64], s_suboff[SUB];
+  __shared__ uint64_t s_excl;
+  __shared__ uint32_t s_run;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t log2b = a.log2b, log2gpb = log2b - 3;
+  const uint32_t bps = (uint32_t)(kTileElems >> log2b);            // blocks per sub-tile
+  const uint64_t n = a.n;
+  const uint64_t start = tile * SUB * kTileElems;
+  const uint64_t left = n - start;
+  const uint64_t span_vals = left < SUB * kTileElems ? left : SUB * kTileElems;
+  const uint32_t nsub = (uint32_t)((span_vals + kTileElems - 1) / kTileElems);
+  const uint32_t span = (1u << log2gpb) < 64 ? (1u << log2gpb) : 64u;   // lanes of one block
+  const __amdgpu_buffer_rsrc_t in_rs =
+      range_rsrc(reinterpret_cast<const uint8_t *>(a.in) + F::kBytes * start, F::kBytes * span_vals);
+  const uint64_t sm_total = (F::kSmBits * n + 7) / 8;                  // bytes of kept fields
+  gu64 *const status = (gu64 *)a.status;
+  // FP16, n odd: the last value's dword straddles the input's end, so the
+  // range check reads it as 0; the value itself comes from this load
+  const uint32_t x_last = DT == 2 ? (uint32_t)*(const ENC_GLOBAL uint16_t *)(a.in + n - 1) : 0u;
+
+  if (tid < 64) {
+    smin[tid] = 255;
+    smax[tid] = 0;
+  }
+  if (tid == 0) s_run = 0;
+  for (uint32_t i = tid; i < kPayBytes / 16; i += kThreads)
+    reinterpret_cast<uint4 *>(pay)[i] = make_uint4(0, 0, 0, 0);
+  uint64_t lb_first = kFlagPre;   // wave 0: first look-back window, read early
+  uint4 g[kGroupsPerThread][CH], gn[kGroupsPerThread][CH];
+  uint32_t valid[kGroupsPerThread], vn[kGroupsPerThread];
+  // the groups of sub-tile `sub` (offsets from the tile start; past the
+  // tile every dword is out of the descriptor's range: zeros, no access)
+  auto load = [&](uint32_t sub, uint4 (&dst)[kGroupsPerThread][CH], uint32_t (&v)[kGroupsPerThread]) {
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+      const uint32_t e0 = (sub * kTileGroups + it * kThreads + tid) * 8;
+#pragma unroll
+      for (uint32_t c = 0; c < CH; ++c) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(in_rs, F::kBytes * e0 + 16 * c, 0, 0);
+        dst[it][c] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+      v[it] = e0 < left ? (left - e0 < 8 ? (uint32_t)(left - e0) : 8u) : 0u;
+    }
+  };
+  load(0, g, valid);
+#pragma unroll 1
+  for (uint32_t sub = 0; sub < nsub; ++sub) {
+    const uint64_t st = tile * SUB + sub;                  // global sub-tile index
+    const uint64_t blk0 = st * bps;
+    load(sub + 1, gn, vn);                                 // next sub-tile, in flight
+    lds_barrier();   // previous sub-tile packed and stored (sblk, smi free), min/max reset
+    for (uint32_t i = tid; i < kTileSm / 16; i += kThreads)
+      reinterpret_cast<uint4 *>(smi)[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it)
+      if (DT == 2 && (valid[it] & 1)) {   // value v - 1 alone in the low half of dword (v - 1) / 2
+        const uint32_t j = (valid[it] - 1) >> 1;
+        uint4 &c = g[it][0];
+        c.x = j == 0 ? x_last : c.x;
+        c.y = j == 1 ? x_last : c.y;
+        c.z = j == 2 ? x_last : c.z;
+        c.w = j == 3 ? x_last : c.w;
+      }
+
+    // per-block min / max exponent over the valid values
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+      uint32_t mn = 255, mx = 0;
+#pragma unroll
+      for (uint32_t k = 0; k < 8; ++k) {
+        const uint32_t e = (wide_value<DT>(g[it], k) >> F::kShift) & F::kExpMask;
+        mn = k < valid[it] && e < mn ? e : mn;
+        mx = k < valid[it] && e > mx ? e : mx;
+      }
+      uint32_t key = valid[it] ? ((255u - mn) << 16) | mx : 0u;   // 0: no valid value here
+      key = span_max16(key, span);
+      const uint32_t q = it * kThreads + tid;
+      if ((lane & (span - 1)) == span - 1 && key != 0) {
+        atomicMin(&smin[q >> log2gpb], 255u - (key >> 16));
+        atomicMax(&smax[q >> log2gpb], key & 0xFFFFu);
+      }
+    }
+    lds_barrier();
+
+    // block parameters, metas, offsets inside the workgroup's payload
+    if (wave == 0) {
+      const uint64_t blk = blk0 + lane;
+      uint32_t P = 0, base = 0, w = 0;
+      if (lane < bps && blk < a.nb) {
+        base = smin[lane];
+        w = block_width(smax[lane] - base, a.pow2);
+        const uint32_t L = (blk + 1 == a.nb) ? (uint32_t)(n - ((a.nb - 1) << log2b)) : (1u << log2b);
+        P = (((w * L + 7) >> 3) + 15) & ~15u;
+      }
+      const __amdgpu_buffer_rsrc_t meta_rs = range_rsrc(
+          a.out + a.meta_off + 2 * blk0, align_up(2 * (a.nb - blk0 < bps ? a.nb - blk0 : bps), 4));
+      const uint32_t mw = base | (w << 8);
+      const uint32_t pair = mw | (__shfl_down(mw, 1, 64) << 16);
+      if (!(lane & 1)) __builtin_amdgcn_raw_buffer_store_b32(pair, meta_rs, 2 * lane, 0, 0);
+      smin[lane] = 255;
+      smax[lane] = 0;
+      const uint32_t run = s_run;
+      const uint32_t incl = wave_incl_scan(P);
+      const uint32_t sub_total = __builtin_amdgcn_readlane(incl, 63);
+      sblk[lane] = base | (w << 8) | ((run + incl - P) << 16);
+      if (lane == 0) {
+        s_suboff[sub] = run;
+        s_run = run + sub_total;
+      }
+      if (sub + 1 == nsub) {
+        if (lane == 0) publish(status, tile, (tile == 0 ? kFlagPre : kFlagAgg) | (run + sub_total));
+        lb_first = window_word(status, (int64_t)tile - 1, lane);
+      }
+    }
+    lds_barrier();
+
+    // codes into the payload image, kept fields into the sub-tile's image
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+      const uint32_t q = it * kThreads + tid;
+      const uint32_t v = valid[it];
+      if (!v) continue;
+      const uint32_t info = sblk[q >> log2gpb];
+      const uint32_t base = info & 0xFFu, w = (info >> 8) & 0xFFu;
+      uint32_t f[8];
+      unsigned long long codes = 0;
+#pragma unroll
+      for (uint32_t k = 0; k < 8; ++k) {
+        const uint32_t x = wide_value<DT>(g[it], k);
+        const uint32_t e = (x >> F::kShift) & F::kExpMask;
+        constexpr uint32_t top = F::kBytes * 8 - 1;
+        f[k] = k < v ? ((x >> top) << F::kShift) | (x & ((1u << F::kShift) - 1)) : 0u;
+        if (k < v) codes |= (unsigned long long)(e - base) << (k * w);
+      }
+      const uint32_t pos = (info >> 16) + (q & ((1u << log2gpb) - 1)) * w;
+      const uint32_t lo = (uint32_t)codes, hi = (uint32_t)(codes >> 32);
+      const uint32_t sh = (pos & 3) * 8, d0 = pos >> 2;
+      const uint32_t w0 = lo << sh;
+      const uint32_t w1 = sh ? (lo >> (32 - sh)) | (hi << sh) : hi;
+      const uint32_t w2 = sh ? hi >> (32 - sh) : 0u;
+      if (w0) atomicOr(&pay[d0], w0);
+      if (w1) atomicOr(&pay[d0 + 1], w1);
+      if (w2) atomicOr(&pay[d0 + 2], w2);
+      if (DT == 3) {
+        // 24 bytes at byte 24 q: six whole dwords, this lane's alone
+        uint32_t *d = smi + 6 * q;
+        d[0] = f[0] | f[1] << 24;
+        d[1] = f[1] >> 8 | f[2] << 16;
+        d[2] = f[2] >> 16 | f[3] << 8;
+        d[3] = f[4] | f[5] << 24;
+        d[4] = f[5] >> 8 | f[6] << 16;
+        d[5] = f[6] >> 16 | f[7] << 8;
+      } else {
+        // 88 bits at bit 88 q, OR-ed into the four dwords they can touch
+        // (the first and last are shared with the neighbouring groups)
+        const unsigned long long fl = (unsigned long long)f[0] | (unsigned long long)f[1] << 11 |
+                                      (unsigned long long)f[2] << 22 | (unsigned long long)f[3] << 33 |
+                                      (unsigned long long)f[4] << 44 | (unsigned long long)f[5] << 55;
+        const uint32_t fh = f[5] >> 9 | f[6] << 2 | f[7] << 13;   // bits 64..87
+        const uint32_t v0 = (uint32_t)fl, v1 = (uint32_t)(fl >> 32), v2 = fh;
+        const uint32_t bit = 88 * q, e0 = bit >> 5, s5 = bit & 31;   // s5 is 0, 8, 16 or 24
+        const uint32_t x0 = v0 << s5;
+        const uint32_t x1 = s5 ? (v0 >> (32 - s5)) | (v1 << s5) : v1;
+        const uint32_t x2 = s5 ? (v1 >> (32 - s5)) | (v2 << s5) : v2;
+        const uint32_t x3 = s5 ? v2 >> (32 - s5) : 0u;
+        if (x0) atomicOr(&smi[e0], x0);
+        if (x1) atomicOr(&smi[e0 + 1], x1);
+        if (x2) atomicOr(&smi[e0 + 2], x2);
+        if (x3) atomicOr(&smi[e0 + 3], x3);
+      }
+    }
+    lds_barrier();
+    // the sub-tile's kept fields (16-byte aligned: 1024 x 11 and 1024 x 24
+    // are multiples of 16); bytes past the section's last field are not
+    // written
+    const uint64_t sm0 = (uint64_t)kTileSm * st;
+    const uint32_t len = (uint32_t)(sm_total - sm0 < kTileSm ? sm_total - sm0 : kTileSm);
+    uint8_t *sdst = a.out + kHeaderBytes + sm0;
+    for (uint32_t i = tid; i < len / 16; i += kThreads) {
+      const uint4 d = reinterpret_cast<const uint4 *>(smi)[i];
+      store_nt16(sdst + 16 * i, d);
+    }
+    if (tid < (len & 15)) {
+      const uint32_t b = (len & ~15u) + tid;
+      sdst[b] = reinterpret_cast<const uint8_t *>(smi)[b];
+    }
+#pragma unroll
+    for (uint32_t it = 0; it < kGroupsPerThread; ++it) {
+#pragma unroll
+      for (uint32_t c = 0; c < CH; ++c) g[it][c] = gn[it][c];
+      valid[it] = vn[it];
+    }
+  }
+  lds_barrier();
+
+  // the workgroup's payload offset
+  if (wave == 0) {
+    const uint32_t agg = s_run;
+    const uint64_t excl = look_back(status, tile, lane, (gu32 *)a.error, a.spin_limit, a.short_sleep,
+                                    lb_first);
+    if (lane == 0) {
+      if (tile > 0) publish(status, tile, kFlagPre | (excl + agg));
+      if (tile + 1 == a.ntiles) *(gu64 *)a.ws_total = excl + agg;
+      s_excl = excl;
+    }
+    if (lane < nsub && (((tile * SUB + lane) * bps) & 63) == 0)   // segment starts
+      *(gu64 *)(a.out + a.segoff_off + 8 * (((tile * SUB + lane) * bps) >> 6)) = excl + s_suboff[lane];
+  }
+  lds_barrier();
+
+  // payload out
+  const uint64_t dst = a.payload_off + s_excl;
+  const __amdgpu_buffer_rsrc_t pay_rs = range_rsrc(a.out + dst, a.cap > dst ? a.cap - dst : 0);
+  for (uint32_t i = tid; i < s_run / 16; i += kThreads) {
+    const uint4 d = reinterpret_cast<const uint4 *>(pay)[i];
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){d.x, d.y, d.z, d.w}, pay_rs, 16 * i, 0, kStoreNT);
+  }
+}
+
+template <uint32_t DT, uint32_t SUB>
+__global__ __launch_bounds__(kThreads) void k_encw_onepass(EncodeArgs a) {
+  onepass_tile_wide<DT, SUB>(a, blockIdx.x);
+}
+
+// Many FP16 or FP32 streams (one dtype per launch) in one launch, as
+// k_enc_onepass_batch.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_encw_onepass_batch(const uint8_t *__restrict__ table) {
+  const EncBatchHeader *h = reinterpret_cast<const EncBatchHeader *>(table);
+  const uint32_t count = h->count;
+  const EncodeArgs *items = reinterpret_cast<const EncodeArgs *>(table + sizeof(EncBatchHeader));
+  const uint64_t *begin = reinterpret_cast<const uint64_t *>(table + sizeof(EncBatchHeader) +
+                                                             count * sizeof(EncodeArgs));
+  const uint64_t b = blockIdx.x;
+  uint32_t lo = 0, hi = count;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (begin[mid] <= b) lo = mid; else hi = mid;
+  }
+  const EncodeArgs a = items[lo];
+  onepass_tile_wide<DT, kOnePassMaxSub>(a, b - begin[lo]);
+}
+
 // Header and the zero padding of the sm, meta and segment-offset sections of
 // a stream the single pass wrote (threads tid, tid + stride, ...).
 __device__ __forceinline__ void pads_body(const EncodeArgs &a, const HeaderImage &h, uint64_t tid,
                                           uint64_t stride) {
   if (tid < 64) reinterpret_cast<uint32_t *>(a.out)[tid] = reinterpret_cast<const uint32_t *>(h.bytes)[tid];
-  const uint64_t sm_from = kHeaderBytes + align_up(a.n, 8), sm_to = a.meta_off;
+  // the single pass writes BF16 sign+mantissa bytes in whole groups, the
+  // wide types' kept fields up to the section's last byte
+  const uint64_t sm_from = kHeaderBytes + (a.dtype == 2   ? (11 * a.n + 7) / 8
+                                           : a.dtype == 3 ? 3 * a.n
+                                                          : align_up(a.n, 8)),
+                 sm_to = a.meta_off;
   const uint64_t meta_from = a.meta_off + 2 * a.nb, meta_to = a.segoff_off;
   const uint64_t seg_from = a.segoff_off + 8 * a.nseg, seg_to = a.payload_off;
   const uint64_t l0 = sm_to - sm_from, l1 = meta_to - meta_from, l2 = seg_to - seg_from;
@@ -458,6 +746,33 @@ hipError_t launch_encode_onepass(const EncodeArgs &a, hipStream_t s) {
     case 2: hipLaunchKernelGGL(k_enc_onepass<2>, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a); break;
     default: hipLaunchKernelGGL(k_enc_onepass<4>, dim3((uint32_t)a.ntiles), dim3(kThreads), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_wide_onepass(const EncodeArgs &a, hipStream_t s) {
+  const dim3 grid((uint32_t)a.ntiles), block(kThreads);
+  const uint32_t sub = onepass_sub(a.n);
+  if (a.dtype == 2) {
+    if (sub == 1) hipLaunchKernelGGL((k_encw_onepass<2, 1>), grid, block, 0, s, a);
+    else if (sub == 2) hipLaunchKernelGGL((k_encw_onepass<2, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_encw_onepass<2, 4>), grid, block, 0, s, a);
+  } else {
+    if (sub == 1) hipLaunchKernelGGL((k_encw_onepass<3, 1>), grid, block, 0, s, a);
+    else if (sub == 2) hipLaunchKernelGGL((k_encw_onepass<3, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_encw_onepass<3, 4>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_wide_onepass_batch(const void *table, uint64_t total_wgs, uint32_t dtype,
+                                            hipStream_t s) {
+  if (total_wgs == 0) return hipSuccess;
+  const dim3 grid((uint32_t)total_wgs), block(kThreads);
+  const uint8_t *t = static_cast<const uint8_t *>(table);
+  if (dtype == 2)
+    hipLaunchKernelGGL(k_encw_onepass_batch<2>, grid, block, 0, s, t);
+  else
+    hipLaunchKernelGGL(k_encw_onepass_batch<3>, grid, block, 0, s, t);
   return hipGetLastError();
 }
 

@@ -83,6 +83,8 @@ SIGNATURES = {
     "enc_compress_batch_workspace_bytes": (_U64, [ctypes.POINTER(EncCItem), ctypes.c_int, _U32]),
     "enc_compress_batch": (_ST, [ctypes.POINTER(EncCItem), ctypes.c_int, _U32, _U32, _VP, _U64, _VP,
                                  _INFO_P]),
+    "enc_compress_batch_dt": (_ST, [ctypes.POINTER(EncCItem), ctypes.c_int, _U32, _U32, _U32, _VP,
+                                    _U64, _VP, _INFO_P]),
     "enc_parse_header": (_ST, [_VP, _U64, _U64, _INFO_P]),
     "enc_read_info": (_ST, [_VP, _U64, _VP, _INFO_P]),
     "enc_decompress": (_ST, [_VP, _INFO_P, _VP, _U64, _VP]),
@@ -263,6 +265,32 @@ def enc_compress_batch(xs, block_size=512, outs=None, ws=None, stream=None, pow2
     _check(lib().enc_compress_batch(arr, len(xs), block_size,
                                     ENC_OPT_POW2_WIDTHS if pow2_widths else 0, _ptr(ws), ws.numel(),
                                     _stream(stream), infos))
+    return [(out[:infos[k].total_bytes], EncInfo.from_buffer_copy(infos[k]))
+            for k, out in enumerate(outs)]
+
+
+def enc_compress_batch_dt(xs, dtype, block_size=512, outs=None, ws=None, stream=None,
+                          pow2_widths=False):
+    """enc_compress_batch for tensors of one header element type (BF16, FP16
+    or FP32; every x must have that type's element size). Each result is
+    byte-identical to enc_compress of the same tensor."""
+    xs = [x.view(-1) for x in xs]
+    if not xs:
+        return []
+    for x in xs:
+        _dtype_of(x, dtype)
+    if outs is None:
+        outs = [_empty_u8(enc_compress_bound_dt(x.numel(), dtype), x.device) for x in xs]
+    if len(outs) != len(xs):
+        raise ValueError("outs must match xs")
+    arr = _citems(xs, outs)
+    if ws is None:
+        ws = _empty_u8(lib().enc_compress_batch_workspace_bytes(arr, len(xs), block_size),
+                       xs[0].device)
+    infos = (EncInfo * len(xs))()
+    _check(lib().enc_compress_batch_dt(arr, len(xs), dtype, block_size,
+                                       ENC_OPT_POW2_WIDTHS if pow2_widths else 0, _ptr(ws), ws.numel(),
+                                       _stream(stream), infos))
     return [(out[:infos[k].total_bytes], EncInfo.from_buffer_copy(infos[k]))
             for k, out in enumerate(outs)]
 

@@ -262,3 +262,61 @@ def _mixed_batch(E, orc, also_single):
             got = o2.cpu().numpy()
             got = got.view(np.uint32) if dt == 3 else got.view(np.uint16)
             assert np.array_equal(got, x), ("single", dt, x.size, info.flags)
+
+
+# ------------------------------------------------- single pass: batch, fallback
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_mid_size_single_pass(E, orc, dtype):
+    """12M values: the single-pass size class with two 8192-value sub-tiles
+    per workgroup (the smaller tests take one, the full layer four); the
+    stream equals the oracle's."""
+    n = 12 * 1024 * 1024 + 77
+    x = values(n, dtype, 901)
+    say("wide mid size dtype=%d n=%d" % (dtype, n))
+    got, info = gpu_stream(E, x, dtype, 512)
+    assert np.array_equal(got, orc.encode(x, 512, dtype=dtype))
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+@pytest.mark.parametrize("B,pow2", [(512, False), (128, False), (1024, True)])
+def test_batch_dt_matches_oracle_and_single(E, orc, dtype, B, pow2):
+    """enc_compress_batch_dt over ragged FP16 / FP32 items -- single values,
+    tails, several tiles, an item that ends RAW and an empty one: every
+    stream equals the oracle's and the per-tensor call's."""
+    rng = np.random.default_rng(40 + dtype)
+    raw = rng.integers(0, 1 << (16 if dtype == 2 else 32), 20_001, dtype=np.uint64)
+    xs = [values(1, dtype, 1), values(9, dtype, 2), values(8193, dtype, 3),
+          values(300_001, dtype, 4), raw.astype(np.uint16 if dtype == 2 else np.uint32),
+          np.zeros(0, np.uint16 if dtype == 2 else np.uint32), values(5_000_000 + 3, dtype, 5)]
+    say("wide batch dtype=%d B=%d pow2=%d" % (dtype, B, pow2))
+    res = E.enc_compress_batch_dt([dev(x, dtype) for x in xs], dtype, B, pow2_widths=pow2)
+    torch.cuda.synchronize()
+    for x, (comp, info) in zip(xs, res):
+        want = orc.encode(x, B, pow2=pow2, dtype=dtype)
+        got = comp.cpu().numpy()
+        assert info.dtype == dtype and np.array_equal(got, want), (dtype, x.size, B, pow2)
+        single, _ = gpu_stream(E, x, dtype, B, pow2)
+        assert np.array_equal(single, got)
+
+
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_single_pass_give_up_falls_back(E, orc, dtype):
+    """With no second look-back poll allowed (ENC_LOOKBACK_SPINS=0) every
+    tile with a predecessor gives up at once: the per-tensor call takes the
+    two-pass encoder and the batch re-encodes its items one by one; the
+    streams are still the oracle's."""
+    import os
+    xs = [values(300_001, dtype, 11), values(70_000, dtype, 12)]
+    wants = [orc.encode(x, 512, dtype=dtype) for x in xs]
+    os.environ["ENC_LOOKBACK_SPINS"] = "0"
+    try:
+        say("wide look-back spin limit 0 dtype=%d" % dtype)
+        for x, want in zip(xs, wants):
+            got, _ = gpu_stream(E, x, dtype, 512)
+            assert np.array_equal(got, want)
+        res = E.enc_compress_batch_dt([dev(x, dtype) for x in xs], dtype, 512)
+        torch.cuda.synchronize()
+        for (comp, _), want in zip(res, wants):
+            assert np.array_equal(comp.cpu().numpy(), want)
+    finally:
+        os.environ.pop("ENC_LOOKBACK_SPINS", None)
