@@ -737,6 +737,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// This lane's index, computed where it is used. The asm is volatile, so the
+// compiler neither hoists it out of a loop nor keeps it in a register across
+// one: at 128 registers per lane such loop-invariant values get spilled, and
+// each reload from scratch waits for every outstanding global load (it counts
+// in the same counter), which drains the prefetch ring.
+__device__ __forceinline__ uint32_t lane_here() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // M tile of k_gemm_mfmau; larger M runs several 128-row tiles.
 uint32_t mfmau_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
@@ -758,7 +769,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   constexpr uint32_t XP = MT * KS / 8;          // 16-byte pieces of a step's X slice
   constexpr uint32_t XPITCH = xs_pitch(KS);
   static_assert(WAVES == 16 && (KS == 32 || KS == 64), "16 waves, steps of 32 or 64 rows");
-  static_assert(XP <= NTHR, "at most one X piece per thread");
+  static_assert(XP <= NTHR && XP % 64 == 0, "at most one X piece per thread, whole waves");
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][KS / 2 * kPitchU];
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * XPITCH];
   const uint32_t tid = threadIdx.x, lane = tid & 63;
@@ -772,6 +783,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   const uint32_t nsteps = (k1 - k0 + KS - 1) / KS;   // RPW * nsteps <= 64: at most 1024 rows
   const uint32_t col0 = c * kStrip, m0 = mt * MT;
   const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.wstream, a.total);
+  // The thread index where the X slice is loaded and stored. The 128-row tile
+  // uses all 128 registers of a lane, and a loop-invariant index there was
+  // spilled and reloaded every step (with a wait for all loads in flight):
+  // it recomputes the index each time (M = 128 56.7 -> 53.0 us per call on a
+  // 4096 x 14336 W). The smaller tiles have room and keep it (recomputing
+  // cost them 1-2%).
+  auto xtid = [&]() -> uint32_t { return MT >= 128 ? wave * 64 + lane_here() : tid; };
 
   // Row table of this wave (coded W): lane l describes row KS (l / RPW) +
   // RPW wave + l % RPW of the K range -- a row the wave decodes in step
@@ -847,7 +865,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
     // pieces past the K range are zeroed when the last step stores them (a
     // select right after the load would make the compiler wait for it, i.e.
     // for every load just issued).
-    const uint32_t p = tid % XP;
+    const uint32_t p = xtid() % XP;
     const uint32_t m = m0 + p / (KS / 8), kx = kb + 8 * (p % (KS / 8));
     S.x = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)min(m, M - 1) * K + min(kx, k1 - 8));
     S.xm = (st < nsteps && kx < k1) ? ~0u : 0u;
@@ -919,10 +937,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
         }
       }
     }
-    if (tid < XP) {
+    if (wave * 64 < XP) {   // tid < XP; XP is a multiple of 64
       uint4 x = S.x;
       if (tail) x = make_uint4(x.x & S.xm, x.y & S.xm, x.z & S.xm, x.w & S.xm);
-      *reinterpret_cast<uint4 *>(&xs[buf][(tid / (KS / 8)) * XPITCH + 8 * (tid % (KS / 8))]) = x;
+      const uint32_t t = xtid();
+      *reinterpret_cast<uint4 *>(&xs[buf][(t / (KS / 8)) * XPITCH + 8 * (t % (KS / 8))]) = x;
     }
   };
   f32x4 acc[MSUB][NSUB];
