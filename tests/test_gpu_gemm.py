@@ -115,6 +115,22 @@ def test_long_k_ragged_tail(E, orc, M):
     assert_within(run_fused(E, X, comp, info, N), Y, A, "fused K=%d M=%d" % (K, M))
 
 
+@pytest.mark.parametrize("M", [16, 100, 130])
+def test_long_k_ragged_tail_b512(E, orc, M):
+    """K = 2056 at B = 512 (row-uniform kernels: a K range ending 8 rows into
+    a 32- or 64-row step), two 512-column strips (four 256-column ones), M
+    below, inside and past one 128-row tile."""
+    K, N = 2056, 1024
+    W = synth.gaussian_bits((K, N), 0.02, 207, M)
+    X = synth.gemm_activations(M, K)
+    comp = torch.from_numpy(orc.encode(W.reshape(-1), 512)).cuda()
+    info = E.enc_read_info(comp)
+    Y, A = orc.gemm_f64(X, W)
+    say("K=%d N=%d M=%d B=512" % (K, N, M))
+    assert_within(run_fused(E, X, comp, info, N), Y, A, "fused K=%d M=%d" % (K, M))
+    assert_within(run_dense(E, X, W), Y, A, "dense K=%d M=%d" % (K, M))
+
+
 def test_raw_weight(E, orc):
     # exponents 1..64 and 129..190 in every block: width 8 everywhere -> RAW
     K, N = 128, 1024
