@@ -53,6 +53,10 @@ def parse():
                         "then a 1 GiB device copy of known size for counter calibration")
     p.add_argument("--gemm-m", default="1,2,4,8,16,32,64,128,256",
                    help="comma-separated M values of the [K, N] GEMM sweep")
+    p.add_argument("--gemm-nt-m", default="1,16,128",
+                   help="comma-separated M values of the [N, K] (linear-layer) GEMM")
+    p.add_argument("--gemm-b", type=int, default=512,
+                   help="block size of the compressed W in both GEMM measurements")
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other configurations (tiny, layer sweep, stress)")
@@ -106,14 +110,14 @@ def main():
     B = args.block_size
 
     if args.gemm_only:
-        g = bench_gemm(enc, synth, torch, np, dev, stream, args.gemm_m)
-        gnt = bench_gemm_nt(enc, synth, torch, np, dev)
+        g = bench_gemm(enc, synth, torch, np, dev, stream, args.gemm_m, args.gemm_b)
+        gnt = bench_gemm_nt(enc, synth, torch, np, dev, args.gemm_nt_m, args.gemm_b)
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)                       # calibration: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
         print(json.dumps({"metric": "fused decompress-GEMM us per call", "fused_gemm": g,
-                          "fused_gemm_nt": gnt, "gemm_roofline": gemm_roofline(g, gnt)}),
+                          "fused_gemm_nt": gnt, "gemm_roofline": gemm_roofline(g, gnt, args.gemm_b)}),
               flush=True)
         return
 
@@ -339,9 +343,12 @@ def main():
         result["other_configs"] = bench_configs(enc, synth, torch, np, dev, stream, args)
 
     if not args.no_gemm:
-        result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream, args.gemm_m)
-        result["fused_gemm_nt"] = bench_gemm_nt(enc, synth, torch, np, dev)
-        result["gemm_roofline"] = gemm_roofline(result["fused_gemm"], result["fused_gemm_nt"])
+        result["fused_gemm"] = bench_gemm(enc, synth, torch, np, dev, stream, args.gemm_m,
+                                          args.gemm_b)
+        result["fused_gemm_nt"] = bench_gemm_nt(enc, synth, torch, np, dev, args.gemm_nt_m,
+                                                args.gemm_b)
+        result["gemm_roofline"] = gemm_roofline(result["fused_gemm"], result["fused_gemm_nt"],
+                                                args.gemm_b)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth, np, torch, dev, args.cpu_layers,
@@ -550,8 +557,8 @@ def _graph_time_us(fn, torch, calls=8, replays=20):
     return e0.elapsed_time(e1) * 1e3 / (replays * calls), g
 
 
-def bench_gemm(enc, synth, torch, np, dev, stream, ms):
-    """Y = X W with W 4096x14336 compressed (B=512) vs the same GEMM on the
+def bench_gemm(enc, synth, torch, np, dev, stream, ms, B=512):
+    """Y = X W with W 4096x14336 compressed (block size B) vs the same GEMM on the
     uncompressed W, M from 1 to 256. Eight rotating weight copies keep the
     working set well above the 256 MB last-level cache; times are GPU time per
     call from HIP-graph replays, and every replayed result is checked
@@ -560,8 +567,8 @@ def bench_gemm(enc, synth, torch, np, dev, stream, ms):
     W = torch.from_numpy(synth.gemm_weight(K, N).view(np.int16)).to(dev)
     copies = GEMM_COPIES
     Ws = [W.clone() for _ in range(copies)]
-    comps = [enc.enc_compress(w, 512) for w in Ws]
-    out = {"shape": "X[M,4096] x W[4096,14336], W compressed at B=512",
+    comps = [enc.enc_compress(w, B) for w in Ws]
+    out = {"shape": "X[M,4096] x W[4096,14336], W compressed at B=%d" % B,
            "rotating_copies": copies,
            "timing": "GPU time per call, HIP-graph replay of 8 calls x 20",
            "w_bytes_compressed": comps[0][1].total_bytes, "w_bytes_dense": 2 * K * N}
@@ -569,7 +576,7 @@ def bench_gemm(enc, synth, torch, np, dev, stream, ms):
         X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
         Xb = X.view(torch.bfloat16)
         Ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(copies)]
-        ws = enc.gemm_workspace(M, K, N, 512, dev)
+        ws = enc.gemm_workspace(M, K, N, B, dev)
         try:
             ref = [enc.enc_decompress_gemm(X, c, inf, N, ws=ws).clone() for c, inf in comps]
             k = [0]
@@ -610,24 +617,24 @@ def bench_gemm(enc, synth, torch, np, dev, stream, ms):
     return out
 
 
-def bench_gemm_nt(enc, synth, torch, np, dev):
+def bench_gemm_nt(enc, synth, torch, np, dev, ms="1,16,128", B=512):
     """Y = X W^T with W in linear-layer layout [14336, 4096], compressed at
-    B=512, against the same kernel on the dense W and torch's F.linear
+    block size B, against the same kernel on the dense W and torch's F.linear
     (hipBLASLt); eight rotating weight copies, HIP-graph replay timing."""
     import torch.nn.functional as F
     K, N = 4096, 14336
     W = torch.from_numpy(synth.gaussian_bits((N, K), 0.02, 4, 1, outliers=False).view(np.int16)).to(dev)
     copies = GEMM_COPIES
     Ws = [W.clone() for _ in range(copies)]
-    comps = [enc.enc_compress(w.reshape(-1), 512) for w in Ws]
-    out = {"shape": "X[M,4096] x W^T, W [14336,4096] compressed at B=512",
+    comps = [enc.enc_compress(w.reshape(-1), B) for w in Ws]
+    out = {"shape": "X[M,4096] x W^T, W [14336,4096] compressed at B=%d" % B,
            "rotating_copies": copies,
            "w_bytes_compressed": comps[0][1].total_bytes}
-    for M in (1, 16, 128):
+    for M in [int(v) for v in ms.split(",")]:
         X = torch.from_numpy(synth.gemm_activations(M, K).view(np.int16)).to(dev)
         Xb = X.view(torch.bfloat16)
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ws = enc.gemm_nt_workspace(M, K, N, 512, dev)
+        ws = enc.gemm_nt_workspace(M, K, N, B, dev)
         k = [0]
 
         def fused():
@@ -791,16 +798,17 @@ GEMM_PMC = os.path.join(ROOT, "profiles", "gemm_w4096x14336_b512_pmc.json")
 GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "group_math.h", "enc_common.h")]
 
 
-def gemm_roofline(g, gnt):
+def gemm_roofline(g, gnt, B=512):
     """Roofline of the fused decompress-GEMM at M = 1, 16, 128 (both
     layouts): algorithmic bytes per call (the compressed stream, X and Y) over
     the GPU time per call, against 8 TB/s, and the MFMA share of the 2.5
     PFLOP/s dense BF16 peak; the HBM traffic per call comes from the
-    committed rocprofv3 PMC summary when it was taken on the current source."""
+    committed rocprofv3 PMC summary when it was taken on the current source
+    (at B = 512, the block size it was taken at)."""
     pmc = None
     try:
         d = json.load(open(GEMM_PMC))
-        if d.get("gemm_source_sha256_16") == source_hash(GEMM_SRCS):
+        if B == 512 and d.get("gemm_source_sha256_16") == source_hash(GEMM_SRCS):
             pmc = d
     except (OSError, ValueError):
         pass
@@ -821,8 +829,9 @@ def gemm_roofline(g, gnt):
                 "mfma_frac": round(2.0 * M * K * N / t / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
                 "traffic": None,
             }
-            if pmc and name == "kn" and ("M%d" % M) in pmc.get("per_call", {}):
-                tr = pmc["per_call"]["M%d" % M]
+            calls = pmc.get("per_call" if name == "kn" else "nt_per_call", {}) if pmc else {}
+            if ("M%d" % M) in calls:
+                tr = calls["M%d" % M]
                 ent["traffic"] = tr["hbm_bytes"]
                 ent["traffic_ratio"] = round(tr["hbm_bytes"] / alg, 4)
             out["%s.M%d" % (name, M)] = ent
