@@ -722,6 +722,7 @@ def cpu_baseline(synth, np, torch, dev, layers_T, layers_1, B):
     nT = sum(x.size for x in xsT)
     encT, decT = run(xsT, T)
     del xsT
+    gemm = cpu_gemm_baseline(synth, np, orc, T)
     return {
         "value": round(2 * nT / decT / 1e9, 4),
         "unit": "GB/s",
@@ -742,7 +743,43 @@ def cpu_baseline(synth, np, torch, dev, layers_T, layers_1, B):
             "decode_s": round(dec1, 3),
             "encode_s": round(enc1, 3),
         },
+        "gemm": gemm,
     }
+
+
+GEMM_ORACLE_COLS = 112   # columns of W per thread in the oracle's GEMM timing sample
+
+
+def cpu_gemm_baseline(synth, np, orc, T):
+    """The oracle's fp64 GEMM (Y and its absolute bound, as the tests use it)
+    on X [M, 4096] x W [4096, 14336] at M = 1, 16, 128: a bounded sample of
+    GEMM_ORACLE_COLS output columns per thread, on 1 thread and on T threads
+    (one contiguous column range each), scaled to the time of the whole
+    product."""
+    from concurrent.futures import ThreadPoolExecutor
+    K, N = 4096, 14336
+    W = synth.gemm_weight(K, N)
+    out = {"sample": "%d output columns per thread of X[M,4096] x W[4096,14336]" % GEMM_ORACLE_COLS,
+           "threads": T}
+    for M in (1, 16, 128):
+        X = synth.gemm_activations(M, K)
+        cols1 = np.arange(GEMM_ORACLE_COLS, dtype=np.uint32)
+        t0 = time.perf_counter()
+        orc.gemm_f64_cols(X, W, cols1)
+        t1 = time.perf_counter() - t0
+        ranges = [np.arange(i * GEMM_ORACLE_COLS, (i + 1) * GEMM_ORACLE_COLS, dtype=np.uint32) % N
+                  for i in range(T)]
+        with ThreadPoolExecutor(T) as ex:
+            t0 = time.perf_counter()
+            list(ex.map(lambda c: orc.gemm_f64_cols(X, W, c), ranges))
+            tT = time.perf_counter() - t0
+        flops_1, flops_T = 2.0 * M * K * GEMM_ORACLE_COLS, 2.0 * M * K * GEMM_ORACLE_COLS * T
+        out["M%d" % M] = {
+            "one_thread_gflops": round(flops_1 / t1 / 1e9, 3),
+            "threads_gflops": round(flops_T / tT / 1e9, 3),
+            "threads_us_per_call": round(2.0 * M * K * N / (flops_T / tT) * 1e6, 1),
+        }
+    return out
 
 
 def stream_ceiling(enc, torch, np, dev, stream, read_bytes, write_bytes):
