@@ -75,9 +75,16 @@ def parse():
 
 
 def source_hash(paths):
+    """Hash of the code in the given C++ sources: line comments, trailing
+    blanks and empty lines are left out, so a change to a comment does not
+    retire a profile taken on the same code (the sources hold no '//' inside
+    string literals and no block comments)."""
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        for line in open(p, encoding="utf-8").read().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -16,7 +16,7 @@
 // that crossover the MFMA kernels' cost hardly depends on M (measured on a
 // 4096 x 14336 W, GPU time per call: M = 2 27.5 us either way, M = 3 29.2 on
 // VALU vs 27.7 on MFMA, M = 4 31.3 vs 28.0).
-//  * k_gemm_rowu (small M, B >= 512): a wave owns a 512-column strip and 32
+//  * k_gemm_rowu (small M, B >= 512): a wave owns a 512-column strip and 64
 //    rows; every row's width, base and block offset are wave-uniform, so
 //    codes come in with one buffer load per lane and row and the byte planes
 //    turn into fp32 with v_perm; M x 8 fp32 FMAs per row.
@@ -29,10 +29,11 @@
 //  * W stored [N, K] (a linear layer's layout, Y = X W^T): k_gemm_ntu
 //    decodes 128-k runs of TN rows into an LDS tile read as MFMA fragments
 //    (B >= 512, or dense W); k_gemm_nt decodes groups straight into
-//    fragments (any other block size).
-//  * split K: workgroups over K ranges write fp32 partial slices, and
-//    k_splitk_reduce, launched next on the same stream, adds them in K order
-//    (deterministic).
+//    fragments (any other block size); k_gemv_nt serves M = 1 (whole rows
+//    of W per workgroup, no split over K).
+//  * split K: workgroups over K ranges write fp32 partial slices, added in
+//    K order (deterministic) by k_splitk_reduce, launched next on the same
+//    stream -- or, in k_gemm_rowu, by the last workgroup of each strip.
 #include "enc_common.h"
 #include "group_math.h"
 
