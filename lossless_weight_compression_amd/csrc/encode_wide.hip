@@ -14,7 +14,11 @@
 // segment totals), the shared segment scan, k_encw_pack (one 1024-group
 // tile per workgroup iteration: the tile's codes and kept fields are
 // assembled in zeroed LDS images and written out with 16-byte stores) and
-// k_encw_finish (header, metas, offsets, section padding).
+// k_encw_finish (header, metas, offsets, section padding). The single-pass
+// kernels of encode_onepass.hip write the same streams and serve FP16 and
+// FP32 too; these passes run when the output buffer is smaller than the RAW
+// size (the single pass writes in place up to it) or a look-back wait gave
+// up.
 #include "enc_common.h"
 #include "group_math.h"
 
