@@ -752,23 +752,16 @@ __device__ __forceinline__ uint32_t lane_here() {
 // M tile of k_gemm_mfmau; larger M runs several 128-row tiles.
 uint32_t mfmau_tile_m(uint32_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
-// The X slice in LDS: one row per X row, KS bf16 (KS / 8 16-byte chunks).
-// ds_read_b128 serves 16 lanes per cycle, but not 16 consecutive ones:
-// measured on gfx950 with the SQ_LDS_BANK_CONFLICT counter, the MFMA
-// A-fragment read (lane l: row l % 16, chunk l / 16) costs twice the cycles
-// of a conflict-free read from rows padded to 80, 144 or 272 bytes. With
-// KS = 32 rows are 64 bytes and chunk c of row r sits at position
-// c ^ ((r >> 1) & 2), which makes that read conflict-free (and the writes of
-// whole rows by consecutive lanes stay so). The 128-row tile keeps rows
-// padded by 8 bf16: with the swizzled layout the compiler spilled one
-// accumulator tile in its loop (128 registers per lane are all it has).
-constexpr bool xs_swizzled(uint32_t mt, uint32_t ks) { return ks == 32 && mt < 128; }
-constexpr uint32_t xs_pitch(uint32_t mt, uint32_t ks) { return xs_swizzled(mt, ks) ? 32 : ks + 8; }
-template <uint32_t MT, uint32_t KS>
-__device__ __forceinline__ uint32_t xs_at(uint32_t row, uint32_t chunk) {
-  if (xs_swizzled(MT, KS)) return row * 32 + 8 * (chunk ^ ((row >> 1) & 2));
-  return row * (KS + 8) + 8 * chunk;
-}
+// The X slice in LDS: one row per X row, KS bf16 (KS / 8 16-byte chunks),
+// rows padded by 16 bf16. ds_read_b128 serves 16 lanes per cycle, but not
+// 16 consecutive ones: measured on gfx950 with the SQ_LDS_BANK_CONFLICT
+// counter, the MFMA A-fragment read (lane l: row l % 16, chunk l / 16) costs
+// twice the cycles of a conflict-free read from rows padded to 80, 144 or
+// 272 bytes, and none from 288-byte rows; the lane groups that fit those
+// measurements make 96-byte (KS = 32) and 160-byte (KS = 64) rows
+// conflict-free as well, and the writes of whole rows by consecutive lanes
+// stay so.
+constexpr uint32_t xs_pitch(uint32_t ks) { return ks + 16; }   // bf16 per LDS row of the X slice
 
 // Each K step, the workgroup's threads load the step's X slice (MT rows x 32
 // k, one 16-byte piece per thread) and store it in LDS next to the decoded W
@@ -784,7 +777,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
   constexpr uint32_t MSUB = MT / 16;
   constexpr uint32_t NTHR = WAVES * 64;
   constexpr uint32_t XP = MT * KS / 8;          // 16-byte pieces of a step's X slice
-  constexpr uint32_t XPITCH = xs_pitch(MT, KS);
+  constexpr uint32_t XPITCH = xs_pitch(KS);
   static_assert(WAVES == 16 && (KS == 32 || KS == 64), "16 waves, steps of 32 or 64 rows");
   static_assert(XP <= NTHR && XP % 64 == 0, "at most one X piece per thread, whole waves");
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][KS / 2 * kPitchU];
@@ -958,7 +951,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
       uint4 x = S.x;
       if (tail) x = make_uint4(x.x & S.xm, x.y & S.xm, x.z & S.xm, x.w & S.xm);
       const uint32_t t = xtid();
-      *reinterpret_cast<uint4 *>(&xs[buf][xs_at<MT, KS>(t / (KS / 8), t % (KS / 8))]) = x;
+      *reinterpret_cast<uint4 *>(&xs[buf][(t / (KS / 8)) * XPITCH + 8 * (t % (KS / 8))]) = x;
     }
   };
   f32x4 acc[MSUB][NSUB];
@@ -981,11 +974,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_mfmau(GemmArgs a) {
         bw.w = tile[buf][(kq + 3) * kPitchU + n];
         b[ns] = __builtin_bit_cast(bf16x8, bw);
       }
-      // row 16 mi + lane % 16: the swizzle depends on the row's low four bits only
-      const uint32_t a0 = xs_at<MT, KS>(lane & 15, 4 * kc + (lane >> 4));
 #pragma unroll
       for (uint32_t mi = 0; mi < MSUB; ++mi) {
-        const uint4 av = *reinterpret_cast<const uint4 *>(&xs[buf][16 * mi * XPITCH + a0]);
+        const uint4 av = *reinterpret_cast<const uint4 *>(
+            &xs[buf][(16 * mi + (lane & 15)) * XPITCH + 32 * kc + 8 * (lane >> 4)]);
         const bf16x8 af = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
         for (uint32_t ns = 0; ns < NSUB; ++ns)
