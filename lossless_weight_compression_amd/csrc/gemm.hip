@@ -1365,10 +1365,18 @@ __global__ __launch_bounds__(kNtuWaves * 64) void k_gemm_ntu(GemmArgs a) {
         const uint32_t off = tbl_off[r * kNtuMaxBlocks + j];
         const uint32_t meta = tbl_meta[r * kNtuMaxBlocks + j];
         const uint32_t w = (meta >> 8) & 15u;
-        const uint32_t sh = ((off + ((k & ((1u << log2b) - 1)) >> 3) * w) & 3u) * 8;
-        const uint32_t lo = __builtin_amdgcn_alignbit(S.q[h].y, S.q[h].x, sh);
-        const uint32_t hi = __builtin_amdgcn_alignbit(S.q[h].z, S.q[h].y, sh);
-        v = join_group(lo, hi, w, (meta & 0xFFu) * 0x01010101u, S.sm[h].x, S.sm[h].y);
+        uint32_t el, eh;
+        if (__ballot(w != 4) == 0) {
+          // every row of the wave has width 4 (most blocks of these
+          // weights): a group's codes are one dword-aligned dword
+          codes_to_bytes_w4(S.q[h].x, el, eh);
+        } else {
+          const uint32_t sh = ((off + ((k & ((1u << log2b) - 1)) >> 3) * w) & 3u) * 8;
+          const uint32_t lo = __builtin_amdgcn_alignbit(S.q[h].y, S.q[h].x, sh);
+          const uint32_t hi = __builtin_amdgcn_alignbit(S.q[h].z, S.q[h].y, sh);
+          codes_to_bytes(lo, hi, w, el, eh);
+        }
+        v = bytes_to_bf16(el, eh, (meta & 0xFFu) * 0x01010101u, S.sm[h].x, S.sm[h].y);
       }
       *reinterpret_cast<uint4 *>(&wt[buf][ntu_at(r, g)]) = v;
     }
@@ -1735,10 +1743,17 @@ __global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
       }
       if (!DENSE) {
         const uint32_t w = (info[i] >> 8) & 15u;
-        const uint32_t sh = ((info[i] >> 16) & 3u) * 8;
-        const uint32_t lo = __builtin_amdgcn_alignbit(qd[i].y, qd[i].x, sh);
-        const uint32_t hi = __builtin_amdgcn_alignbit(qd[i].z, qd[i].y, sh);
-        wv[i] = join_group(lo, hi, w, (info[i] & 0xFFu) * 0x01010101u, sm[i].x, sm[i].y);
+        uint32_t el, eh;
+        if (__ballot(w != 4) == 0) {
+          // width 4 across the wave: a group's codes are one aligned dword
+          codes_to_bytes_w4(qd[i].x, el, eh);
+        } else {
+          const uint32_t sh = ((info[i] >> 16) & 3u) * 8;
+          const uint32_t lo = __builtin_amdgcn_alignbit(qd[i].y, qd[i].x, sh);
+          const uint32_t hi = __builtin_amdgcn_alignbit(qd[i].z, qd[i].y, sh);
+          codes_to_bytes(lo, hi, w, el, eh);
+        }
+        wv[i] = bytes_to_bf16(el, eh, (info[i] & 0xFFu) * 0x01010101u, sm[i].x, sm[i].y);
       }
       const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
