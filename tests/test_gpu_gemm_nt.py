@@ -238,6 +238,32 @@ def test_gemv_rows(E, orc, M, K, B):
         assert np.array_equal(y[m], bf16_f64(W[:, k])), (m, k)
 
 
+@pytest.mark.parametrize("M", [1, 16])
+def test_rows_of_mixed_widths(E, orc, M):
+    """Rows of W whose blocks have exactly the widths 0, 1, 3, 4, 4, 4, 5, 8
+    (in turn, one width per row), B = 512: the waves of the M = 1 GEMV and
+    of the staged-row kernel see rows of width 4 only (the nibble split)
+    and rows of other widths (bit-field extracts) in the same call."""
+    N, K, B = 64, 4096, 512
+    rng = np.random.default_rng(143)
+    widths = [0, 1, 3, 4, 4, 4, 5, 8]
+    W = np.empty((N, K), np.uint16)
+    for n in range(N):
+        w = widths[n % len(widths)]
+        base = 0 if w == 8 else 100
+        exps = base + rng.integers(0, 1 << w, K)
+        exps.reshape(-1, B)[:, 0] = base                    # every block spans its full range
+        exps.reshape(-1, B)[:, 1] = base + (1 << w) - 1
+        sm = rng.integers(0, 256, K)
+        W[n] = (((sm & 0x80) << 8) | (exps << 7) | (sm & 0x7F)).astype(np.uint16)
+    X = synth.gemm_activations(M, K)
+    comp, info = oracle_stream(E, orc, W, B)
+    assert info.flags == 0
+    say("mixed widths M=%d" % M)
+    Y, A = oracle_nt(orc, X, W)
+    assert_within(run_fused(E, X, comp, info, N), Y, A, "mixed widths")
+
+
 def test_gemv_raw_and_pow2(E, orc):
     """The M = 1 GEMV on a RAW stream (multiplied from its verbatim values)
     and on a power-of-two-width stream."""
