@@ -327,6 +327,9 @@ def main():
         "encode_batch_ms": round(enc_batch_ms, 2),
         "encode_batch_gbs": round((2 * n_total + comp_total) / (enc_batch_ms * 1e-3) / 1e9, 1),
         "per_tensor_launch_ms_per_step": round(per_tensor_ms, 4),
+        "decode_launch_ms": {"mean": round(avg_launch_ms, 4),
+                             "median": round(float(np.median(launch_ms)), 4),
+                             "min": round(min(launch_ms), 4), "max": round(max(launch_ms), 4)},
         "roofline": {
             "bound": "hbm",
             "kernel": "k_decode_batch",
