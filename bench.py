@@ -796,9 +796,10 @@ def stream_ceiling(enc, torch, np, dev, stream, read_bytes, write_bytes):
     """HBM rate of the library's streaming kernel with the decoder's access
     shape (16-byte loads, non-temporal 16-byte stores, one contiguous run per
     workgroup, workgroups in order) over exactly one decode step's bytes:
-    read_bytes read, write_bytes written. 1, 2 and 4 items per thread (4, 8
-    and 16 KB written per workgroup; the decoder writes 8 KB). The ceiling
-    is the fastest of the three. A 4 GiB torch copy_ is kept for context."""
+    read_bytes read, write_bytes written. Workgroups of 64 or 256 threads, 1,
+    2 or 4 items per thread (the decoder: 256 threads, 8 KB written per
+    workgroup). The ceiling is the fastest shape. A 4 GiB torch copy_ is
+    kept for context."""
     rb = (read_bytes + 15) // 16 * 16
     wb = (write_bytes + 15) // 16 * 16
     src = torch.empty(rb, dtype=torch.uint8, device=dev)
@@ -806,22 +807,22 @@ def stream_ceiling(enc, torch, np, dev, stream, read_bytes, write_bytes):
     src.fill_(0x3C)
     res = {"read_bytes": rb, "write_bytes": wb}
     best = 0.0
-    for items in (1, 2, 4):
-        enc.enc_stream_probe(src, dst, items)
+    for threads, items in ((64, 1), (64, 2), (256, 1), (256, 2), (256, 4)):
+        enc.enc_stream_probe(src, dst, items, threads)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 5
         e0.record(stream)
         for _ in range(reps):
-            enc.enc_stream_probe(src, dst, items)
+            enc.enc_stream_probe(src, dst, items, threads)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         gbs = (rb + wb) / (ms * 1e-3) / 1e9
-        res["items%d" % items] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
-                                  "kb_written_per_workgroup": 4 * items}
+        res["t%d_items%d" % (threads, items)] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                                                 "kb_written_per_workgroup": threads * items // 64}
         best = max(best, gbs)
-        log("stream probe, %d item(s) per thread: %.3f ms, %.1f GB/s" % (items, ms, gbs))
+        log("stream probe, %d threads x %d item(s): %.3f ms, %.1f GB/s" % (threads, items, ms, gbs))
     del src, dst
     torch.cuda.empty_cache()
     a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)

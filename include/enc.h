@@ -370,15 +370,16 @@ enc_status enc_validate(const void *d_comp, const enc_info *h_info, void *d_ws, 
  * decoder's roofline is memory bandwidth: every stream byte is read once and
  * every output byte written once, as the MINE Abstract describes for
  * single-stream inference). Reads src_bytes from d_src and writes dst_bytes
- * to d_dst (16-byte items, non-temporal stores): workgroup b writes the b-th
- * run of 256 x items_per_thread output items and reads the b-th
+ * to d_dst (16-byte items, non-temporal stores): workgroup b (of
+ * threads_per_workgroup threads: 64, 128 or 256) writes the b-th run of
+ * threads_per_workgroup x items_per_thread output items and reads the b-th
  * proportional run of the source; the output holds copies of source items
  * (which ones is unspecified). Sizes: nonzero multiples of 16;
  * items_per_thread 1, 2 or 4; buffers 16-byte aligned, not overlapping.
  * Asynchronous; allocates nothing. Errors: ENC_ERR_INVALID_ARG,
  * ENC_ERR_UNSUPPORTED (sizes past the index arithmetic), ENC_ERR_HIP. */
 enc_status enc_stream_probe(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
-                            uint32_t items_per_thread, void *stream);
+                            uint32_t items_per_thread, uint32_t threads_per_workgroup, void *stream);
 
 /* Static text for a status code. */
 const char *enc_status_string(enc_status s);

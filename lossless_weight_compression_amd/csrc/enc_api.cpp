@@ -1049,7 +1049,7 @@ enc_status enc_gemm_dense_nt(const uint16_t *d_x, uint32_t M, uint32_t K, const 
 }
 
 enc_status enc_stream_probe(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
-                            uint32_t items_per_thread, void *stream) {
+                            uint32_t items_per_thread, uint32_t threads_per_workgroup, void *stream) {
   clear_err();
   if (!d_src || !d_dst) return fail(ENC_ERR_INVALID_ARG, "NULL device pointer");
   if (!aligned16(d_src) || !aligned16(d_dst)) return fail(ENC_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
@@ -1057,15 +1057,18 @@ enc_status enc_stream_probe(const void *d_src, uint64_t src_bytes, void *d_dst, 
     return fail(ENC_ERR_INVALID_ARG, "sizes must be nonzero multiples of 16 bytes");
   if (items_per_thread != 1 && items_per_thread != 2 && items_per_thread != 4)
     return fail(ENC_ERR_INVALID_ARG, "items_per_thread must be 1, 2 or 4");
+  const uint32_t T = threads_per_workgroup;
+  if (T != 64 && T != 128 && T != 256)
+    return fail(ENC_ERR_INVALID_ARG, "threads_per_workgroup must be 64, 128 or 256");
   const uintptr_t s0 = (uintptr_t)d_src, d0 = (uintptr_t)d_dst;
   if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return fail(ENC_ERR_INVALID_ARG, "buffers overlap");
-  const uint64_t nwg = (dst_bytes / 16 + 256ull * items_per_thread - 1) / (256ull * items_per_thread);
+  const uint64_t nwg = (dst_bytes / 16 + (uint64_t)T * items_per_thread - 1) / ((uint64_t)T * items_per_thread);
   const uint64_t si = src_bytes / 16;
   // 32.32 fixed-point source run per workgroup: (workgroups x ratio) < 2^64
   if (nwg > (1ull << 30) || si >= (1ull << 31) || si / nwg + 1 >= (1ull << 31))
     return fail(ENC_ERR_UNSUPPORTED, "sizes too large for the probe's index arithmetic");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return launched(launch_stream_probe(d_src, src_bytes, d_dst, dst_bytes, items_per_thread, s), s,
+  return launched(launch_stream_probe(d_src, src_bytes, d_dst, dst_bytes, items_per_thread, T, s), s,
                   "probe launch");
 }
 

@@ -170,7 +170,7 @@ enc_status set_error(enc_status st, const char *fmt, ...);
 
 // ---- measurement: streaming kernel with the decoder's access shape --------
 hipError_t launch_stream_probe(const void *src, uint64_t src_bytes, void *dst, uint64_t dst_bytes,
-                               uint32_t items, hipStream_t s);
+                               uint32_t items, uint32_t threads, hipStream_t s);
 
 // ---- deep stream check ------------------------------------------------------
 struct ValidateArgs {

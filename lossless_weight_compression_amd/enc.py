@@ -102,7 +102,7 @@ SIGNATURES = {
     "enc_gemm_nt_workspace_bytes": (_U64, [_U32, _U32, _U32, _U32]),
     "enc_decompress_gemm_nt": (_ST, [_VP, _U32, _U32, _VP, _INFO_P, _U32, _VP, _VP, _U64, _VP]),
     "enc_gemm_dense_nt": (_ST, [_VP, _U32, _U32, _VP, _U32, _VP, _VP, _U64, _VP]),
-    "enc_stream_probe": (_ST, [_VP, _U64, _VP, _U64, _U32, _VP]),
+    "enc_stream_probe": (_ST, [_VP, _U64, _VP, _U64, _U32, _U32, _VP]),
     "enc_status_string": (ctypes.c_char_p, [_ST]),
     "enc_last_error": (ctypes.c_char_p, []),
 }
@@ -508,12 +508,12 @@ def enc_validate(comp, info, ws=None, stream=None):
     return chk
 
 
-def enc_stream_probe(src, dst, items_per_thread=1, stream=None):
+def enc_stream_probe(src, dst, items_per_thread=1, threads_per_workgroup=256, stream=None):
     """Streaming kernel with the decoder's access shape (measurement helper):
     reads all of `src`, writes all of `dst` (both CUDA tensors)."""
     _check(lib().enc_stream_probe(_ptr(src), src.numel() * src.element_size(), _ptr(dst),
                                   dst.numel() * dst.element_size(), items_per_thread,
-                                  _stream(stream)))
+                                  threads_per_workgroup, _stream(stream)))
 
 
 def enc_status_string(status):
