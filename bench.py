@@ -143,6 +143,7 @@ def main():
     streams, enc_ms, n_total, comp_total = [], 0.0, 0, 0
     algo_read = 0
     ws_cache = {}
+    warmed = set()
     for k, i in enumerate(idx):
         x = xs[k]
         n = x.numel()
@@ -151,6 +152,9 @@ def main():
         ws = ws_cache.get(wsb)
         if ws is None:
             ws = ws_cache[wsb] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        if n not in warmed:   # first call of each shape untimed (code loading, allocations)
+            enc.enc_compress(x, B, out=out, ws=ws)
+            warmed.add(n)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         comp, info = enc.enc_compress(x, B, out=out, ws=ws)   # synchronises once inside
@@ -383,8 +387,12 @@ def bench_wide(enc, synth, torch, np, dev, stream, args):
         esize = 2 if dt == 2 else 4
         streams, n_total, comp_total, read, enc_ms = [], 0, 0, 0, 0.0
         S = 11 if dt == 2 else 24
+        warmed = set()
         for i in idx:
             x = synth.set8b_tensor_gpu_dt(i, dt, device=dev).reshape(-1)
+            if x.numel() not in warmed:   # first call of each shape untimed
+                enc.enc_compress(x, B, dtype=dt)
+                warmed.add(x.numel())
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             comp, info = enc.enc_compress(x, B, dtype=dt)
