@@ -211,8 +211,8 @@ enc_status enc_parse_header(const void *h_header, uint64_t header_bytes, uint64_
 enc_status enc_read_info(const void *d_comp, uint64_t comp_bytes, void *stream, enc_info *h_info);
 
 /* Decompress a whole stream into out_elems values of the stream's dtype
- * (2 bytes each for BF16 and FP16, 4 for FP32; ZipServ Abstract:
- * constant-time, parallel decoding). One kernel launch; asynchronous;
+ * (2 bytes each for BF16 and FP16, 4 for FP32; ZipServ Abstract: each
+ * block is found in a fixed number of steps and all decode in parallel). One kernel launch; asynchronous;
  * allocates nothing. h_info must describe d_comp (enc_read_info or the
  * enc_info enc_compress returned); out_elems must equal its n_elems. */
 enc_status enc_decompress(const void *d_comp, const enc_info *h_info, void *d_out,

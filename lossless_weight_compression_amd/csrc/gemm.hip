@@ -3,9 +3,9 @@
 //
 // "ZipServ: Fast and Memory-Efficient LLM Inference with Hardware-Aware
 // Lossless Compression", Abstract: the weights are decompressed on the fly
-// inside the GEMM kernel ("load-compressed, compute-decompressed"), so the
-// decoded W never goes back to HBM and the kernel reads only the compressed
-// bytes.
+// inside the GEMM kernel: compressed bytes are what is loaded, decoded values
+// are what the matrix units consume, so the decoded W never goes back to HBM
+// and the kernel reads only the compressed bytes.
 //
 // Both paths locate the block of a row the way the decoder does: the stored
 // offset of the block's 64-block segment plus the payload sizes of the earlier

@@ -522,8 +522,9 @@ int64_t orc_stream_elements(const uint8_t *s, uint64_t bytes) {
 
 /* Payload start of block i, found the way a parallel decoder finds it: the
  * stored offset of its segment plus the sizes of the earlier blocks of the
- * same segment (ZipServ Abstract: constant-time, parallel decoding; ENEC
- * Abstract: intra-segment scan). */
+ * same segment (ZipServ Abstract: every block is located in the same, fixed
+ * number of steps, so all blocks decode in parallel; ENEC Abstract: the scan
+ * within a segment). */
 static uint64_t block_payload_start(const uint8_t *s, const orc_header *h, uint64_t i) {
   uint64_t seg = i / ORC_SEG_BLOCKS;
   uint64_t off = get_le(s + h->segoff_off + 8 * seg, 8);
