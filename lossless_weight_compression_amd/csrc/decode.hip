@@ -18,7 +18,8 @@
 //    size and a wave64 inclusive scan gives every block's start -- no
 //    workgroup barrier and no LDS;
 //  * a group's 8 codes of w bits are exactly w bytes starting on a byte
-//    boundary; the lane loads the (up to three) dwords that cover them,
+//    boundary; the lane loads the three dwords that cover them with one
+//    buffer_load_dwordx3 (dwords past the stream's end read as zero),
 //    funnel-shifts them into place (v_alignbit) and cuts the fields with
 //    v_bfe; exponent bytes get the block base with one packed add (a valid
 //    stream never carries out of a byte), and v_bfi/v_perm interleave them
@@ -62,13 +63,31 @@ template <class T>   // scalar types
 __device__ __forceinline__ T ldg(gsrc p) {
   return *(const ENC_GLOBAL T *)p;
 }
-__device__ __forceinline__ uint2 ldg2(gsrc p) {
-  const u32x2_g v = *(const ENC_GLOBAL u32x2_g *)p;
-  return make_uint2(v.x, v.y);
-}
 __device__ __forceinline__ uint4 ldg4(gsrc p) {
   const u32x4_nt v = *(const ENC_GLOBAL u32x4_nt *)p;
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Raw buffer descriptors over the stream. Range checking as the CDNA3 ISA
+// reference guide defines it for buffer instructions (section on buffer
+// addressing, range checking; CDNA4 keeps the rule): with stride 0 an access
+// is out of range when its byte offset is at or past num_records, the check
+// is made for each dword of a multi-dword access, and out-of-range dwords
+// load as zero without a memory access.
+typedef uint32_t u32x3_g __attribute__((ext_vector_type(3)));
+constexpr uint32_t kPastRange = 0xFFFFFFF0u;   // an offset no descriptor here reaches
+// Descriptor over the stream bytes [from, total), at most kPastRange of them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc_from(const DecodeDesc &d, uint64_t from) {
+  const uint64_t room = d.total > from ? d.total - from : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(d.stream + from), 0,
+                                           (int)(room < kPastRange ? room : kPastRange), 0x00020000);
+}
+// A value the caller knows to be equal in every lane, in scalar registers.
+// (The builtin returns int: each half goes through uint32_t, so the low half
+// is not sign-extended into the high one.)
+__device__ __forceinline__ uint64_t wave_uniform(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | lo;
 }
 template <class T>
 __device__ __forceinline__ void stg(gdst p, T v) {
@@ -159,7 +178,6 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     copy_tile_raw(d, tile, tid);
     return;
   }
-  const gsrc s = stream_of(d);
   const gdst ob = output_of(d);
   const uint64_t n = d.n;
   const uint32_t lane = tid & 63;
@@ -173,7 +191,16 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
   uint64_t seg_payload;
   segment_scan(d, seg, lane, pk, seg_payload);
 
-  // Phase 1: issue every load of this lane's groups.
+  // Phase 1: issue every load of this lane's groups: the 8 sign+mantissa
+  // bytes (one dwordx2) and the 12 bytes from the code dword holding the
+  // group's first code bit (one dwordx3), both off raw buffer descriptors.
+  // A lane with nothing to read points its load past the range (zeros, no
+  // memory access), and a dwordx3 that runs past the stream's end loads
+  // zeros for the dwords outside it, so no load needs a guard or a
+  // substitute address.
+  const uint64_t segp = wave_uniform(seg_payload);
+  const __amdgpu_buffer_rsrc_t code_rs = stream_rsrc_from(d, segp);
+  const __amdgpu_buffer_rsrc_t sm_rs = stream_rsrc_from(d, kHeaderBytes + g0 * 8);
   uint32_t sml[GPT], smh[GPT], q0[GPT], q1[GPT], q2[GPT], info[GPT];
 #pragma unroll
   for (uint32_t it = 0; it < GPT; ++it) {
@@ -186,33 +213,26 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     const uint64_t rem = e0 < n ? n - e0 : 0;
     const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
     const uint32_t nbytes = (valid * w + 7) >> 3;
-    const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
-    const uint64_t a = pb & ~3ull;
-    const uint32_t lead = (uint32_t)(pb & 3);
-    // Branch-free, in-bounds addressing: a dword is read only if it holds a
-    // needed byte; otherwise the lane re-reads a dword it does need (or,
-    // with no payload bytes at all, its own sign+mantissa dword).
-    const uint64_t sm_addr = kHeaderBytes + (valid ? e0 : 0);
-    const uint64_t a0 = nbytes ? a : sm_addr;
-    const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
-    const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
-    // Issued on every path (a group past n reads the plane's first bytes):
-    // a load under a branch made the compiler wait for it at the join,
-    // before the next group's loads went out.
-    const uint2 smv = ldg2(s + sm_addr);
+    const uint32_t off = (p & 0xFFFFFu) + u * w;   // from the segment's payload start (16-byte aligned)
+    const u32x2_g smv = __builtin_amdgcn_raw_buffer_load_b64(sm_rs, valid ? 8 * q : kPastRange, 0, 0);
+    const u32x3_g qv = __builtin_amdgcn_raw_buffer_load_b96(code_rs, nbytes ? (off & ~3u) : kPastRange, 0, 0);
     sml[it] = smv.x;
     smh[it] = smv.y;
-    q0[it] = ldg<uint32_t>(s + a0);
-    q1[it] = ldg<uint32_t>(s + a1);
-    q2[it] = ldg<uint32_t>(s + a2);
-    info[it] = (p & 0xFFF00000u) | (lead << 3) | (valid << 8);
+    q0[it] = qv.x;
+    q1[it] = qv.y;
+    q2[it] = qv.z;
+    info[it] = (p & 0xFFF00000u) | ((off & 3u) << 3) | (valid << 8);
   }
 
-  // Phase 2: decode and store.
+  // Phase 2: decode and store. Every group is decoded, also one past the
+  // end whose loads read zeros, and only the store depends on `valid`: with
+  // `if (!valid) continue` here the compiler moved the second group's loads
+  // under that test, behind the first group's wait (8B-shaped set: 4.65-4.70
+  // ms per decode with global loads and the skip, 4.60-4.64 without the
+  // skip, 4.48-4.57 with the buffer loads as well).
 #pragma unroll
   for (uint32_t it = 0; it < GPT; ++it) {
     const uint32_t valid = (info[it] >> 8) & 15u;
-    if (!valid) continue;
     const uint32_t q = it * kThreads + tid;
     const uint64_t e0 = (g0 + q) * 8;
     const uint32_t w = (info[it] >> 20) & 15u;
@@ -223,7 +243,7 @@ __device__ __forceinline__ void decode_tile(const DecodeDesc &d, uint64_t tile, 
     const uint4 o = join_group(lo, hi, w, base4, sml[it], smh[it]);
     if (valid == 8)
       store_out16(ob + 2 * e0, o);
-    else
+    else if (valid)
       store_partial(ob, e0, n, o);
   }
 }
@@ -428,7 +448,12 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
 // workgroups that gave each XCD a contiguous eighth of the tiles (each XCD
 // then streamed its own region, eight fronts at once), 5.26 ms for that
 // split with one tile per workgroup, and 5.9-6.5 ms with a persistent grid
-// of 2048-8192 workgroups stepping through the tiles in order.
+// of 2048-8192 workgroups stepping through the tiles in order. With the
+// current 4096-value tiles, other orders of the same grid (the tile of
+// workgroup b taken from b mod 8, the XCD, and b / 8) measured: each XCD a
+// contiguous eighth of the tiles 4.83-5.01 ms, each of 2 or 4 XCD groups a
+// contiguous half or quarter 4.75-4.88 ms, a tile's four quarters on four
+// XCDs 6.4-6.7 ms, against 4.65-4.71 ms in order.
 constexpr uint32_t kMaxGrid = 1u << 23;
 
 // Workgroups per launch: kMaxGrid, or fewer when ENC_DECODE_MAX_GRID says
