@@ -294,6 +294,8 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     // Every load of the lane's half groups first (addresses clamped in
     // bounds, no branch), then decode and store.
     constexpr uint32_t NH = 2 * WGPT;
+    const __amdgpu_buffer_rsrc_t code_rs = stream_rsrc_from(d, wave_uniform(seg_payload));
+    const __amdgpu_buffer_rsrc_t fld_rs = stream_rsrc_from(d, kHeaderBytes + 24 * g0);
     uint32_t q0[NH], q1[NH], q2[NH], fd[NH][3], info[NH];
 #pragma unroll
     for (uint32_t it = 0; it < NH; ++it) {
@@ -309,26 +311,24 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       const uint64_t remg = live ? n - g * 8 : 0;
       const uint32_t validg = remg < 8 ? (uint32_t)remg : 8u;   // values of the group
       const uint32_t nbytes = (validg * w + 7) >> 3;
-      const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
-      const uint64_t a = pb & ~3ull;
-      const uint32_t lead = (uint32_t)(pb & 3);
-      // 12 bytes of fields at 24 g + 12 h (4-aligned; a tail group's read
-      // stays in the stream: the metadata sections follow; a half group
-      // past n reads the first one's)
-      const uint64_t fa = kHeaderBytes + (live ? 24 * g + 12 * h : 0);
-      const uint64_t a0 = nbytes ? a : fa;
-      const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
-      const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
-      q0[it] = ldg<uint32_t>(s + a0);
-      q1[it] = ldg<uint32_t>(s + a1);
-      q2[it] = ldg<uint32_t>(s + a2);
-#pragma unroll
-      for (uint32_t j = 0; j < 3; ++j) fd[it][j] = ldg<uint32_t>(s + fa + 4 * j);
-      info[it] = (p & 0xFFF00000u) | ((uint32_t)live << 8) | (lead << 3);
+      const uint32_t off = (p & 0xFFFFFu) + u * w;
+      // codes as in the BF16 tile; the half group's 12 bytes of fields at
+      // 24 g + 12 h (4-aligned; a tail group's read stays in the stream,
+      // whose metadata sections follow)
+      const u32x3_g qv = __builtin_amdgcn_raw_buffer_load_b96(code_rs, nbytes ? (off & ~3u) : kPastRange, 0, 0);
+      const u32x3_g fv = __builtin_amdgcn_raw_buffer_load_b96(fld_rs, live ? 24 * q + 12 * h : kPastRange, 0, 0);
+      q0[it] = qv.x;
+      q1[it] = qv.y;
+      q2[it] = qv.z;
+      fd[it][0] = fv.x;
+      fd[it][1] = fv.y;
+      fd[it][2] = fv.z;
+      info[it] = (p & 0xFFF00000u) | ((uint32_t)live << 8) | ((off & 3u) << 3);
     }
+    // every half group is decoded (those past n from zeros) and only the
+    // store depends on it being live, so no load moves under a branch
 #pragma unroll
     for (uint32_t it = 0; it < NH; ++it) {
-      if (!((info[it] >> 8) & 1u)) continue;
       const uint32_t hq = it * kThreads + tid;
       const uint32_t h = hq & 1;
       const uint64_t e0 = (g0 + (hq >> 1)) * 8 + 4 * h;
@@ -346,10 +346,10 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
       for (uint32_t k = 0; k < 4; ++k)
         o[k] = ((f[k] >> 23) << 31) | (((eb >> (8 * k)) & 0xFFu) << 23) | (f[k] & 0x7FFFFFu);
       const gdst dst = outb + 4 * e0;
-      const uint64_t rem = n - e0;
+      const uint64_t rem = e0 < n ? n - e0 : 0;
       if (rem >= 4) {
         store_out16(dst, make_uint4(o[0], o[1], o[2], o[3]));
-      } else {
+      } else if (rem) {
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k)
           if (k < rem) stg<uint32_t>(dst + 4 * k, o[k]);
@@ -358,9 +358,12 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     return;
   }
 
-  // FP16: every load of the lane's groups first (addresses clamped in
-  // bounds, no branch), then decode and store, as in the BF16 tile: loads
-  // under a branch made the compiler wait for them at the join.
+  // FP16: every load of the lane's groups first, then decode and store, as
+  // in the BF16 tile (buffer loads, lanes with nothing to read past the
+  // range; every group decoded, only the store depends on its valid count).
+  const __amdgpu_buffer_rsrc_t code_rs = stream_rsrc_from(d, wave_uniform(seg_payload));
+  const uint64_t fbase = (kHeaderBytes + 11 * g0) & ~15ull;
+  const __amdgpu_buffer_rsrc_t fld_rs = stream_rsrc_from(d, fbase);
   uint32_t q0[WGPT], q1[WGPT], q2[WGPT], fw[WGPT][4], info[WGPT];
 #pragma unroll
   for (uint32_t it = 0; it < WGPT; ++it) {
@@ -374,29 +377,25 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     const uint64_t rem = e0 < n ? n - e0 : 0;
     const uint32_t valid = rem < 8 ? (uint32_t)rem : 8u;
     const uint32_t nbytes = (valid * w + 7) >> 3;
-    const uint64_t pb = seg_payload + (p & 0xFFFFFu) + (uint64_t)u * w;
-    const uint64_t a = pb & ~3ull;
-    const uint32_t lead = (uint32_t)(pb & 3);
+    const uint32_t off = (p & 0xFFFFFu) + u * w;
     // 11-bit fields of 8 values: 11 bytes at 11 g (any alignment), read as
     // the 16-byte aligned-dword window that covers them (a tail group's
-    // window stays in the stream: the metadata sections follow; a group past
-    // n reads group 0's)
-    const uint64_t b0 = kHeaderBytes + 11 * (valid ? g : 0);
-    const uint64_t fa = b0 & ~3ull;
-    const uint64_t a0 = nbytes ? a : fa;
-    const uint64_t a1 = (lead + nbytes > 4) ? a + 4 : a0;
-    const uint64_t a2 = (lead + nbytes > 8) ? a + 8 : a0;
-    q0[it] = ldg<uint32_t>(s + a0);
-    q1[it] = ldg<uint32_t>(s + a1);
-    q2[it] = ldg<uint32_t>(s + a2);
-#pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) fw[it][j] = ldg<uint32_t>(s + fa + 4 * j);
-    info[it] = (p & 0xFFF00000u) | ((uint32_t)(b0 & 3) << 15) | (valid << 8) | (lead << 3);
+    // window stays in the stream: the metadata sections follow)
+    const uint32_t fo = (uint32_t)(kHeaderBytes + 11 * g - fbase);
+    const u32x3_g qv = __builtin_amdgcn_raw_buffer_load_b96(code_rs, nbytes ? (off & ~3u) : kPastRange, 0, 0);
+    const u32x4_nt fv = __builtin_amdgcn_raw_buffer_load_b128(fld_rs, valid ? (fo & ~3u) : kPastRange, 0, 0);
+    q0[it] = qv.x;
+    q1[it] = qv.y;
+    q2[it] = qv.z;
+    fw[it][0] = fv.x;
+    fw[it][1] = fv.y;
+    fw[it][2] = fv.z;
+    fw[it][3] = fv.w;
+    info[it] = (p & 0xFFF00000u) | ((fo & 3u) << 15) | (valid << 8) | ((off & 3u) << 3);
   }
 #pragma unroll
   for (uint32_t it = 0; it < WGPT; ++it) {
     const uint32_t valid = (info[it] >> 8) & 15u;
-    if (!valid) continue;
     const uint64_t e0 = (g0 + it * kThreads + tid) * 8;
     const uint32_t w = (info[it] >> 20) & 15u;
     const uint32_t lsh = info[it] & 31u;
@@ -430,7 +429,7 @@ __device__ __forceinline__ void decode_tile_wide(const DecodeDesc &d, uint64_t t
     if (valid == 8) {
       store_out16(dst, make_uint4(o[0] | o[1] << 16, o[2] | o[3] << 16, o[4] | o[5] << 16,
                                   o[6] | o[7] << 16));
-    } else {
+    } else if (valid) {
 #pragma unroll
       for (uint32_t k = 0; k < 8; ++k)
         if (k < valid) stg<uint16_t>(dst + 2 * k, (uint16_t)o[k]);
