@@ -278,7 +278,7 @@ uint64_t enc_gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N, uint32_t b
  * with per-strip arrival counters, which every call leaves at zero again
  * (the rest is scratch). When the K dimension is split, the fp32 partial
  * slices are added in K order -- by the last workgroup of each strip to
- * finish (M <= 2, coded W with B >= 512) or by a second kernel on the same
+ * finish (M = 1, coded W with B >= 512) or by a second kernel on the same
  * stream -- so the result is deterministic; calls sharing one workspace must
  * not overlap. Accumulation is fp32. Asynchronous; allocates nothing. */
 enc_status enc_decompress_gemm(const uint16_t *d_x, uint32_t M, uint32_t K, const void *d_wcomp,

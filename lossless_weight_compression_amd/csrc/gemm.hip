@@ -12,10 +12,12 @@
 // blocks of that segment. Every block of W is full (N % B == 0), so a block's
 // payload is w * B / 8 bytes.
 //
-// Small M (below kMfmaMinM = 3) runs on VALU FMAs, larger M on MFMA; above
-// that crossover the MFMA kernels' cost hardly depends on M (measured on a
-// 4096 x 14336 W, GPU time per call: M = 2 27.5 us either way, M = 3 29.2 on
-// VALU vs 27.7 on MFMA, M = 4 31.3 vs 28.0).
+// Small M runs on VALU FMAs, larger M on MFMA: from M = 2 on for the
+// uniform-row kernels (kMfmaMinMUniform), from M = 3 for the generic ones
+// (kMfmaMinM). Above the crossover the MFMA kernels' cost hardly depends on
+// M (4096 x 14336 W, GPU time per call: M = 2 29.5 us with k_gemm_rowu<2>,
+// 27.2 with k_gemm_mfmau; M = 3 29.2 on VALU vs 27.7 on MFMA, M = 4 31.3 vs
+// 28.0 for the generic pair).
 //  * k_gemm_rowu (small M, B >= 512): a wave owns a 512-column strip and 64
 //    rows; every row's width, base and block offset are wave-uniform, so
 //    codes come in with one buffer load per lane and row and the byte planes
@@ -64,8 +66,10 @@
 namespace enc {
 namespace {
 
-constexpr uint32_t kMfmaMinM = 3;              // smallest M routed to the MFMA kernels
-static_assert(kMfmaMinM == 3, "the VALU launchers instantiate M = 1..2");
+constexpr uint32_t kMfmaMinM = 3;              // smallest M on the generic MFMA kernel
+constexpr uint32_t kMfmaMinMUniform = 2;       // smallest M on the uniform-row MFMA kernel
+static_assert(kMfmaMinM == 3 && kMfmaMinMUniform == 2,
+              "the VALU launchers instantiate M = 1..2 (generic) and M = 1 (uniform rows)");
 constexpr uint32_t kStrip = 512;               // VALU path: columns per workgroup
 constexpr uint32_t kValuRowsPerWave = 64;
 constexpr uint32_t kValuRows = 4 * kValuRowsPerWave;
@@ -1044,7 +1048,7 @@ hipError_t launch_rowu(const GemmArgs &a, hipStream_t s) {
   switch (a.M) {
 #define CASE(m) \
   case m: hipLaunchKernelGGL((k_gemm_rowu<m>), grid, dim3(kRowuWaves * 64), 0, s, a); break;
-    CASE(1) CASE(2)
+    CASE(1)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
@@ -1514,14 +1518,14 @@ void gemm_ntu_plan(bool dense, uint32_t M, uint32_t K, uint32_t N, uint32_t log2
 }  // namespace
 
 // Which kernel serves a call: 0 = generic VALU (M < kMfmaMinM), 1 =
-// uniform-row VALU (M < kMfmaMinM, compressed, B >= 512, stream below 2 GiB:
-// 32-bit buffer offsets), 2 = generic MFMA (M >= kMfmaMinM, B < 512), 3 =
-// uniform-row MFMA (M >= kMfmaMinM, dense W or B >= 512).
+// uniform-row VALU (M < kMfmaMinMUniform, compressed, B >= 512, stream below
+// 2 GiB: 32-bit buffer offsets), 2 = generic MFMA (M >= kMfmaMinM, B < 512),
+// 3 = uniform-row MFMA (M >= kMfmaMinMUniform, dense W or B >= 512).
 
 uint32_t gemm_kind(uint32_t M, bool dense, uint32_t log2b, uint64_t total) {
   const bool uniform = dense || (log2b >= 9 && total < (1ull << 31));
-  if (M >= kMfmaMinM) return uniform ? 3 : 2;
-  return (!dense && uniform) ? 1 : 0;
+  if (uniform) return M >= kMfmaMinMUniform ? 3 : dense ? 0 : 1;
+  return M >= kMfmaMinM ? 2 : 0;
 }
 
 
@@ -1570,7 +1574,10 @@ uint64_t gemm_workspace_bytes(uint32_t M, uint32_t K, uint32_t N) {
   // whichever kernel the call selects
   uint64_t most = 256;
   for (uint32_t kind = 0; kind < 4; ++kind) {
-    if ((kind >= 2) != (M >= kMfmaMinM)) continue;
+    const bool mfma_kind = kind >= 2;
+    const bool used = kind == 3 || kind == 1 ? (M >= kMfmaMinMUniform) == mfma_kind
+                                             : (M >= kMfmaMinM) == mfma_kind;
+    if (!used) continue;
     uint32_t ks, kr;
     gemm_plan_kind(kind, M, K, N, &ks, &kr);
     const uint64_t partial = ks > 1 ? (uint64_t)ks * M * N * 4 : 0;
