@@ -70,7 +70,7 @@ def compress_oracle(orc, W, B):
     return comp, None
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 15, 16, 17, 40, 65, 128, 129, 200])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 15, 16, 17, 40, 65, 128, 129, 200])
 def test_one_hot_rows_exact(E, orc, M):
     K, N = 256, 1024
     W = synth.gaussian_bits((K, N), 0.02, 200, M)
@@ -88,7 +88,7 @@ def test_one_hot_rows_exact(E, orc, M):
 
 
 @pytest.mark.parametrize("B", [128, 256, 512, 1024, 4096])
-@pytest.mark.parametrize("M", [1, 4, 5, 16, 33, 130])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 16, 33, 130])
 def test_block_sizes_small(E, orc, B, M):
     K, N = 520, 4096                                  # K not a multiple of the K ranges
     W = synth.gaussian_bits((K, N), 0.02, 201, B)
@@ -115,7 +115,7 @@ def test_long_k_ragged_tail(E, orc, M):
     assert_within(run_fused(E, X, comp, info, N), Y, A, "fused K=%d M=%d" % (K, M))
 
 
-@pytest.mark.parametrize("M", [16, 100, 130])
+@pytest.mark.parametrize("M", [2, 16, 100, 130])
 def test_long_k_ragged_tail_b512(E, orc, M):
     """K = 2056 at B = 512 (row-uniform kernels: a K range ending 8 rows into
     a 32- or 64-row step), two 512-column strips (four 256-column ones), M
@@ -166,7 +166,7 @@ def test_gpu_stream_and_workspace_reuse(E, orc):
     assert np.array_equal(ys[4], ys[5]) and np.array_equal(ys[3], ys[6])
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 2, 16])
 def test_full_size_all_outputs(E, orc, M):
     K, N = 4096, 14336
     W = synth.gemm_weight(K, N)

@@ -74,7 +74,7 @@ def oracle_stream(E, orc, W, B, pow2=False):
     return comp, E.enc_read_info(comp)
 
 
-@pytest.mark.parametrize("M", [1, 3, 5, 16, 17, 33, 64, 65, 128])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 16, 17, 33, 64, 65, 128])
 def test_one_hot_rows_exact(E, orc, M):
     N, K = 256, 1024
     W = synth.gaussian_bits((N, K), 0.02, 210, M)
@@ -90,7 +90,7 @@ def test_one_hot_rows_exact(E, orc, M):
 
 
 @pytest.mark.parametrize("B", [128, 256, 512, 1024, 4096])
-@pytest.mark.parametrize("M", [1, 5, 16, 33, 70])
+@pytest.mark.parametrize("M", [1, 2, 5, 16, 33, 70])
 def test_block_sizes(E, orc, B, M):
     N, K = 192, 4096
     W = synth.gaussian_bits((N, K), 0.02, 211, B)
