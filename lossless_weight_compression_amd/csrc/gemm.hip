@@ -1672,8 +1672,11 @@ __host__ __device__ constexpr uint32_t gemv_batch(int mm) { return mm <= 2 ? 4 :
 constexpr uint32_t kGemvMaxBlocks = kGemvRows * (kGemvMaxK / 128) + 1;
 
 // XFIXED: the host has checked that 256 * gemv_batch(MM) groups are a whole
-// number of rows (groups per row divide it), so lane t's X chunks are the
-// same in every iteration and are loaded once, before the loop.
+// number of rows (groups per row, then a power of two, divide it), so lane
+// t's X chunks are the same in every iteration and are loaded once, before
+// the loop; and, for a coded W, that B >= 512, so the 64 groups of a wave
+// instruction (512 values from a multiple of 512) lie in one block, whose
+// offset and {base, width} are then wave-uniform (scalar registers).
 template <int MM, bool DENSE, bool XFIXED>
 __global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
   constexpr uint32_t R = kGemvRows;
@@ -1729,6 +1732,14 @@ __global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
       for (int m = 0; m < MM; ++m) xpre[i][m] = *reinterpret_cast<const uint4 *>(a.x + (uint64_t)m * K + kc);
     }
   }
+  // wave-uniform block parameters and 32-bit offsets inside the workgroup's
+  // rows: 24.1 -> 23.2 us per call (M = 1, 14336x4096 W), fewer VALU
+  // instructions per group
+  constexpr bool UNIF = !DENSE && XFIXED;
+  const uint32_t bmask = (1u << log2b) - 1;
+  const uint32_t e0m = (uint32_t)(e0 & bmask);
+  const uint32_t smbase = kHeaderBytes + (uint32_t)e0;
+  const uint32_t log2gpr = 31 - __builtin_clz(gpr);
   for (uint32_t f0 = 0; f0 < ng; f0 += 256 * NB) {
     uint4 wv[NB], xs[NB][MM];
     u32x2 sm[NB];
@@ -1745,6 +1756,19 @@ __global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
         xs[i][m] = XFIXED ? xpre[XFIXED ? i : 0][m] : *reinterpret_cast<const uint4 *>(a.x + (uint64_t)m * K + kc);
       if (DENSE) {
         wv[i] = *reinterpret_cast<const uint4 *>(a.wdense + e);
+      } else if (UNIF) {
+        const uint32_t fw = f0 + i * 256 + 64 * wave;
+        const uint32_t fwc = fw < ng ? fw : ng - 64;
+        const uint32_t le = e0m + 8 * fwc;
+        const uint32_t j = le >> log2b;
+        const uint32_t meta = __builtin_amdgcn_readfirstlane(t_meta[j]);
+        const uint32_t boff = __builtin_amdgcn_readfirstlane(t_off[j]);
+        const uint32_t w = meta >> 8;
+        const uint32_t u = ((le & bmask) >> 3) + lane;
+        const uint32_t pb = boff + u * w;
+        sm[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, smbase + 8 * (fwc + lane), 0, 0);
+        qd[i] = __builtin_amdgcn_raw_buffer_load_b96(rs, pb & ~3u, 0, 0);
+        info[i] = (meta & 0xFFu) | (w << 8) | ((pb & 3u) << 16);
       } else {
         const uint32_t j = (uint32_t)((e >> log2b) - b_first);
         const uint32_t meta = t_meta[j];
@@ -1760,7 +1784,7 @@ __global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
     for (uint32_t i = 0; i < NB; ++i) {
       const uint32_t fw = f0 + i * 256 + 64 * wave;   // the wave's first group (uniform)
       if (fw >= ng) break;
-      const uint32_t row = fw / gpr;
+      const uint32_t row = XFIXED ? fw >> log2gpr : fw / gpr;
       if (row != cur) {
         flush(cur);
         cur = row;
@@ -1768,7 +1792,7 @@ __global__ __launch_bounds__(256) void k_gemv_nt(GemmArgs a) {
       if (!DENSE) {
         const uint32_t w = (info[i] >> 8) & 15u;
         uint32_t el, eh;
-        if (__ballot(w != 4) == 0) {
+        if (UNIF ? __builtin_amdgcn_readfirstlane(w) == 4 : __ballot(w != 4) == 0) {
           // width 4 across the wave: a group's codes are one aligned dword
           codes_to_bytes_w4(qd[i].x, el, eh);
         } else {
@@ -1808,7 +1832,7 @@ template <bool DENSE>
 hipError_t launch_gemv_nt(const GemmArgs &a, hipStream_t s) {
   const dim3 grid((a.N + kGemvRows - 1) / kGemvRows), block(256);
   static_assert(kGemvMaxM == 1, "one instantiation per M");
-  if ((256u * gemv_batch(1)) % (a.K >> 3) == 0)
+  if ((256u * gemv_batch(1)) % (a.K >> 3) == 0 && (DENSE || a.log2b >= 9))
     hipLaunchKernelGGL((k_gemv_nt<1, DENSE, true>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((k_gemv_nt<1, DENSE, false>), grid, block, 0, s, a);
